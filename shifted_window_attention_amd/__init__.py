@@ -1,0 +1,17 @@
+"""MI355X (gfx950) shifted-window multi-head self-attention.
+
+A thin ctypes binding over libswinattn.so: every function here only marshals
+arguments (tensor data pointers, sizes, the current HIP stream) to the C ABI
+declared in include/swin_attn.h, under the same names. All computation runs in
+the library's HIP kernels; there is no fallback. If the library has not been
+built, importing the binding raises.
+"""
+import ctypes
+import os
+
+from .native import (  # noqa: F401
+    SWIN_BF16, SWIN_F32, SWIN_OK, SWIN_PERIODIC_LAT, SWIN_PERIODIC_LEVEL, SWIN_PERIODIC_LON, SwinAttnDesc,
+    SwinAttnStats, SwinError, lib, make_desc, swin_attn_bwd, swin_attn_fwd, swin_attn_host_index_map,
+    swin_attn_host_stats, swin_attn_plan_create, swin_attn_plan_destroy, swin_attn_plan_stats, swin_attn_sizes,
+    swin_status_string, swin_window_gather, swin_window_scatter, Plan,
+)

@@ -1,0 +1,394 @@
+// Window attention backward (bf16 MFMA, fp32 softmax gradients), head_dim 32.
+//
+// With S2 = log2(e) S, P = exp2(S2 - lse2), natural-unit gradients:
+//   dV = P^T dO;  dP = dO V^T;  D = rowsum(dO * O);  dS = P * (dP - D);
+//   dq = tau dS K;  dk = tau dS^T q = (dS^T q') / log2(e);  dT[h, bin] += dS
+// (q' = tau log2(e) q is the stored query). The inverse routes carry these gradients
+// back to their sources (TERRA section IV-D).
+//
+// Work decomposition: one workgroup per (chunk of windows of one class, head), one wave
+// per 16-key tile. A lane holds one key and 4 consecutive queries of every 16-query tile
+// (S = Q K^T on v_mfma_f32_16x16x32_bf16), so dV^T = dO^T P and dK^T = Q'^T dS contract
+// over queries inside the wave: P and dS of two adjacent query tiles are directly the B
+// operand, and dO^T, Q'^T come from the row-major LDS tiles through gfx950's transposing
+// LDS read. dQ contracts over keys, i.e. over waves: dS goes through LDS once (bf16) and
+// every wave then forms dQ^T = K^T dS^T for one query tile.
+//
+// Bias gradient without global atomics: all windows of a chunk share one class, so a
+// lane's (query, key) positions are the same in every window and its dS values are summed
+// over the chunk in registers. Once per workgroup the per-position sums are binned into
+// the relative-position table in LDS, each bin owned by one thread and filled in a fixed
+// order, and the workgroup writes one partial table. A second kernel adds the partials
+// in order of work item. Every reduction therefore has a fixed order and repeated calls
+// are bitwise identical.
+#include "device_common.h"
+#include "swin_internal.h"
+
+namespace swin {
+
+__device__ __forceinline__ bf16x4 lds_tr4b(const bf16* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 tr_frag(const bf16* tile, int pitch, int row0, int col0, int g, int li) {
+  // 8 k values for column col0 + li: rows row0 + 4g + r (r < 4) and row0 + 16 + 4g + r
+  const bf16* base = tile + (row0 + 4 * g + (li >> 2)) * pitch + col0 + 4 * (li & 3);
+  const bf16x4 lo = lds_tr4b(base);
+  const bf16x4 hi = lds_tr4b(base + 16 * pitch);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+struct BwdArgs {
+  const bf16* qkv;          // saved [3][nh][n_tok][32] (q pre-scaled)
+  const bf16* o;            // saved [n_tok][C]
+  const float* lse;         // saved [nh][n_tok] (log2 units)
+  const bf16* dO;           // [nh][n_tok][32]
+  const float* table;       // [nh][nbins]
+  bf16* dqkv;               // [n_tok][3C]
+  float* dbias_part;        // [n_items_total][nh][nbins]
+  const WorkItem* work;     // this launch's items
+  int item_base;            // index of work[0] among all backward work items
+  const ClassInfo* classes;
+  const int32_t* class_win;
+  const int32_t* win_off;
+  int64_t n_tok;
+  int nh, C, nbins;
+  int win[3];
+  float tau;
+};
+
+__device__ __forceinline__ void coords_of(const ClassInfo& ci, int j, int& ld, int& lh, int& lw, int& lab) {
+  lw = j % ci.ext[2];
+  const int r = j / ci.ext[2];
+  lh = r % ci.ext[1];
+  ld = r / ci.ext[1];
+  lab = (ld >= ci.split[0] ? 1 : 0) | (lh >= ci.split[1] ? 2 : 0) | (lw >= ci.split[2] ? 4 : 0);
+}
+
+__device__ __forceinline__ float bias2_of(const ClassInfo& ci, const float* __restrict__ tab, const int* win, int q,
+                                          int k) {
+  if (q >= ci.n || k >= ci.n) return -INFINITY;
+  int qd, qh, qw, ql, kd, kh, kw, kl;
+  coords_of(ci, q, qd, qh, qw, ql);
+  coords_of(ci, k, kd, kh, kw, kl);
+  if (ql != kl) return -INFINITY;
+  const int bin = ((qd - kd + win[0] - 1) * (2 * win[1] - 1) + (qh - kh + win[1] - 1)) * (2 * win[2] - 1) +
+                  (qw - kw + win[2] - 1);
+  return tab[bin] * kLog2e;
+}
+
+template <int NKT>
+struct BwdLds {
+  static constexpr int NKC = (NKT + 1) / 2;
+  static constexpr int ROWS = NKC * 32;      // staged query/key rows (zero beyond n)
+  static constexpr int QP = 40;              // Q', dO pitch (bf16)
+  static constexpr int KP = 48;              // K pitch (bf16), read transposed only
+  static constexpr int SP = ROWS + 4;        // dS pitch (bf16)
+  static constexpr int Q_OFF = 0;
+  static constexpr int DO_OFF = Q_OFF + ROWS * QP * 2;
+  static constexpr int K_OFF = DO_OFF + ROWS * QP * 2;
+  static constexpr int S_OFF = K_OFF + ROWS * KP * 2;
+  static constexpr int L_OFF = S_OFF + ROWS * SP * 2;
+  static constexpr int D_OFF = L_OFF + ROWS * 4;
+  static constexpr int ARENA = D_OFF + ROWS * 4;   // bytes reused by the dbias binning
+  static constexpr int SLAB = (ARENA / (NKT * 16 * 4)) / 16 * 16;  // query rows per binning slab
+};
+
+template <int NKT>
+__global__ __launch_bounds__(64 * NKT) void k_attn_bwd(BwdArgs a) {
+  using L = BwdLds<NKT>;
+  constexpr int NKC = L::NKC;
+  constexpr int NT = 64 * NKT;
+  static_assert(L::SLAB >= 16, "LDS arena too small for the bias-gradient slab");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[L::ARENA];
+  extern __shared__ float bins_lds[];  // [nbins], dynamic
+  bf16* Qs = (bf16*)(lds + L::Q_OFF);
+  bf16* dOs = (bf16*)(lds + L::DO_OFF);
+  bf16* Ks = (bf16*)(lds + L::K_OFF);
+  bf16* dSs = (bf16*)(lds + L::S_OFF);
+  float* LSEs = (float*)(lds + L::L_OFF);
+  float* Ds = (float*)(lds + L::D_OFF);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, kt = tid >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const WorkItem wk = a.work[blockIdx.x];
+  const int h = blockIdx.y;
+  const ClassInfo ci = a.classes[wk.cls];
+  const int n = ci.n;
+  const int nqt = ci.nqt;  // == NKT
+  const int key = 16 * kt + li;
+  const float* tab = a.table + (int64_t)h * a.nbins;
+
+  // lane's bias + mask for every query tile (S layout: key fixed, queries 16 qt + 4 g + i)
+  f32x4 bias[NKT], dbacc[NKT];
+#pragma unroll
+  for (int qt = 0; qt < NKT; ++qt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bias[qt][i] = bias2_of(ci, tab, a.win, 16 * qt + 4 * g + i, key);
+      dbacc[qt][i] = 0.f;
+    }
+  for (int i = tid; i < a.nbins; i += NT) bins_lds[i] = 0.f;
+
+  const bf16* Qh = a.qkv + ((int64_t)(0 * a.nh + h) * a.n_tok) * 32;
+  const bf16* Kh = a.qkv + ((int64_t)(1 * a.nh + h) * a.n_tok) * 32;
+  const bf16* Vh = a.qkv + ((int64_t)(2 * a.nh + h) * a.n_tok) * 32;
+  const bf16* dOh = a.dO + ((int64_t)h * a.n_tok) * 32;
+  const float* LSEh = a.lse + (int64_t)h * a.n_tok;
+  const int C = a.C;
+  const float inv_log2e = 1.f / kLog2e;
+  // key columns of dS that no wave owns (odd tile count) are read by dQ: keep them zero
+  if constexpr (L::ROWS > 16 * NKT) {
+    constexpr int EXTRA = L::ROWS - 16 * NKT;
+    for (int c = tid; c < L::ROWS * EXTRA; c += NT) dSs[(c / EXTRA) * L::SP + 16 * NKT + c % EXTRA] = to_bf16(0.f);
+  }
+
+  for (int w = 0; w < wk.count; ++w) {
+    const int64_t off = a.win_off[a.class_win[wk.first + w]];
+    __syncthreads();
+    // stage Q', dO, K (zero beyond n), lse2 and D = rowsum(dO * O)
+    for (int c = tid; c < L::ROWS * 4; c += NT) {
+      const int row = c >> 2, part = (c & 3) * 8;
+      bf16x8 qv = {}, dv = {}, kv = {};
+      if (row < n) {
+        qv = *(const bf16x8*)(Qh + (off + row) * 32 + part);
+        dv = *(const bf16x8*)(dOh + (off + row) * 32 + part);
+        kv = *(const bf16x8*)(Kh + (off + row) * 32 + part);
+      }
+      *(bf16x8*)(Qs + row * L::QP + part) = qv;
+      *(bf16x8*)(dOs + row * L::QP + part) = dv;
+      *(bf16x8*)(Ks + row * L::KP + part) = kv;
+    }
+    for (int r = tid; r < L::ROWS; r += NT) {
+      float lv = 0.f, dv = 0.f;
+      if (r < n) {
+        lv = LSEh[off + r];
+        const bf16* orow = a.o + (off + r) * C + h * 32;
+        const bf16* drow = dOh + (off + r) * 32;
+#pragma unroll
+        for (int d8 = 0; d8 < 32; d8 += 8) {
+          const bf16x8 ov = *(const bf16x8*)(orow + d8);
+          const bf16x8 gv = *(const bf16x8*)(drow + d8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dv += to_f32(ov[e]) * to_f32(gv[e]);
+        }
+      }
+      LSEs[r] = lv;
+      Ds[r] = dv;
+    }
+    // the wave's own key tile as B operands (K^T for S, V^T for dP)
+    bf16x8 kb = {}, vb = {};
+    if (key < n) {
+      kb = *(const bf16x8*)(Kh + (off + key) * 32 + 8 * g);
+      vb = *(const bf16x8*)(Vh + (off + key) * 32 + 8 * g);
+    }
+    __syncthreads();
+
+    f32x4 dvacc[2] = {f32x4{}, f32x4{}}, dkacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      bf16x8 pb = {}, sb = {};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int qt = 2 * c + u;
+        if (qt < NKT) {
+          const bf16x8 qa = *(const bf16x8*)(Qs + (16 * qt + li) * L::QP + 8 * g);
+          const f32x4 s = mfma16(qa, kb, bias[qt]);
+          const bf16x8 da = *(const bf16x8*)(dOs + (16 * qt + li) * L::QP + 8 * g);
+          const f32x4 dp = mfma16(da, vb, f32x4{});
+          const f32x4 l4 = *(const f32x4*)(LSEs + 16 * qt + 4 * g);
+          const f32x4 d4 = *(const f32x4*)(Ds + 16 * qt + 4 * g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = fast_exp2(s[i] - l4[i]);
+            const float ds = p * (dp[i] - d4[i]);
+            dbacc[qt][i] += ds;
+            pb[4 * u + i] = to_bf16(p);
+            sb[4 * u + i] = to_bf16(ds);
+            dSs[(16 * qt + 4 * g + i) * L::SP + key] = sb[4 * u + i];
+          }
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const bf16x8 doT = tr_frag(dOs, L::QP, 32 * c, 16 * dt, g, li);
+        dvacc[dt] = mfma16(doT, pb, dvacc[dt]);
+        const bf16x8 qT = tr_frag(Qs, L::QP, 32 * c, 16 * dt, g, li);
+        dkacc[dt] = mfma16(qT, sb, dkacc[dt]);
+      }
+    }
+    if (key < n) {
+      bf16* row = a.dqkv + (off + key) * (3 * C) + h * 32;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        bf16x4 kv4, vv4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kv4[i] = to_bf16(dkacc[dt][i] * inv_log2e);
+          vv4[i] = to_bf16(dvacc[dt][i]);
+        }
+        *(bf16x4*)(row + C + 16 * dt + 4 * g) = kv4;
+        *(bf16x4*)(row + 2 * C + 16 * dt + 4 * g) = vv4;
+      }
+    }
+    __syncthreads();  // dS complete
+    // dQ^T for query tile qt = kt: K^T (transposed read of K) times dS^T (rows of dS)
+    {
+      const int q = 16 * kt + li;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        f32x4 dq = f32x4{};
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) {
+          const bf16x8 kT = tr_frag(Ks, L::KP, 32 * c, 16 * dt, g, li);
+          const bf16x4 lo = *(const bf16x4*)(dSs + q * L::SP + 32 * c + 4 * g);
+          const bf16x4 hi = *(const bf16x4*)(dSs + q * L::SP + 32 * c + 16 + 4 * g);
+          const bf16x8 sb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          dq = mfma16(kT, sb, dq);
+        }
+        if (q < n) {
+          bf16x4 v4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v4[i] = to_bf16(dq[i] * a.tau);
+          *(bf16x4*)(a.dqkv + (off + q) * (3 * C) + h * 32 + 16 * dt + 4 * g) = v4;
+        }
+      }
+    }
+  }
+
+  // bin the chunk's per-position dS sums into the relative-position table, slab by slab
+  __syncthreads();
+  float* acc = (float*)lds;  // [SLAB][16 NKT] fp32
+  const int kcols = 16 * NKT;
+  for (int q0 = 0; q0 < 16 * NKT; q0 += L::SLAB) {
+#pragma unroll
+    for (int qt = 0; qt < NKT; ++qt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = 16 * qt + 4 * g + i;
+        if (q >= q0 && q < q0 + L::SLAB) acc[(q - q0) * kcols + key] = dbacc[qt][i];
+      }
+    __syncthreads();
+    for (int b = tid; b < a.nbins; b += NT) {
+      // bin b <-> offset (query minus key) along each axis
+      const int tw = 2 * a.win[2] - 1, th = 2 * a.win[1] - 1;
+      const int rw = b % tw - (a.win[2] - 1);
+      const int rh = (b / tw) % th - (a.win[1] - 1);
+      const int rd = b / (tw * th) - (a.win[0] - 1);
+      float sum = bins_lds[b];
+      const int q1 = q0 + L::SLAB < n ? q0 + L::SLAB : n;
+      for (int q = q0; q < q1; ++q) {
+        const int qw = q % ci.ext[2], qr = q / ci.ext[2];
+        const int qh = qr % ci.ext[1], qd = qr / ci.ext[1];
+        const int kw = qw - rw, kh = qh - rh, kd = qd - rd;
+        if (kw < 0 || kw >= ci.ext[2] || kh < 0 || kh >= ci.ext[1] || kd < 0 || kd >= ci.ext[0]) continue;
+        const int k = (kd * ci.ext[1] + kh) * ci.ext[2] + kw;
+        sum += acc[(q - q0) * kcols + k];
+      }
+      bins_lds[b] = sum;
+    }
+    __syncthreads();
+  }
+  float* part = a.dbias_part + ((int64_t)(a.item_base + blockIdx.x) * a.nh + h) * a.nbins;
+  for (int b = tid; b < a.nbins; b += NT) part[b] = bins_lds[b];
+  (void)nqt;
+}
+
+// dT[h][b] = sum over work items (in order) of the partial tables.
+__global__ void k_dbias_reduce(const float* __restrict__ part, int n_items, int per_item, float* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= per_item) return;
+  float acc = 0.f;
+  for (int it = 0; it < n_items; ++it) acc += part[(int64_t)it * per_item + i];
+  out[i] = acc;
+}
+
+template <int NKT>
+static void launch_bwd_one(const BwdArgs& a, int n_items, int nh, size_t dyn, hipStream_t s) {
+  k_attn_bwd<NKT><<<dim3((unsigned)n_items, (unsigned)nh), 64 * NKT, dyn, s>>>(a);
+}
+
+// The staged Q', dO, K and dS tiles fit the 160 KB of LDS up to 12 key tiles (192 tokens).
+typedef void (*bwd_launcher)(const BwdArgs&, int, int, size_t, hipStream_t);
+static const bwd_launcher kBwd[kMaxBwdTiles + 1] = {nullptr,           launch_bwd_one<1>, launch_bwd_one<2>,
+                                                    launch_bwd_one<3>, launch_bwd_one<4>, launch_bwd_one<5>,
+                                                    launch_bwd_one<6>, launch_bwd_one<7>, launch_bwd_one<8>,
+                                                    launch_bwd_one<9>, launch_bwd_one<10>, launch_bwd_one<11>,
+                                                    launch_bwd_one<12>};
+
+hipError_t launch_dproj_bf16(const swin_attn_plan* p, const void* dy, const void* wprojT, void* dO, hipStream_t s);
+hipError_t launch_dgrad_qkv_bf16(const swin_attn_plan* p, const void* dqkv, const void* wqkvT, void* dx,
+                                 hipStream_t s);
+hipError_t launch_wgrad_bf16(const bf16* A, int64_t lda, const int32_t* a_rows, const bf16* B, int64_t ldb,
+                             const int32_t* b_rows, int64_t T, int M, int N, int splits, int64_t chunk, float* part,
+                             float* dw, float* db, hipStream_t s);
+hipError_t launch_transpose_bf16(const void* in, void* out, int R, int Cn, hipStream_t s);
+
+hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* x, const void* w_qkv,
+                           const void* w_proj, const float* table, const void* saved, void* dx, float* dw_qkv,
+                           float* db_qkv, float* dw_proj, float* db_proj, float* dtable, void* ws,
+                           hipStream_t s) {
+  const int C = p->C;
+  const char* sv = (const char*)saved;
+  const bf16* qkv = (const bf16*)sv;
+  const bf16* o = (const bf16*)(sv + p->saved_qkv);
+  const float* lse = (const float*)(sv + p->saved_qkv + p->saved_o);
+  char* w = (char*)ws;
+  bf16* dO = (bf16*)w;
+  bf16* dqkv = (bf16*)(w + p->bwd_do);
+  bf16* wprojT = (bf16*)(w + p->bwd_do + p->bwd_dqkv);
+  bf16* wqkvT = wprojT + (size_t)C * C;
+  float* part = (float*)(w + p->bwd_do + p->bwd_dqkv + p->bwd_wt);
+  float* dbias_part = (float*)(w + p->bwd_do + p->bwd_dqkv + p->bwd_wt + p->bwd_part);
+
+  hipError_t e = launch_transpose_bf16(w_proj, wprojT, C, C, s);
+  if (e == hipSuccess) e = launch_transpose_bf16(w_qkv, wqkvT, 3 * C, C, s);
+  // proj backward: dO = gather(dy) W_proj (head-split), dW_proj = gather(dy)^T o, db_proj
+  if (e == hipSuccess) e = launch_dproj_bf16(p, dy, wprojT, dO, s);
+  if (e == hipSuccess)
+    e = launch_wgrad_bf16((const bf16*)dy, C, p->dev.perm, o, C, nullptr, p->n_tok, C, C, p->wgrad_splits_proj,
+                          p->wgrad_chunk_proj, part, dw_proj, db_proj, s);
+  if (e != hipSuccess) return e;
+  // attention core backward
+  BwdArgs a{};
+  a.qkv = qkv;
+  a.o = o;
+  a.lse = lse;
+  a.dO = dO;
+  a.table = table;
+  a.dqkv = dqkv;
+  a.dbias_part = dbias_part;
+  a.classes = p->dev.classes;
+  a.class_win = p->dev.class_win;
+  a.win_off = p->dev.win_off;
+  a.n_tok = p->n_tok;
+  a.nh = p->nh;
+  a.C = C;
+  a.nbins = p->nbins;
+  for (int i = 0; i < 3; ++i) a.win[i] = p->d.window[i];
+  a.tau = p->tau;
+  const size_t dyn = (size_t)p->nbins * sizeof(float);
+  for (const auto& r : p->bwd_ranges) {
+    a.work = p->dev.bwd_work + r.begin;
+    a.item_base = r.begin;
+    kBwd[r.nqt](a, r.count, p->nh, dyn, s);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int per_item = p->nh * p->nbins;
+  k_dbias_reduce<<<(unsigned)((per_item + 255) / 256), 256, 0, s>>>(dbias_part, (int)p->bwd_work.size(), per_item,
+                                                                     dtable);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // QKV backward: dx = scatter(dqkv W_qkv), dW_qkv = dqkv^T gather(x), db_qkv
+  e = launch_dgrad_qkv_bf16(p, dqkv, wqkvT, dx, s);
+  if (e == hipSuccess)
+    e = launch_wgrad_bf16(dqkv, 3 * C, nullptr, (const bf16*)x, C, p->dev.perm, p->n_tok, 3 * C, C,
+                          p->wgrad_splits_qkv, p->wgrad_chunk_qkv, part, dw_qkv, db_qkv, s);
+  return e;
+}
+
+}  // namespace swin

@@ -1,0 +1,206 @@
+// Fused window attention forward (bf16 MFMA, fp32 softmax), head_dim 32.
+//
+// For one head h and one window (TERRA section IV-A / Fig. 4: W-MSA and SW-MSA; BEAST
+// "Domain-Tensor Parallelism": attention is independent per head):
+//   S2 = q' k^T + log2(e) * (T[h, bin] or -inf where wrap labels differ)
+//   P  = exp2(S2 - rowmax) / rowsum,  o = P v,  lse2 = rowmax + log2(rowsum)
+// where q' = tau * log2(e) * q was folded into the QKV projection, so S2 = log2(e) * S.
+//
+// Work decomposition: one workgroup per (chunk of windows of one class, head); one wave
+// per 16-query tile. Every window of a class has the same extent and label split, so a
+// lane's bias + mask values (its query against every key) are computed once per
+// workgroup and then serve as the initial accumulator of the Q K^T MFMA for every window
+// of the chunk. A window's K and V (n x 32 bf16 each) are staged in LDS; Q comes straight
+// from HBM into the MFMA operand registers.
+//
+// The logits are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16), so a lane
+// holds one query and 4 consecutive keys of every 16-key tile: the row max and row sum
+// are in-register reductions plus two cross-lane steps, and the probabilities of two
+// adjacent key tiles are already the B operand of O^T = V^T P^T. The V^T operand is read
+// from the row-major V tile with gfx950's transposing LDS read. A window has at most 256
+// tokens, so a query's whole key row lives in registers and the softmax is exact in a
+// single pass (no online rescaling).
+#include "device_common.h"
+#include "swin_internal.h"
+
+namespace swin {
+
+__device__ __forceinline__ bf16x4 lds_tr4(const bf16* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+struct AttnArgs {
+  const bf16* qkv;          // [3][nh][n_tok][32]
+  const float* table;       // [nh][nbins]
+  bf16* o;                  // [n_tok][C]
+  float* lse;               // [nh][n_tok]
+  const WorkItem* work;
+  const ClassInfo* classes;
+  const int32_t* class_win;
+  const int32_t* win_off;
+  int64_t n_tok;
+  int nh, C, nbins;
+  int win[3];               // nominal window (wd, wh, ww)
+};
+
+// Local coordinates and label bits of token j of a window class.
+__device__ __forceinline__ void token_coords(const ClassInfo& ci, int j, int& ld, int& lh, int& lw, int& lab) {
+  lw = j % ci.ext[2];
+  const int r = j / ci.ext[2];
+  lh = r % ci.ext[1];
+  ld = r / ci.ext[1];
+  lab = (ld >= ci.split[0] ? 1 : 0) | (lh >= ci.split[1] ? 2 : 0) | (lw >= ci.split[2] ? 4 : 0);
+}
+
+// Logit offset (log2 units) of query q against key k, or -inf if the pair is not allowed.
+__device__ __forceinline__ float pair_bias2(const ClassInfo& ci, const float* __restrict__ tab, const int* win,
+                                            int q, int k) {
+  if (k >= ci.n) return -INFINITY;
+  int qd, qh, qw, ql, kd, kh, kw, kl;
+  token_coords(ci, q, qd, qh, qw, ql);
+  token_coords(ci, k, kd, kh, kw, kl);
+  if (ql != kl) return -INFINITY;
+  const int bin = ((qd - kd + win[0] - 1) * (2 * win[1] - 1) + (qh - kh + win[1] - 1)) * (2 * win[2] - 1) +
+                  (qw - kw + win[2] - 1);
+  return tab[bin] * kLog2e;
+}
+
+template <int NKT>
+__global__ __launch_bounds__(64 * NKT) void k_attn_fwd(AttnArgs a) {
+  constexpr int NKC = (NKT + 1) / 2;   // 32-key chunks of the PV product
+  constexpr int KROWS = NKC * 32;      // staged key rows (zero beyond n)
+  constexpr int KP = 40;               // K row pitch (bf16): conflict-free 16-byte fragment reads
+  constexpr int VP = 48;               // V row pitch (bf16): conflict-free transposed reads
+  __shared__ __attribute__((aligned(16))) bf16 Ks[KROWS * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[KROWS * VP];
+
+  const int lane = threadIdx.x & 63, qt = threadIdx.x >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const WorkItem wk = a.work[blockIdx.x];
+  const int h = blockIdx.y;
+  const ClassInfo ci = a.classes[wk.cls];
+  const int n = ci.n;
+  const int q = qt * 16 + li;
+  const bool qv = q < n;
+  const float* tab = a.table + (int64_t)h * a.nbins;
+
+  f32x4 bias[NKT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bias[kt][i] = qv ? pair_bias2(ci, tab, a.win, q, 16 * kt + 4 * g + i) : 0.f;
+
+  const bf16* Qh = a.qkv + ((int64_t)(0 * a.nh + h) * a.n_tok) * 32;
+  const bf16* Kh = a.qkv + ((int64_t)(1 * a.nh + h) * a.n_tok) * 32;
+  const bf16* Vh = a.qkv + ((int64_t)(2 * a.nh + h) * a.n_tok) * 32;
+
+  for (int w = 0; w < wk.count; ++w) {
+    const int64_t off = a.win_off[a.class_win[wk.first + w]];
+    __syncthreads();  // previous window's LDS reads are done
+    for (int c = threadIdx.x; c < KROWS * 4; c += 64 * NKT) {
+      const int row = c >> 2, part = (c & 3) * 8;
+      bf16x8 kv = {}, vv = {};
+      if (row < n) {
+        kv = *(const bf16x8*)(Kh + (off + row) * 32 + part);
+        vv = *(const bf16x8*)(Vh + (off + row) * 32 + part);
+      }
+      *(bf16x8*)(Ks + row * KP + part) = kv;
+      *(bf16x8*)(Vs + row * VP + part) = vv;
+    }
+    bf16x8 bq = {};
+    if (qv) bq = *(const bf16x8*)(Qh + (off + q) * 32 + 8 * g);
+    __syncthreads();
+
+    f32x4 s[NKT];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      const bf16x8 ka = *(const bf16x8*)(Ks + (16 * kt + li) * KP + 8 * g);
+      s[kt] = mfma16(ka, bq, bias[kt]);
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, s[kt][i]);
+    m = wave_max_xor16_32(m);
+    float l = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(s[kt][i] - m);
+        s[kt][i] = p;
+        l += p;
+      }
+    l = wave_sum_xor16_32(l);
+
+    f32x4 oacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      bf16x8 pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = to_bf16(s[2 * c][i]);
+        pb[4 + i] = (2 * c + 1 < NKT) ? to_bf16(s[2 * c + 1][i]) : to_bf16(0.f);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const bf16* base = Vs + (32 * c + 4 * g + (li >> 2)) * VP + 16 * dt + 4 * (li & 3);
+        const bf16x4 lo = lds_tr4(base);
+        const bf16x4 hi = lds_tr4(base + 16 * VP);
+        const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[dt] = mfma16(va, pb, oacc[dt]);
+      }
+    }
+    if (qv) {
+      const float inv = 1.f / l;
+      bf16* orow = a.o + (off + q) * a.C + h * 32;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        bf16x4 ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = to_bf16(oacc[dt][i] * inv);
+        *(bf16x4*)(orow + 16 * dt + 4 * g) = ov;
+      }
+      if (g == 0) a.lse[(int64_t)h * a.n_tok + off + q] = m + fast_log2(l);
+    }
+  }
+}
+
+template <int NKT>
+static void launch_one(const AttnArgs& a, int n_items, int nh, hipStream_t s) {
+  k_attn_fwd<NKT><<<dim3((unsigned)n_items, (unsigned)nh), 64 * NKT, 0, s>>>(a);
+}
+
+typedef void (*fwd_launcher)(const AttnArgs&, int, int, hipStream_t);
+static const fwd_launcher kFwd[17] = {nullptr,          launch_one<1>,  launch_one<2>,  launch_one<3>,
+                                      launch_one<4>,    launch_one<5>,  launch_one<6>,  launch_one<7>,
+                                      launch_one<8>,    launch_one<9>,  launch_one<10>, launch_one<11>,
+                                      launch_one<12>,   launch_one<13>, launch_one<14>, launch_one<15>,
+                                      launch_one<16>};
+
+hipError_t launch_attn_fwd_bf16(const swin_attn_plan* p, const void* qkv, const float* table, void* o, float* lse,
+                                hipStream_t s) {
+  AttnArgs a{};
+  a.qkv = (const bf16*)qkv;
+  a.table = table;
+  a.o = (bf16*)o;
+  a.lse = lse;
+  a.classes = p->dev.classes;
+  a.class_win = p->dev.class_win;
+  a.win_off = p->dev.win_off;
+  a.n_tok = p->n_tok;
+  a.nh = p->nh;
+  a.C = p->C;
+  a.nbins = p->nbins;
+  for (int i = 0; i < 3; ++i) a.win[i] = p->d.window[i];
+  for (const auto& r : p->fwd_ranges) {
+    a.work = p->dev.fwd_work + r.begin;
+    kFwd[r.nqt](a, r.count, p->nh, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace swin

@@ -1,0 +1,434 @@
+// Host plan and C ABI of the shifted-window attention library.
+//
+// The plan turns a descriptor into the tables the kernels run from:
+//   * the window-major slot -> grid row map (roll by -shift, row-major window
+//     order, row-major tokens inside a window; TERRA section IV-D and V-A),
+//   * the per-window token offset/length table, which lets short edge windows
+//     run without padding,
+//   * window classes (extent + wrap-label split) and per-class work chunks.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "swin_internal.h"
+
+namespace swin {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+static swin_status fail(swin_status st, const std::string& msg) {
+  set_error(msg);
+  return st;
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Validate a descriptor; fills a short reason on failure.
+static swin_status validate(const swin_attn_desc* d) {
+  if (!d) return fail(SWIN_ERR_ARG, "descriptor is NULL");
+  if (d->ndim != 2 && d->ndim != 3) return fail(SWIN_ERR_ARG, "ndim must be 2 or 3");
+  if (d->dtype != SWIN_F32 && d->dtype != SWIN_BF16) return fail(SWIN_ERR_ARG, "dtype must be SWIN_F32 or SWIN_BF16");
+  if (d->batch < 1) return fail(SWIN_ERR_ARG, "batch must be >= 1");
+  for (int a = 0; a < 3; ++a) {
+    if (d->grid[a] < 1) return fail(SWIN_ERR_ARG, "grid extents must be >= 1");
+    if (d->window[a] < 1) return fail(SWIN_ERR_ARG, "window extents must be >= 1");
+    if (d->window[a] > d->grid[a]) return fail(SWIN_ERR_ARG, "window larger than the grid");
+    if (d->shift[a] < 0 || d->shift[a] >= d->window[a]) return fail(SWIN_ERR_ARG, "shift must satisfy 0 <= s < window");
+  }
+  if (d->ndim == 2 && (d->grid[0] != 1 || d->window[0] != 1 || d->shift[0] != 0))
+    return fail(SWIN_ERR_ARG, "2-D descriptors need grid[0] == window[0] == 1 and shift[0] == 0");
+  if (d->channels < 1 || d->heads < 1) return fail(SWIN_ERR_ARG, "channels and heads must be >= 1");
+  if (d->channels % d->heads != 0) return fail(SWIN_ERR_ARG, "channels must be a multiple of heads");
+  if (d->periodic > 7u) return fail(SWIN_ERR_ARG, "periodic has bits outside 0x7");
+  if (!(d->scale >= 0.f) || !std::isfinite(d->scale)) return fail(SWIN_ERR_ARG, "scale must be finite and >= 0");
+  const double ntok = double(d->batch) * double(d->grid[0]) * double(d->grid[1]) * double(d->grid[2]);
+  if (ntok >= 2147483647.0) return fail(SWIN_ERR_UNSUPPORTED, "more than 2^31-1 tokens");
+  if (ntok * double(d->channels) * 3.0 >= 9.2e18) return fail(SWIN_ERR_UNSUPPORTED, "tensor too large");
+  return SWIN_OK;
+}
+
+static swin_status check_kernel_support(const swin_attn_desc* d, int64_t max_tokens) {
+  const int hd = d->channels / d->heads;
+  if (max_tokens > 16 * kMaxFwdTiles)
+    return fail(SWIN_ERR_UNSUPPORTED, "windows of more than 256 tokens are not supported");
+  if (d->dtype == SWIN_BF16) {
+    if (hd != 32) return fail(SWIN_ERR_UNSUPPORTED, "bf16 kernels need head_dim == 32");
+    if (d->channels % 64 != 0) return fail(SWIN_ERR_UNSUPPORTED, "bf16 kernels need channels % 64 == 0");
+  } else {
+    if (hd > 64) return fail(SWIN_ERR_UNSUPPORTED, "fp32 kernels need head_dim <= 64");
+    if (2 * max_tokens * hd * 4 > 160 * 1024)
+      return fail(SWIN_ERR_UNSUPPORTED, "fp32 window K/V tiles exceed the 160 KB of LDS");
+  }
+  return SWIN_OK;
+}
+
+// Host layout: everything the plan needs, without touching a device.
+struct HostLayout {
+  int64_t n_tok = 0, n_win = 0;
+  std::vector<int32_t> perm;      // slot -> grid row
+  std::vector<uint8_t> labels;    // slot -> label bits
+  std::vector<int32_t> win_off;   // n_win + 1
+  std::vector<int32_t> win_cls;   // window -> class
+  std::vector<ClassInfo> classes;
+  swin_attn_stats stats{};
+};
+
+static void build_layout(const swin_attn_desc* d, HostLayout& L) {
+  const int64_t N[3] = {d->grid[0], d->grid[1], d->grid[2]};
+  const int64_t w[3] = {d->window[0], d->window[1], d->window[2]};
+  const int64_t s[3] = {d->shift[0], d->shift[1], d->shift[2]};
+  int64_t nk[3];
+  for (int a = 0; a < 3; ++a) nk[a] = (N[a] + w[a] - 1) / w[a];
+  L.n_tok = d->batch * N[0] * N[1] * N[2];
+  L.n_win = d->batch * nk[0] * nk[1] * nk[2];
+  L.perm.resize(L.n_tok);
+  L.labels.resize(L.n_tok);
+  L.win_off.resize(L.n_win + 1);
+  L.win_cls.resize(L.n_win);
+  std::map<std::tuple<int, int, int, int, int, int>, int> cls_of;
+  int64_t slot = 0, wi = 0, masked = 0, max_tok = 0, pairs = 0;
+  for (int64_t b = 0; b < d->batch; ++b)
+    for (int64_t kd = 0; kd < nk[0]; ++kd)
+      for (int64_t kh = 0; kh < nk[1]; ++kh)
+        for (int64_t kw = 0; kw < nk[2]; ++kw, ++wi) {
+          const int64_t k[3] = {kd, kh, kw};
+          int64_t start[3], ext[3], split[3];
+          bool is_split = false;
+          for (int a = 0; a < 3; ++a) {
+            start[a] = k[a] * w[a];
+            ext[a] = std::min(w[a], N[a] - start[a]);
+            // rolled index r carries label 1 iff the axis is masked, s > 0 and r >= N - s
+            split[a] = ext[a];
+            if (!((d->periodic >> a) & 1u) && s[a] > 0) {
+              const int64_t sp = N[a] - s[a] - start[a];
+              if (sp > 0 && sp < ext[a]) {
+                split[a] = sp;
+                is_split = true;
+              }
+            }
+          }
+          const int64_t n = ext[0] * ext[1] * ext[2];
+          L.win_off[wi] = (int32_t)slot;
+          auto key = std::make_tuple((int)ext[0], (int)ext[1], (int)ext[2], (int)split[0], (int)split[1], (int)split[2]);
+          auto it = cls_of.find(key);
+          int c;
+          if (it == cls_of.end()) {
+            c = (int)L.classes.size();
+            cls_of[key] = c;
+            ClassInfo ci{};
+            for (int a = 0; a < 3; ++a) {
+              ci.ext[a] = (int32_t)ext[a];
+              ci.split[a] = (int32_t)split[a];
+            }
+            ci.n = (int32_t)n;
+            ci.nqt = (int32_t)((n + 15) / 16);
+            L.classes.push_back(ci);
+          } else {
+            c = it->second;
+          }
+          L.win_cls[wi] = c;
+          L.classes[c].count++;
+          masked += is_split;
+          max_tok = std::max(max_tok, n);
+          int64_t lab_count[8] = {0};
+          for (int64_t ld = 0; ld < ext[0]; ++ld)
+            for (int64_t lh = 0; lh < ext[1]; ++lh)
+              for (int64_t lw = 0; lw < ext[2]; ++lw, ++slot) {
+                const int64_t r[3] = {start[0] + ld, start[1] + lh, start[2] + lw};
+                int64_t o[3];
+                uint8_t lab = 0;
+                for (int a = 0; a < 3; ++a) {
+                  o[a] = (r[a] + s[a]) % N[a];  // rolled index r holds original (r + s) mod N
+                  if (!((d->periodic >> a) & 1u) && s[a] > 0 && r[a] >= N[a] - s[a]) lab |= uint8_t(1u << a);
+                }
+                L.perm[slot] = (int32_t)(((b * N[0] + o[0]) * N[1] + o[1]) * N[2] + o[2]);
+                L.labels[slot] = lab;
+                lab_count[lab]++;
+              }
+          for (int l = 0; l < 8; ++l) pairs += lab_count[l] * lab_count[l];
+        }
+  L.win_off[L.n_win] = (int32_t)slot;
+  L.stats.n_tokens = L.n_tok;
+  L.stats.n_windows = L.n_win;
+  L.stats.n_masked = masked;
+  L.stats.n_classes = (int64_t)L.classes.size();
+  L.stats.max_tokens = max_tok;
+  L.stats.allowed_pairs = pairs;
+}
+
+template <class T>
+static hipError_t upload(T** dst, const std::vector<T>& src) {
+  *dst = nullptr;
+  if (src.empty()) return hipSuccess;
+  hipError_t e = hipMalloc((void**)dst, src.size() * sizeof(T));
+  if (e != hipSuccess) return e;
+  return hipMemcpy(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice);
+}
+
+static void free_dev(swin_attn_plan* p) {
+  if (p->device >= 0) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(p->device);
+    hipFree(p->dev.perm);
+    hipFree(p->dev.win_off);
+    hipFree(p->dev.class_win);
+    hipFree(p->dev.classes);
+    hipFree(p->dev.fwd_work);
+    hipFree(p->dev.bwd_work);
+    if (cur >= 0) (void)hipSetDevice(cur);
+  }
+  p->dev = DevTables{};
+}
+
+// Windows per workgroup: enough chunks to fill the chip several times over, few enough
+// that per-class bias/mask setup is amortised.
+static int chunk_for(int64_t count, int heads, int64_t target_wgs, int cap) {
+  int64_t c = (count * heads + target_wgs - 1) / target_wgs;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(cap, c));
+}
+
+// Work items grouped by tile count (one kernel instantiation per count), then by class.
+static void build_work(const std::vector<ClassInfo>& classes, int heads, int64_t target, int cap,
+                       std::vector<WorkItem>& out, std::vector<WorkRange>& ranges) {
+  out.clear();
+  ranges.clear();
+  for (int nqt = 16; nqt >= 1; --nqt) {
+    const int begin = (int)out.size();
+    for (int c = 0; c < (int)classes.size(); ++c) {
+      if (classes[c].nqt != nqt) continue;
+      const int ch = chunk_for(classes[c].count, heads, target, cap);
+      for (int f = 0; f < classes[c].count; f += ch) {
+        WorkItem w{};
+        w.cls = c;
+        w.first = classes[c].first + f;
+        w.count = std::min(ch, classes[c].count - f);
+        out.push_back(w);
+      }
+    }
+    if ((int)out.size() > begin) ranges.push_back(WorkRange{nqt, begin, (int)out.size() - begin});
+  }
+}
+
+}  // namespace swin
+
+using namespace swin;
+
+extern "C" {
+
+const char* swin_status_string(swin_status st) {
+  switch (st) {
+    case SWIN_OK: return "SWIN_OK";
+    case SWIN_ERR_ARG: return "SWIN_ERR_ARG: invalid argument";
+    case SWIN_ERR_UNSUPPORTED: return "SWIN_ERR_UNSUPPORTED: shape or dtype not supported";
+    case SWIN_ERR_WORKSPACE: return "SWIN_ERR_WORKSPACE: workspace missing or too small";
+    case SWIN_ERR_HIP: return "SWIN_ERR_HIP: HIP runtime error";
+  }
+  return "unknown swin_status";
+}
+
+const char* swin_attn_last_error(void) { return g_last_error.c_str(); }
+
+swin_status swin_attn_host_index_map(const swin_attn_desc* desc, int64_t* map, uint8_t* labels) {
+  swin_status st = validate(desc);
+  if (st != SWIN_OK) return st;
+  HostLayout L;
+  build_layout(desc, L);
+  for (int64_t t = 0; t < L.n_tok; ++t) {
+    if (map) map[t] = L.perm[t];
+    if (labels) labels[t] = L.labels[t];
+  }
+  return SWIN_OK;
+}
+
+swin_status swin_attn_host_stats(const swin_attn_desc* desc, swin_attn_stats* out) {
+  if (!out) return fail(SWIN_ERR_ARG, "stats output is NULL");
+  swin_status st = validate(desc);
+  if (st != SWIN_OK) return st;
+  HostLayout L;
+  build_layout(desc, L);
+  *out = L.stats;
+  return SWIN_OK;
+}
+
+swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** out) {
+  if (!out) return fail(SWIN_ERR_ARG, "plan output is NULL");
+  *out = nullptr;
+  swin_status st = validate(desc);
+  if (st != SWIN_OK) return st;
+  HostLayout L;
+  build_layout(desc, L);
+  st = check_kernel_support(desc, L.stats.max_tokens);
+  if (st != SWIN_OK) return st;
+
+  swin_attn_plan* p = new (std::nothrow) swin_attn_plan();
+  if (!p) return fail(SWIN_ERR_ARG, "out of host memory");
+  p->d = *desc;
+  p->n_tok = L.n_tok;
+  p->n_win = L.n_win;
+  p->C = desc->channels;
+  p->nh = desc->heads;
+  p->hd = p->C / p->nh;
+  p->nbins = (2 * desc->window[0] - 1) * (2 * desc->window[1] - 1) * (2 * desc->window[2] - 1);
+  p->tau = desc->scale > 0.f ? desc->scale : 1.0f / std::sqrt((float)p->hd);
+  p->stats = L.stats;
+  p->perm = std::move(L.perm);
+  p->win_off = std::move(L.win_off);
+  p->classes = std::move(L.classes);
+  // class-sorted window list (row-major order inside a class)
+  {
+    int f = 0;
+    for (auto& c : p->classes) {
+      c.first = f;
+      f += c.count;
+    }
+    std::vector<int32_t> fill(p->classes.size(), 0);
+    p->class_win.resize(p->n_win);
+    for (int64_t w = 0; w < p->n_win; ++w) {
+      const int c = L.win_cls[w];
+      p->class_win[p->classes[c].first + fill[c]++] = (int32_t)w;
+    }
+  }
+  build_work(p->classes, p->nh, 4096, 16, p->fwd_work, p->fwd_ranges);
+  build_work(p->classes, p->nh, 2048, 32, p->bwd_work, p->bwd_ranges);
+
+  // saved state and workspace layout
+  const size_t es = desc->dtype == SWIN_BF16 ? 2 : 4;
+  const size_t nt = (size_t)p->n_tok, C = (size_t)p->C;
+  p->saved_qkv = align256(3 * nt * C * es);
+  p->saved_o = align256(nt * C * es);
+  p->saved_lse = align256(nt * (size_t)p->nh * 4);
+  p->saved_total = p->saved_qkv + p->saved_o + p->saved_lse;
+  if (desc->dtype == SWIN_BF16) {
+    // split-K for the weight gradients: enough output-tile x split workgroups to fill the chip
+    auto splits = [&](int64_t M, int64_t N) {
+      const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+      int64_t s = std::max<int64_t>(1, (1024 + tiles - 1) / tiles);
+      s = std::min<int64_t>(s, std::max<int64_t>(1, p->n_tok / 256));
+      return (int)s;
+    };
+    p->wgrad_splits_qkv = splits(3 * C, C);
+    p->wgrad_splits_proj = splits(C, C);
+    auto chunk = [&](int s) {
+      int64_t c = (p->n_tok + s - 1) / s;
+      return (c + 31) / 32 * 32;
+    };
+    p->wgrad_chunk_qkv = chunk(p->wgrad_splits_qkv);
+    p->wgrad_chunk_proj = chunk(p->wgrad_splits_proj);
+    p->bwd_do = align256(nt * C * 2);
+    p->bwd_dqkv = align256(nt * 3 * C * 2);
+    p->bwd_wt = align256((C * C + 3 * C * C) * 2);
+    const size_t part_qkv = (size_t)p->wgrad_splits_qkv * (3 * C * C + 3 * C);
+    const size_t part_proj = (size_t)p->wgrad_splits_proj * (C * C + C);
+    p->bwd_part = align256(std::max(part_qkv, part_proj) * 4);
+    p->bwd_dbias_part = align256(p->bwd_work.size() * (size_t)p->nh * (size_t)p->nbins * 4);
+    p->bwd_total = p->bwd_do + p->bwd_dqkv + p->bwd_wt + p->bwd_part + p->bwd_dbias_part;
+  }
+
+  hipError_t e = hipGetDevice(&p->device);
+  if (e == hipSuccess) e = upload(&p->dev.perm, p->perm);
+  if (e == hipSuccess) e = upload(&p->dev.win_off, p->win_off);
+  if (e == hipSuccess) e = upload(&p->dev.class_win, p->class_win);
+  if (e == hipSuccess) e = upload(&p->dev.classes, p->classes);
+  if (e == hipSuccess) e = upload(&p->dev.fwd_work, p->fwd_work);
+  if (e == hipSuccess) e = upload(&p->dev.bwd_work, p->bwd_work);
+  if (e != hipSuccess) {
+    set_error(std::string("plan upload failed: ") + hipGetErrorString(e));
+    free_dev(p);
+    delete p;
+    return SWIN_ERR_HIP;
+  }
+  *out = p;
+  return SWIN_OK;
+}
+
+void swin_attn_plan_destroy(swin_attn_plan* plan) {
+  if (!plan) return;
+  free_dev(plan);
+  delete plan;
+}
+
+swin_status swin_attn_plan_stats(const swin_attn_plan* plan, swin_attn_stats* out) {
+  if (!plan || !out) return fail(SWIN_ERR_ARG, "plan or output is NULL");
+  *out = plan->stats;
+  return SWIN_OK;
+}
+
+swin_status swin_attn_sizes(const swin_attn_plan* plan, size_t* fwd_ws, size_t* bwd_ws, size_t* saved_bytes) {
+  if (!plan) return fail(SWIN_ERR_ARG, "plan is NULL");
+  if (fwd_ws) *fwd_ws = 0;
+  if (bwd_ws) *bwd_ws = plan->bwd_total;
+  if (saved_bytes) *saved_bytes = plan->saved_total;
+  return SWIN_OK;
+}
+
+static swin_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SWIN_OK;
+  set_error(std::string(what) + ": " + hipGetErrorString(e));
+  return SWIN_ERR_HIP;
+}
+
+swin_status swin_window_gather(const swin_attn_plan* plan, const void* x, void* xw, void* stream) {
+  if (!plan || !x || !xw) return fail(SWIN_ERR_ARG, "NULL plan or buffer");
+  if (x == xw) return fail(SWIN_ERR_ARG, "gather cannot run in place");
+  return hip_status(launch_gather(plan, x, xw, false, (hipStream_t)stream), "gather launch");
+}
+
+swin_status swin_window_scatter(const swin_attn_plan* plan, const void* yw, void* y, void* stream) {
+  if (!plan || !yw || !y) return fail(SWIN_ERR_ARG, "NULL plan or buffer");
+  if (yw == y) return fail(SWIN_ERR_ARG, "scatter cannot run in place");
+  return hip_status(launch_gather(plan, yw, y, true, (hipStream_t)stream), "scatter launch");
+}
+
+swin_status swin_attn_fwd(const swin_attn_plan* plan, const void* x, const void* w_qkv, const void* b_qkv,
+                          const void* w_proj, const void* b_proj, const float* bias_table, void* y, void* saved,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (!plan) return fail(SWIN_ERR_ARG, "plan is NULL");
+  if (!x || !w_qkv || !w_proj || !bias_table || !y) return fail(SWIN_ERR_ARG, "NULL input or output pointer");
+  if (x == y) return fail(SWIN_ERR_ARG, "y must not alias x");
+  void* sv = saved;
+  if (!sv) {
+    if (!ws || ws_bytes < plan->saved_total)
+      return fail(SWIN_ERR_WORKSPACE, "inference call needs a workspace of saved_bytes");
+    sv = ws;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (plan->d.dtype == SWIN_F32)
+    return hip_status(launch_fwd_f32(plan, x, w_qkv, b_qkv, w_proj, b_proj, bias_table, y, sv, s), "fp32 forward");
+  char* base = (char*)sv;
+  void* qkv = base;
+  void* o = base + plan->saved_qkv;
+  float* lse = (float*)(base + plan->saved_qkv + plan->saved_o);
+  hipError_t e = launch_qkv_fwd_bf16(plan, x, w_qkv, b_qkv, qkv, s);
+  if (e == hipSuccess) e = launch_attn_fwd_bf16(plan, qkv, bias_table, o, lse, s);
+  if (e == hipSuccess) e = launch_proj_fwd_bf16(plan, o, w_proj, b_proj, y, s);
+  return hip_status(e, "bf16 forward");
+}
+
+swin_status swin_attn_bwd(const swin_attn_plan* plan, const void* dy, const void* x, const void* w_qkv,
+                          const void* w_proj, const float* bias_table, const void* saved, void* dx, float* dw_qkv,
+                          float* db_qkv, float* dw_proj, float* db_proj, float* dbias_table, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!plan) return fail(SWIN_ERR_ARG, "plan is NULL");
+  if (plan->d.dtype != SWIN_BF16) return fail(SWIN_ERR_UNSUPPORTED, "backward is implemented for bf16 only");
+  if (!dy || !x || !w_qkv || !w_proj || !bias_table || !saved || !dx || !dw_qkv || !dw_proj || !dbias_table)
+    return fail(SWIN_ERR_ARG, "NULL input or output pointer");
+  if (dx == dy || dx == x) return fail(SWIN_ERR_ARG, "dx must not alias dy or x");
+  if (plan->stats.max_tokens > 16 * kMaxBwdTiles)
+    return fail(SWIN_ERR_UNSUPPORTED, "backward supports windows of at most 192 tokens");
+  if (!ws || ws_bytes < plan->bwd_total) return fail(SWIN_ERR_WORKSPACE, "backward workspace too small");
+  return hip_status(launch_bwd_bf16(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_qkv, dw_proj,
+                                    db_proj, dbias_table, ws, (hipStream_t)stream),
+                    "bf16 backward");
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Internal declarations shared by the host plan and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/swin_attn.h"
+
+namespace swin {
+
+// A window class: every window with the same extents and the same wrap-label
+// split shares one bias/mask pattern, so a workgroup that handles one class can
+// load that pattern once and reuse it for all of its windows.
+struct ClassInfo {
+  int32_t ext[3];    // window extents along (D, H, W)
+  int32_t split[3];  // first local index carrying wrap label 1, or ext[a] if the axis does not split
+  int32_t n;         // tokens per window
+  int32_t first;     // offset of this class in the class-sorted window list
+  int32_t count;     // windows in the class
+  int32_t nqt;       // 16-token tiles per window, ceil(n/16)
+};
+
+// A contiguous chunk of one class's windows, processed by one workgroup per head.
+struct WorkItem {
+  int32_t cls;
+  int32_t first;  // offset into the class-sorted window list
+  int32_t count;
+  int32_t pad;
+};
+
+// Work items of one tile count (ceil(n/16)), contiguous in the work list.
+struct WorkRange {
+  int nqt;
+  int begin;
+  int count;
+};
+
+constexpr int kMaxFwdTiles = 16;  // forward: windows of up to 256 tokens
+constexpr int kMaxBwdTiles = 12;  // backward: windows of up to 192 tokens (LDS budget)
+
+struct DevTables {
+  int32_t* perm = nullptr;       // [n_tok] window-major slot -> grid row
+  int32_t* win_off = nullptr;    // [n_win + 1] token offset of each window (row-major window order)
+  int32_t* class_win = nullptr;  // [n_win] window ids sorted by class
+  ClassInfo* classes = nullptr;  // [n_cls]
+  WorkItem* fwd_work = nullptr;  // [n_fwd_work]
+  WorkItem* bwd_work = nullptr;  // [n_bwd_work]
+};
+
+}  // namespace swin
+
+struct swin_attn_plan {
+  swin_attn_desc d;
+  int64_t n_tok = 0, n_win = 0;
+  int C = 0, nh = 0, hd = 0;
+  int nbins = 0;  // entries per head of the bias table
+  float tau = 0.f;
+  int device = -1;
+  swin_attn_stats stats{};
+  std::vector<int32_t> perm, win_off, class_win;
+  std::vector<swin::ClassInfo> classes;
+  std::vector<swin::WorkItem> fwd_work, bwd_work;
+  std::vector<swin::WorkRange> fwd_ranges, bwd_ranges;
+  swin::DevTables dev;
+  // workspace / saved-state layout (bytes)
+  size_t saved_qkv = 0, saved_o = 0, saved_lse = 0, saved_total = 0;
+  size_t bwd_do = 0, bwd_dqkv = 0, bwd_wt = 0, bwd_dd = 0, bwd_part = 0, bwd_dbias_part = 0, bwd_total = 0;
+  int wgrad_splits_qkv = 1, wgrad_splits_proj = 1;
+  int64_t wgrad_chunk_qkv = 0, wgrad_chunk_proj = 0;
+};
+
+namespace swin {
+
+void set_error(const std::string& msg);
+
+// ---- kernel launchers (return hipSuccess or the launch error) ----
+hipError_t launch_gather(const swin_attn_plan* p, const void* x, void* xw, bool scatter, hipStream_t s);
+
+// bf16 path
+hipError_t launch_qkv_fwd_bf16(const swin_attn_plan* p, const void* x, const void* w, const void* b,
+                               void* qkv, hipStream_t s);
+hipError_t launch_attn_fwd_bf16(const swin_attn_plan* p, const void* qkv, const float* table, void* o,
+                                float* lse, hipStream_t s);
+hipError_t launch_proj_fwd_bf16(const swin_attn_plan* p, const void* o, const void* w, const void* b, void* y,
+                                hipStream_t s);
+hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* x, const void* w_qkv,
+                           const void* w_proj, const float* table, const void* saved, void* dx, float* dw_qkv,
+                           float* db_qkv, float* dw_proj, float* db_proj, float* dtable, void* ws,
+                           hipStream_t s);
+
+// fp32 path (forward only)
+hipError_t launch_fwd_f32(const swin_attn_plan* p, const void* x, const void* w_qkv, const void* b_qkv,
+                          const void* w_proj, const void* b_proj, const float* table, void* y, void* saved,
+                          hipStream_t s);
+
+}  // namespace swin

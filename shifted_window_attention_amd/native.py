@@ -1,0 +1,210 @@
+"""ctypes declarations of the C ABI (include/swin_attn.h) and argument marshalling.
+
+Functions take torch tensors (device memory, already allocated by the caller)
+and pass their data pointers and the current HIP stream to the library.
+Host-only entry points (index map, stats) take numpy arrays.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libswinattn.so")
+
+SWIN_OK = 0
+SWIN_F32 = 0
+SWIN_BF16 = 1
+SWIN_PERIODIC_LEVEL = 0x1
+SWIN_PERIODIC_LAT = 0x2
+SWIN_PERIODIC_LON = 0x4
+
+
+class SwinError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = "%s: %s (%s)" % (where, lib.swin_status_string(status).decode(), lib.swin_attn_last_error().decode())
+        super().__init__(msg)
+
+
+class SwinAttnDesc(ctypes.Structure):
+    _fields_ = [("ndim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("batch", ctypes.c_int64),
+                ("grid", ctypes.c_int64 * 3), ("channels", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("window", ctypes.c_int32 * 3), ("shift", ctypes.c_int32 * 3), ("periodic", ctypes.c_uint32),
+                ("scale", ctypes.c_float)]
+
+
+class SwinAttnStats(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int64), ("n_windows", ctypes.c_int64), ("n_masked", ctypes.c_int64),
+                ("n_classes", ctypes.c_int64), ("max_tokens", ctypes.c_int64), ("allowed_pairs", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {f: int(getattr(self, f)) for f, _ in self._fields_}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libswinattn.so is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+                          "or `python -m shifted_window_attention_amd.build_lib`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    P = ctypes.POINTER
+    sigs = {
+        "swin_attn_host_index_map": (st, [P(SwinAttnDesc), P(ctypes.c_int64), P(ctypes.c_uint8)]),
+        "swin_attn_host_stats": (st, [P(SwinAttnDesc), P(SwinAttnStats)]),
+        "swin_attn_plan_create": (st, [P(SwinAttnDesc), P(vp)]),
+        "swin_attn_plan_destroy": (None, [vp]),
+        "swin_attn_plan_stats": (st, [vp, P(SwinAttnStats)]),
+        "swin_attn_sizes": (st, [vp, P(sz), P(sz), P(sz)]),
+        "swin_attn_fwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "swin_attn_bwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "swin_window_gather": (st, [vp, vp, vp, vp]),
+        "swin_window_scatter": (st, [vp, vp, vp, vp]),
+        "swin_status_string": (ctypes.c_char_p, [st]),
+        "swin_attn_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def _check(status, where):
+    if status != SWIN_OK:
+        raise SwinError(status, where)
+
+
+def make_desc(batch, grid, channels, heads, window, shift, periodic=SWIN_PERIODIC_LON, dtype=SWIN_BF16,
+              scale=0.0, ndim=None):
+    d = SwinAttnDesc()
+    grid = tuple(int(g) for g in grid)
+    window = tuple(int(w) for w in window)
+    shift = tuple(int(s) for s in shift)
+    if len(grid) == 2:
+        grid, window, shift = (1,) + grid, (1,) + window, (0,) + shift
+    d.ndim = int(ndim) if ndim is not None else (2 if grid[0] == 1 and window[0] == 1 and shift[0] == 0 else 3)
+    d.dtype = int(dtype)
+    d.batch = int(batch)
+    for a in range(3):
+        d.grid[a] = grid[a]
+        d.window[a] = window[a]
+        d.shift[a] = shift[a]
+    d.channels = int(channels)
+    d.heads = int(heads)
+    d.periodic = int(periodic)
+    d.scale = float(scale)
+    return d
+
+
+def swin_attn_host_index_map(desc):
+    st = SwinAttnStats()
+    _check(lib.swin_attn_host_stats(ctypes.byref(desc), ctypes.byref(st)), "swin_attn_host_stats")
+    n = st.n_tokens
+    m = np.empty(n, dtype=np.int64)
+    lab = np.empty(n, dtype=np.uint8)
+    _check(lib.swin_attn_host_index_map(ctypes.byref(desc), m.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                        lab.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))),
+           "swin_attn_host_index_map")
+    return m, lab
+
+
+def swin_attn_host_stats(desc):
+    st = SwinAttnStats()
+    _check(lib.swin_attn_host_stats(ctypes.byref(desc), ctypes.byref(st)), "swin_attn_host_stats")
+    return st.as_dict()
+
+
+def swin_status_string(status):
+    return lib.swin_status_string(status).decode()
+
+
+def swin_attn_plan_create(desc):
+    h = ctypes.c_void_p()
+    _check(lib.swin_attn_plan_create(ctypes.byref(desc), ctypes.byref(h)), "swin_attn_plan_create")
+    return h
+
+
+def swin_attn_plan_destroy(plan):
+    lib.swin_attn_plan_destroy(plan)
+
+
+def swin_attn_plan_stats(plan):
+    st = SwinAttnStats()
+    _check(lib.swin_attn_plan_stats(plan, ctypes.byref(st)), "swin_attn_plan_stats")
+    return st.as_dict()
+
+
+def swin_attn_sizes(plan):
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.swin_attn_sizes(plan, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "swin_attn_sizes")
+    return a.value, b.value, c.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def swin_attn_fwd(plan, x, w_qkv, b_qkv, w_proj, b_proj, bias_table, y, saved, ws=None, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.swin_attn_fwd(plan, _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_proj), _ptr(b_proj), _ptr(bias_table),
+                             _ptr(y), _ptr(saved), _ptr(ws), ws_bytes, _stream(stream)), "swin_attn_fwd")
+
+
+def swin_attn_bwd(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_qkv, dw_proj, db_proj, dbias_table,
+                  ws, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.swin_attn_bwd(plan, _ptr(dy), _ptr(x), _ptr(w_qkv), _ptr(w_proj), _ptr(bias_table), _ptr(saved),
+                             _ptr(dx), _ptr(dw_qkv), _ptr(db_qkv), _ptr(dw_proj), _ptr(db_proj), _ptr(dbias_table),
+                             _ptr(ws), ws_bytes, _stream(stream)), "swin_attn_bwd")
+
+
+def swin_window_gather(plan, x, xw, stream=None):
+    _check(lib.swin_window_gather(plan, _ptr(x), _ptr(xw), _stream(stream)), "swin_window_gather")
+
+
+def swin_window_scatter(plan, yw, y, stream=None):
+    _check(lib.swin_window_scatter(plan, _ptr(yw), _ptr(y), _stream(stream)), "swin_window_scatter")
+
+
+class Plan:
+    """Owns a plan handle plus the device buffers it needs (saved state, backward workspace).
+
+    Buffers are allocated here with torch (device memory plumbing); the library itself never allocates
+    on the forward/backward path."""
+
+    def __init__(self, desc, device="cuda"):
+        import torch
+        self.desc = desc
+        self.handle = swin_attn_plan_create(desc)
+        self.stats = swin_attn_plan_stats(self.handle)
+        self.fwd_ws, self.bwd_ws, self.saved_bytes = swin_attn_sizes(self.handle)
+        self.device = device
+        self._torch = torch
+
+    def alloc_saved(self):
+        return self._torch.empty(max(self.saved_bytes, 1), dtype=self._torch.uint8, device=self.device)
+
+    def alloc_bwd_ws(self):
+        return self._torch.empty(max(self.bwd_ws, 1), dtype=self._torch.uint8, device=self.device)
+
+    def close(self):
+        if self.handle is not None:
+            swin_attn_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,126 @@
+"""The C-ABI library loads, exports every declared symbol, and its host-side
+window layout is bit-exact against the oracle (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import swin_oracle as O
+from workloads import get_config
+from workloads.configs import ORDER
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swin_attn.h")
+
+
+@pytest.fixture(scope="module")
+def native():
+    from shifted_window_attention_amd import native
+    return native
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swin_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for must in ("swin_attn_fwd", "swin_attn_bwd", "swin_window_gather", "swin_window_scatter",
+                 "swin_attn_plan_create", "swin_attn_plan_destroy", "swin_attn_sizes", "swin_status_string"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(native):
+    raw = ctypes.CDLL(native.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def _desc(native, cfg, module=0, dtype=None):
+    return native.make_desc(cfg.batch, cfg.grid, cfg.channels, cfg.heads, cfg.window, cfg.shifts[module],
+                            cfg.periodic, native.SWIN_BF16 if (dtype or cfg.dtype) == "bf16" else native.SWIN_F32)
+
+
+CASES = [(n, m) for n in ORDER for m in range(get_config(n).modules)]
+
+
+@pytest.mark.parametrize("name,module", CASES)
+def test_host_index_map_bit_exact(native, name, module):
+    cfg = get_config(name)
+    lay = O.window_layout(cfg.batch, cfg.grid, cfg.window, cfg.shifts[module], cfg.periodic)
+    m, lab = native.swin_attn_host_index_map(_desc(native, cfg, module))
+    assert np.array_equal(m, lay.perm)
+    assert np.array_equal(lab, lay.labels)
+
+
+@pytest.mark.parametrize("name,module", CASES)
+def test_host_stats_match_oracle(native, name, module):
+    cfg = get_config(name)
+    lay = O.window_layout(cfg.batch, cfg.grid, cfg.window, cfg.shifts[module], cfg.periodic)
+    st = native.swin_attn_host_stats(_desc(native, cfg, module))
+    assert st["n_tokens"] == lay.n_tokens
+    assert st["n_windows"] == len(lay.windows)
+    assert st["max_tokens"] == max(w.n for w in lay.windows)
+    assert st["allowed_pairs"] == O.allowed_pairs(lay)
+    assert st["n_masked"] == sum(len(np.unique(lay.labels[w.tok_off:w.tok_off + w.n])) > 1 for w in lay.windows)
+
+
+def test_host_index_map_random_small_grids(native):
+    rng = np.random.default_rng(3)
+    for _ in range(40):
+        nd = int(rng.integers(2, 4))
+        grid = [1 if nd == 2 else int(rng.integers(1, 7))] + [int(rng.integers(1, 20)) for _ in range(2)]
+        win = [int(rng.integers(1, g + 1)) for g in grid]
+        if nd == 2:
+            win[0] = 1
+        sh = [int(rng.integers(0, w)) for w in win]
+        if nd == 2:
+            sh[0] = 0
+        per = int(rng.integers(0, 8))
+        b = int(rng.integers(1, 3))
+        d = native.make_desc(b, grid, 8, 1, win, sh, per, native.SWIN_F32, ndim=nd)
+        lay = O.window_layout(b, grid, win, sh, per)
+        m, lab = native.swin_attn_host_index_map(d)
+        assert np.array_equal(m, lay.perm), (grid, win, sh, per)
+        assert np.array_equal(lab, lay.labels), (grid, win, sh, per)
+
+
+def _status(native, **kw):
+    base = dict(batch=1, grid=(1, 8, 8), channels=64, heads=2, window=(1, 4, 4), shift=(0, 2, 2),
+                periodic=4, dtype=native.SWIN_BF16)
+    base.update(kw)
+    d = native.make_desc(**base)
+    st = native.SwinAttnStats()
+    return native.lib.swin_attn_host_stats(ctypes.byref(d), ctypes.byref(st))
+
+
+def test_descriptor_errors(native):
+    ARG = 1
+    assert _status(native) == 0
+    assert _status(native, shift=(0, 4, 2)) == ARG          # shift >= window
+    assert _status(native, window=(1, 9, 4)) == ARG         # window > grid
+    assert _status(native, channels=63) == ARG              # C % heads
+    assert _status(native, batch=0) == ARG
+    assert _status(native, periodic=8) == ARG
+    assert _status(native, dtype=7) == ARG
+    assert native.lib.swin_attn_host_stats(None, ctypes.byref(native.SwinAttnStats())) == ARG
+
+
+def test_plan_create_rejects_before_touching_the_device(native):
+    UNSUP = 2
+    h = ctypes.c_void_p()
+    d = native.make_desc(1, (1, 8, 8), 128, 2, (1, 4, 4), (0, 2, 2))   # head_dim 64 in bf16
+    assert native.lib.swin_attn_plan_create(ctypes.byref(d), ctypes.byref(h)) == UNSUP
+    assert h.value is None
+    d = native.make_desc(1, (1, 32, 32), 64, 2, (1, 17, 16), (0, 0, 0))   # 272-token windows
+    assert native.lib.swin_attn_plan_create(ctypes.byref(d), ctypes.byref(h)) == UNSUP
+    assert b"256" in native.lib.swin_attn_last_error()
+
+
+def test_status_strings(native):
+    for s in range(5):
+        assert native.swin_status_string(s).startswith("SWIN_")

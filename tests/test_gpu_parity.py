@@ -1,0 +1,254 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on the same seeded inputs.
+
+Bars: gather/scatter index maps bit-exact; fp32 path max-abs 1e-5; bf16 path max-abs 2e-2
+on per-token outputs (y, dx) and 2e-2 * max(1, |ref|_inf) on reduced gradients (dW, db, dT)."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import log, run_chain, to_dev, from_dev, ModuleOnDevice
+from tests.oracle_runner import chain_full, chain_masked_dy, chain_sampled, layouts
+from workloads import get_config, make_inputs
+from workloads.configs import small_variant
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+TOL_F32 = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from shifted_window_attention_amd import native  # noqa: F401  (raises if the library is missing)
+
+
+def _maxabs(a, b):
+    return float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
+
+
+def _check_grads(got, ref, label):
+    for i, (gm, rm) in enumerate(zip(got, ref)):
+        for k in ("w_qkv", "b_qkv", "w_proj", "b_proj", "table"):
+            r = rm[k].reshape(-1)
+            g = gm[k].reshape(-1)
+            err = _maxabs(g, r)
+            bound = TOL_BF16 * max(1.0, float(np.abs(r).max()))
+            log("  %s module %d d%s max-abs %.3e (bound %.3e, |ref| %.3e)" % (label, i, k, err, bound,
+                                                                             np.abs(r).max()))
+            assert err <= bound, (label, i, k, err, bound)
+
+
+# ---------------------------------------------------------------- index maps
+@pytest.mark.parametrize("name", ["tiny", "om4", "ragged", "highres", "levels3d"])
+def test_gather_scatter_bit_exact(name):
+    import torch
+    from shifted_window_attention_amd import native as N
+    cfg = get_config(name)
+    for mi, shift in enumerate(cfg.shifts):
+        log("gather/scatter", name, "module", mi)
+        desc = N.make_desc(cfg.batch, cfg.grid, cfg.channels, cfg.heads, cfg.window, shift, cfg.periodic,
+                           N.SWIN_BF16 if cfg.dtype == "bf16" else N.SWIN_F32)
+        plan = N.Plan(desc)
+        perm, _ = N.swin_attn_host_index_map(desc)
+        es = 2 if cfg.dtype == "bf16" else 4
+        words = cfg.channels * es // 2
+        # integer-coded grid: every 16-bit word of row g holds (g * 31 + c) mod 2^16
+        g = torch.arange(cfg.n_tokens, dtype=torch.int64, device="cuda")[:, None]
+        c = torch.arange(words, dtype=torch.int64, device="cuda")[None, :]
+        x = ((g * 31 + c) % 65536 - 32768).to(torch.int16)
+        xw = torch.empty_like(x)
+        N.swin_window_gather(plan.handle, x, xw)
+        back = torch.empty_like(x)
+        N.swin_window_scatter(plan.handle, xw, back)
+        torch.cuda.synchronize()
+        assert torch.equal(xw, x[torch.from_numpy(perm).cuda()])
+        assert torch.equal(back, x)
+        plan.close()
+
+
+# ---------------------------------------------------------------- fp32 path
+def test_fwd_tiny_f32():
+    cfg = get_config("tiny")
+    log("fp32 forward", cfg.description)
+    inp = make_inputs(cfg)
+    got = run_chain(cfg, inp, with_bwd=False)
+    ref = chain_full(cfg, inp, with_bwd=False)
+    err = _maxabs(got["y"], ref["y"])
+    log("  y max-abs %.3e" % err)
+    assert err <= TOL_F32
+
+
+# ---------------------------------------------------------------- bf16, oracle at small sizes
+SMALL = [
+    ("om4", dict(grid=(1, 30, 48))),              # 40 windows of 72 tokens, ragged GEMM tails (N = 576)
+    ("ragged", dict(grid=(1, 41, 57))),           # edge windows of 8x9, 1x16 and 1x9 tokens
+    ("highres", dict(grid=(1, 36, 48))),          # W-MSA then SW-MSA, C = 512, 16 heads
+    ("levels3d", dict(grid=(4, 18, 36))),         # 3-D windows masked on level and lat
+    ("om4", dict(grid=(1, 12, 24), batch=3)),     # batch > 1, few windows
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=lambda v: v if isinstance(v, str) else "x".join(map(str, v["grid"])))
+def test_fwd_bwd_small_vs_oracle(name, kw):
+    cfg = small_variant(get_config(name), **kw)
+    log("bf16 fwd+bwd", name, cfg.grid, "batch", cfg.batch)
+    inp = make_inputs(cfg)
+    got = run_chain(cfg, inp)
+    ref = chain_full(cfg, inp)
+    ey, edx = _maxabs(got["y"], ref["y"]), _maxabs(got["dx"], ref["dx"])
+    log("  y max-abs %.3e  dx max-abs %.3e" % (ey, edx))
+    assert ey <= TOL_BF16 and edx <= TOL_BF16
+    _check_grads(got["grads"], ref["grads"], name)
+
+
+def test_lse_matches_oracle_small():
+    import torch
+    cfg = small_variant(get_config("ragged"), grid=(1, 41, 57))
+    inp = make_inputs(cfg)
+    got = run_chain(cfg, inp, with_bwd=False)
+    ref = chain_full(cfg, inp, with_bwd=False)
+    m = got["mods"][0]
+    n, nh = cfg.n_tokens, cfg.heads
+    sv = m.saved
+    # saved layout: qkv (3 C n bf16), o (C n bf16), lse [nh][n] fp32, each 256-byte aligned
+    a = lambda v: (v + 255) // 256 * 256
+    start = a(3 * n * cfg.channels * 2) + a(n * cfg.channels * 2)
+    lse2 = sv[start:start + 4 * n * nh].view(torch.float32).reshape(nh, n).double().cpu().numpy()
+    lse_nat = lse2 / np.log2(np.e)
+    err = _maxabs(lse_nat.T, ref["lse"][0])
+    log("  lse max-abs %.3e" % err)
+    assert err <= TOL_BF16
+
+
+# ---------------------------------------------------------------- bf16, full sizes, sampled windows
+FULL = ["om4", "ragged", "highres", "levels3d"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    cfg = get_config(name)
+    log("full size", name, cfg.description)
+    inp = make_inputs(cfg, bias_scale=0.0)
+    got = run_chain(cfg, inp, with_bias=True)
+    lays = layouts(cfg)
+    last = lays[-1]
+    nwin = len(last.windows)
+    rng = np.random.default_rng(7)
+    # sampled windows: first, last, every mask-split class edge, and random ones
+    masked = [i for i, w in enumerate(last.windows)
+              if len(np.unique(last.labels[w.tok_off:w.tok_off + w.n])) > 1]
+    small = [i for i, w in enumerate(last.windows) if w.n < max(v.n for v in last.windows)]
+    pick = sorted(set([0, nwin - 1] + masked[:2] + masked[-1:] + small[:2] + small[-1:]
+                      + rng.integers(0, nwin, 3).tolist()))
+    C = cfg.channels
+    ref = chain_sampled(cfg, inp, pick)
+    ey = _maxabs(got["y"].reshape(-1, C)[ref["y_tokens"]], ref["y"])
+    edx = _maxabs(got["dx"].reshape(-1, C)[ref["dx_tokens"]], ref["dx"])
+    log("  sampled %d windows: y max-abs %.3e  dx max-abs %.3e" % (len(pick), ey, edx))
+    assert ey <= TOL_BF16 and edx <= TOL_BF16
+    # an exact property at any size: db_proj == sum over tokens of dy
+    dbp_ref = inp.dy.reshape(-1, C).sum(0)
+    e = _maxabs(got["grads"][-1]["b_proj"], dbp_ref)
+    log("  db_proj vs sum(dy): %.3e" % e)
+    assert e <= TOL_BF16 * max(1.0, np.abs(dbp_ref).max())
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_masked_dy(name):
+    """Full-size launch with dy zero outside a few sampled windows of the last module: every
+    reduction (dW, db, dT) and dx then involve only windows the oracle computes in full."""
+    cfg = get_config(name)
+    log("full size, masked dy", name, cfg.description)
+    inp = make_inputs(cfg)
+    lay = layouts(cfg)[-1]
+    nwin = len(lay.windows)
+    masked = [i for i, w in enumerate(lay.windows) if len(np.unique(lay.labels[w.tok_off:w.tok_off + w.n])) > 1]
+    small = [i for i, w in enumerate(lay.windows) if w.n < max(v.n for v in lay.windows)]
+    pick = sorted(set([0, nwin // 2, nwin - 1] + masked[:1] + masked[-1:] + small[:1] + small[-1:]))
+    C = cfg.channels
+    keep = np.zeros(cfg.n_tokens, dtype=bool)
+    for i in pick:
+        w = lay.windows[i]
+        keep[lay.perm[w.tok_off:w.tok_off + w.n]] = True
+    dy_masked = np.where(keep[:, None], inp.dy.reshape(-1, C), 0.0).reshape(inp.dy.shape)
+    dev = np.where(keep[:, None], inp.dy_dev.reshape(-1, C), 0).reshape(inp.dy_dev.shape).astype(inp.dy_dev.dtype)
+    inp.dy, inp.dy_dev = dy_masked, dev
+    got = run_chain(cfg, inp)
+    ref = chain_masked_dy(cfg, inp, pick, dy_masked)
+    edx = _maxabs(got["dx"].reshape(-1, C)[ref["dx_tokens"]], ref["dx"])
+    log("  %d windows: dx max-abs %.3e" % (len(pick), edx))
+    assert edx <= TOL_BF16
+    # dx vanishes on every token the sampled windows do not reach
+    off = np.ones(cfg.n_tokens, dtype=bool)
+    off[ref["dx_tokens"]] = False
+    assert np.all(got["dx"].reshape(-1, C)[off] == 0.0)
+    _check_grads(got["grads"], ref["grads"], name)
+
+
+@pytest.mark.parametrize("name", ["om4", "ragged"])
+def test_full_size_vs_oracle(name):
+    """Every output at the full size (the oracle finishes these in seconds)."""
+    cfg = get_config(name)
+    log("full size, full oracle", name, cfg.description)
+    inp = make_inputs(cfg)
+    got = run_chain(cfg, inp)
+    ref = chain_full(cfg, inp)
+    ey, edx = _maxabs(got["y"], ref["y"]), _maxabs(got["dx"], ref["dx"])
+    log("  y max-abs %.3e  dx max-abs %.3e" % (ey, edx))
+    assert ey <= TOL_BF16 and edx <= TOL_BF16
+    _check_grads(got["grads"], ref["grads"], name)
+
+
+def test_backward_is_deterministic():
+    import torch
+    cfg = get_config("om4")
+    log("determinism", cfg.description)
+    inp = make_inputs(cfg)
+    m = ModuleOnDevice(cfg, 0, inp.modules[0])
+    x = to_dev(inp.x_dev, "bf16")
+    dy = to_dev(inp.dy_dev, "bf16")
+    y1 = m.fwd(x).clone()
+    dx1, g1 = m.bwd(dy, x)
+    dx1 = dx1.clone()
+    g1 = {k: v.clone() for k, v in g1.items()}
+    y2 = m.fwd(x)
+    dx2, g2 = m.bwd(dy, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(dx1, dx2)
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+
+
+def test_abi_errors_on_device():
+    import ctypes
+    import torch
+    from shifted_window_attention_amd import native as N
+    cfg = small_variant(get_config("om4"), grid=(1, 12, 24))
+    inp = make_inputs(cfg)
+    m = ModuleOnDevice(cfg, 0, inp.modules[0])
+    x = to_dev(inp.x_dev, "bf16")
+    y = torch.empty_like(x)
+    L = N.lib
+    h = m.plan.handle
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = L.swin_attn_fwd(h, None, p(m.w_qkv), None, p(m.w_proj), None, p(m.table), p(y), p(m.saved), None, 0, None)
+    assert st == 1  # NULL input
+    st = L.swin_attn_fwd(h, p(x), p(m.w_qkv), None, p(m.w_proj), None, p(m.table), p(y), None, None, 0, None)
+    assert st == 3  # inference call without workspace
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    st = L.swin_attn_bwd(h, p(x), p(x), p(m.w_qkv), p(m.w_proj), p(m.table), p(m.saved), p(y), p(y), None, p(y),
+                         None, p(y), p(small_ws), 16, None)
+    assert st == 3  # workspace too small
+    st = L.swin_attn_fwd(h, p(x), p(m.w_qkv), None, p(m.w_proj), None, p(m.table), p(x), p(m.saved), None, 0, None)
+    assert st == 1  # y aliases x
+    # fp32 plans have no backward
+    tiny = get_config("tiny")
+    d = N.make_desc(tiny.batch, tiny.grid, tiny.channels, tiny.heads, tiny.window, tiny.shifts[0], tiny.periodic,
+                    N.SWIN_F32)
+    pl = N.Plan(d)
+    st = L.swin_attn_bwd(pl.handle, p(x), p(x), p(m.w_qkv), p(m.w_proj), p(m.table), p(m.saved), p(y), p(y), None,
+                         p(y), None, p(y), p(small_ws), 16, None)
+    assert st == 2
+    torch.cuda.synchronize()
