@@ -1,0 +1,313 @@
+"""Throughput of shifted-window attention forward + backward on one MI355X.
+
+One step = the whole hot path on the 540x1080-token, C=512, 16-head, 12x12-window
+workload (a 2160x4320 field after 4x4 patch embedding): W-MSA forward, SW-MSA
+(shift 6,6) forward, SW-MSA backward, W-MSA backward, each module being gather +
+QKV GEMM + window attention + proj GEMM + scatter and their backward. Inputs are
+seeded synthetic data resident in HBM before the timed region.
+
+Prints one JSON line on stdout:
+  value = token-blocks per second (tokens x modules per step / step time),
+  tflops / mfma_peak_frac = algorithmic FLOPs per second and their fraction of the
+  dense bf16 MFMA peak, roofline = the dominant kernel against its bound (stage
+  durations from HIP events recorded on the library's stream inside the timed region),
+  cpu_baseline = the fp64 oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-seconds S]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12   # 256 CUs x 4096 dense bf16 FLOP/clk x 2.4 GHz = 2516.6
+PEAK_HBM_GBS = 8000.0
+METRIC = "window-attn fwd+bwd tokens/s and TFLOPS (% of MI355X bf16 MFMA peak)"
+
+FWD_STAGES = ["qkv_gemm", "attn_fwd", "proj_gemm"]
+BWD_STAGES = ["w_transpose", "dproj_gemm", "wgrad_proj", "attn_bwd", "dbias_reduce", "dgrad_qkv", "wgrad_qkv"]
+# stage -> (kernel name as rocprofv3 reports it, source file) for the single-kernel stages
+STAGE_KERNEL = {
+    "qkv_gemm": ("k_gemm_nt", "gemm.hip"), "proj_gemm": ("k_gemm_nt", "gemm.hip"),
+    "dproj_gemm": ("k_gemm_nt", "gemm.hip"), "dgrad_qkv": ("k_gemm_nt", "gemm.hip"),
+    "attn_fwd": ("k_attn_fwd", "attn_fwd.hip"), "attn_bwd": ("k_attn_bwd", "attn_bwd.hip"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls the bench needs for events."""
+
+    def __init__(self):
+        self.l = ctypes.CDLL("libamdhip64.so")
+        self.l.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.l.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.l.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.l.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.l.hipEventCreate(ctypes.byref(h)) == 0
+            arr[i] = h
+        return arr
+
+    def elapsed_ms(self, a, b):
+        f = ctypes.c_float()
+        assert self.l.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return float(f.value)
+
+    def destroy(self, arr):
+        for h in arr:
+            self.l.hipEventDestroy(h)
+
+
+def stage_flops_bytes(cfg, pairs):
+    """Algorithmic FLOPs and HBM bytes per launch of each stage for one module."""
+    N, C, nh, hd = cfg.n_tokens, cfg.channels, cfg.heads, cfg.head_dim
+    core = 4 * hd * pairs * nh
+    tok_head = N * nh
+    f = {"qkv_gemm": 2 * N * C * 3 * C, "attn_fwd": core, "proj_gemm": 2 * N * C * C,
+         "w_transpose": 0, "dproj_gemm": 2 * N * C * C, "wgrad_proj": 2 * N * C * C, "attn_bwd": 2 * core,
+         "dbias_reduce": 0, "dgrad_qkv": 2 * N * 3 * C * C, "wgrad_qkv": 2 * N * 3 * C * C}
+    # bytes the stage must move as designed: operands in, results out (bf16 = 2 B)
+    b = {"qkv_gemm": 2 * N * C + 2 * N * 3 * C,                     # x in, q/k/v out
+         "attn_fwd": tok_head * (3 * 64 + 64 + 4),                  # q, k, v in; o, lse out
+         "proj_gemm": 2 * N * C * 2,                                # o in, y out
+         "dproj_gemm": 2 * N * C * 2,                               # dy in, dO out
+         "wgrad_proj": 2 * N * C * 2,                               # dy, o in
+         "attn_bwd": tok_head * (5 * 64 + 4 + 3 * 64),              # q k v o dO lse in; dq dk dv out
+         "dgrad_qkv": 2 * N * 3 * C + 2 * N * C,                    # dqkv in, dx out
+         "wgrad_qkv": 2 * N * 3 * C + 2 * N * C,                    # dqkv, x in
+         "w_transpose": 2 * 2 * 4 * C * C, "dbias_reduce": 0}
+    return f, b
+
+
+def source_sha(fname):
+    with open(os.path.join(ROOT, "shifted_window_attention_amd", "csrc", fname), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def traffic_for(stage, per_launch_ref):
+    """HBM bytes per launch from committed rocprofv3 PMC counters, if they were taken on the
+    current kernel source (else None)."""
+    kern = STAGE_KERNEL.get(stage)
+    if not kern:
+        return None
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except ValueError:
+        return None
+    rec = data.get(stage)
+    if not rec or rec.get("source_sha") != source_sha(kern[1]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, seconds):
+    """The fp64 oracle, as it is, on whole windows of both modules until ~`seconds` of CPU work."""
+    import numpy as np
+    from oracle import swin_oracle as O
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [os.cpu_count() or 1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    lays = [O.window_layout(cfg.batch, cfg.grid, cfg.window, s, cfg.periodic) for s in cfg.shifts]
+    ps = [O.Params(m.w_qkv, m.b_qkv, m.w_proj, m.b_proj, m.table) for m in inp.modules]
+    xws = [O.gather(inp.x, lay) for lay in lays]
+    dyws = [O.gather(inp.dy, lay) for lay in lays]
+    rng = np.random.default_rng(11)
+    tokens = 0
+    windows = 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    while elapsed < seconds:
+        for mi, lay in enumerate(lays):
+            ids = sorted(rng.choice(len(lay.windows), 4, replace=False).tolist())
+            O.windows_fwd(xws[mi], ps[mi], lay, cfg.heads, window_ids=ids)
+            O.windows_bwd(dyws[mi], xws[mi], ps[mi], lay, cfg.heads, window_ids=ids)
+            tokens += sum(lay.windows[i].n for i in ids)
+            windows += len(ids)
+        elapsed = time.perf_counter() - t0
+    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d random whole windows (fwd+bwd, float64 oracle) split over the W-MSA and SW-MSA modules "
+                      "of the 540x1080 C=512 workload, %.1f s of CPU work; the full-grid gather is outside the "
+                      "timed part; CPU %s, %d cores visible" % (windows, elapsed, platform.processor() or
+                                                                 platform.machine(), os.cpu_count() or 0),
+            "seconds": round(elapsed, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(see DESIGN.md for how the workload would shard); got --gpus %d" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from __graft_entry__ import _ensure_built
+    _ensure_built()
+    from shifted_window_attention_amd import native as N
+    from tests.gpu_util import ModuleOnDevice, to_dev
+    from workloads import get_config, make_inputs
+
+    cfg = get_config("highres")
+    log("bench: generating inputs", cfg.description)
+    inp = make_inputs(cfg, bias_scale=0.0)
+    torch.cuda.set_device(0)
+    mods = [ModuleOnDevice(cfg, i, p) for i, p in enumerate(inp.modules)]
+    x = to_dev(inp.x_dev, "bf16")
+    dy = to_dev(inp.dy_dev, "bf16")
+    C = cfg.channels
+    y1 = torch.empty_like(x)
+    y2 = torch.empty_like(x)
+    dx2 = torch.empty_like(x)
+    dx1 = torch.empty_like(x)
+    grads = [{"w_qkv": torch.empty(3 * C, C, dtype=torch.float32, device="cuda"),
+              "b_qkv": torch.empty(3 * C, dtype=torch.float32, device="cuda"),
+              "w_proj": torch.empty(C, C, dtype=torch.float32, device="cuda"),
+              "b_proj": torch.empty(C, dtype=torch.float32, device="cuda"),
+              "table": torch.empty_like(m.table)} for m in mods]
+    stream = torch.cuda.current_stream()
+
+    def step():
+        m1, m2 = mods
+        N.swin_attn_fwd(m1.plan.handle, x, m1.w_qkv, m1.b_qkv, m1.w_proj, m1.b_proj, m1.table, y1, m1.saved,
+                        stream=stream)
+        N.swin_attn_fwd(m2.plan.handle, y1, m2.w_qkv, m2.b_qkv, m2.w_proj, m2.b_proj, m2.table, y2, m2.saved,
+                        stream=stream)
+        g = grads[1]
+        N.swin_attn_bwd(m2.plan.handle, dy, y1, m2.w_qkv, m2.w_proj, m2.table, m2.saved, dx2, g["w_qkv"],
+                        g["b_qkv"], g["w_proj"], g["b_proj"], g["table"], m2.ws, stream=stream)
+        g = grads[0]
+        N.swin_attn_bwd(m1.plan.handle, dx2, x, m1.w_qkv, m1.w_proj, m1.table, m1.saved, dx1, g["w_qkv"],
+                        g["b_qkv"], g["w_proj"], g["b_proj"], g["table"], m1.ws, stream=stream)
+
+    log("bench: warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    hip = Hip()
+    per_step = 2 * (len(FWD_STAGES) + 1) + 2 * (len(BWD_STAGES) + 1)
+    ev = hip.events(per_step * args.steps)
+    t_start, t_end = hip.events(2)
+    N.swin_attn_trace_events(ev)
+    torch.cuda.synchronize()
+    assert hip.l.hipEventRecord(t_start, stream.cuda_stream) == 0
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    assert hip.l.hipEventRecord(t_end, stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    recorded = N.swin_attn_trace_cursor()
+    N.swin_attn_trace_events(None)
+    assert recorded == per_step * args.steps, (recorded, per_step * args.steps)
+    total_ms = hip.elapsed_ms(t_start, t_end)
+    ms_step = total_ms / args.steps
+
+    # per-stage durations: each call's events bracket its stages
+    durations = {s: [] for s in FWD_STAGES + BWD_STAGES}
+    k = 0
+    for _ in range(args.steps):
+        for stages in (FWD_STAGES, FWD_STAGES, BWD_STAGES, BWD_STAGES):
+            for j, s in enumerate(stages):
+                durations[s].append(hip.elapsed_ms(ev[k + j], ev[k + j + 1]))
+            k += len(stages) + 1
+    hip.destroy(ev)
+
+    pairs = [m.plan.stats["allowed_pairs"] for m in mods]
+    flops_step = 0
+    bytes_mod = []
+    flops_mod = []
+    for pr in pairs:
+        f, b = stage_flops_bytes(cfg, pr)
+        flops_mod.append(f)
+        bytes_mod.append(b)
+        flops_step += sum(f.values())
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+    tokens_step = cfg.n_tokens * cfg.modules
+    value = tokens_step / (ms_step * 1e-3)
+
+    kernels = {}
+    for s, d in durations.items():
+        avg = float(np.mean(d))
+        fl = float(np.mean([f[s] for f in flops_mod]))
+        by = float(np.mean([b[s] for b in bytes_mod]))
+        rec = {"avg_ms": round(avg, 4), "ms_per_step": round(float(np.sum(d)) / args.steps, 4),
+               "launches_per_step": len(d) // args.steps}
+        if fl:
+            rec["tflops"] = round(fl / (avg * 1e-3) / 1e12, 1)
+            rec["mfma_frac"] = round(rec["tflops"] / PEAK_BF16_TFLOPS, 4)
+        if by:
+            rec["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
+            rec["hbm_frac"] = round(rec["gbs"] / PEAK_HBM_GBS, 4)
+        kernels[s] = rec
+    # dominant single-kernel stage
+    dom = max((s for s in kernels if s in STAGE_KERNEL), key=lambda s: kernels[s]["ms_per_step"])
+    dk = kernels[dom]
+    is_core = dom.startswith("attn")
+    dom_flops = float(np.mean([f[dom] for f in flops_mod]))
+    dom_bytes = float(np.mean([b[dom] for b in bytes_mod]))
+    if is_core:
+        roof = {"bound": "hbm", "achieved": dk["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dk["gbs"] / PEAK_HBM_GBS, 4)}
+        per_launch_ref = dom_bytes
+    else:
+        roof = {"bound": "mfma", "achieved": dk["tflops"], "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                "frac": round(dk["tflops"] / PEAK_BF16_TFLOPS, 4)}
+        per_launch_ref = dom_flops
+    roof["kernel"] = STAGE_KERNEL[dom][0]
+    roof["stage"] = dom
+    roof["avg_launch_ms"] = dk["avg_ms"]
+    roof["algorithmic_per_launch"] = per_launch_ref
+    roof["traffic"] = traffic_for(dom, per_launch_ref)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: oracle CPU baseline (~%.0f s)" % args.cpu_seconds)
+        cpu = cpu_baseline(cfg, inp, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "swin W-MSA -> SW-MSA chain fwd+bwd, 540x1080 lat-lon tokens (2160x4320 field after "
+                               "4x4 patch embedding), batch 1, C=512, 16 heads x 32, window 12x12, shift (6,6), "
+                               "lon periodic, lat masked",
+                   "tokens": cfg.n_tokens, "modules": cfg.modules, "global_batch": cfg.batch, "seq_len": 144,
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "algorithmic_gflop_per_step": round(flops_step / 1e9, 2),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "roofline": roof, "kernels": kernels, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

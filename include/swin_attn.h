@@ -216,6 +216,22 @@ swin_status swin_attn_bwd(const swin_attn_plan* plan, const void* dy, const void
 swin_status swin_window_gather(const swin_attn_plan* plan, const void* x, void* xw, void* stream);
 swin_status swin_window_scatter(const swin_attn_plan* plan, const void* yw, void* y, void* stream);
 
+/*
+ * Stage tracing (a profiling aid for callers that time the library's kernels with HIP
+ * events). swin_attn_trace_events installs, for the calling thread, an array of
+ * `capacity` hipEvent_t handles (created by the caller) and resets a cursor to 0; from then
+ * on every swin_attn_fwd / swin_attn_bwd call on this thread records the next event on its
+ * stream at its start and after each of its stages, until the array is full:
+ *   forward  (bf16): start | QKV GEMM | attention | proj GEMM                 -> 4 events
+ *   backward (bf16): start | weight transposes | dO GEMM | dW_proj GEMM | attention backward
+ *                    | dT reduction | dx GEMM | dW_qkv GEMM                   -> 8 events
+ * The elapsed time between consecutive events is the duration of that stage. events = NULL
+ * uninstalls. swin_attn_trace_cursor returns how many events have been recorded since the
+ * last install. Recording failures are reported as SWIN_ERR_HIP by the fwd/bwd call.
+ */
+swin_status swin_attn_trace_events(void* const* events, int capacity);
+int swin_attn_trace_cursor(void);
+
 /* Static message for a status code. */
 const char* swin_status_string(swin_status status);
 /* Message describing the last failure on the calling thread ("" if none). */

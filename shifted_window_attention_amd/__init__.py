@@ -13,5 +13,5 @@ from .native import (  # noqa: F401
     SWIN_BF16, SWIN_F32, SWIN_OK, SWIN_PERIODIC_LAT, SWIN_PERIODIC_LEVEL, SWIN_PERIODIC_LON, SwinAttnDesc,
     SwinAttnStats, SwinError, lib, make_desc, swin_attn_bwd, swin_attn_fwd, swin_attn_host_index_map,
     swin_attn_host_stats, swin_attn_plan_create, swin_attn_plan_destroy, swin_attn_plan_stats, swin_attn_sizes,
-    swin_status_string, swin_window_gather, swin_window_scatter, Plan,
+    swin_status_string, swin_window_gather, swin_window_scatter, swin_attn_trace_events, swin_attn_trace_cursor, Plan,
 )

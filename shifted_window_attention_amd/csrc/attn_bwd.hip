@@ -344,13 +344,17 @@ hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* 
   float* part = (float*)(w + p->bwd_do + p->bwd_dqkv + p->bwd_wt);
   float* dbias_part = (float*)(w + p->bwd_do + p->bwd_dqkv + p->bwd_wt + p->bwd_part);
 
-  hipError_t e = launch_transpose_bf16(w_proj, wprojT, C, C, s);
+  hipError_t e = trace_mark(s);
+  if (e == hipSuccess) e = launch_transpose_bf16(w_proj, wprojT, C, C, s);
   if (e == hipSuccess) e = launch_transpose_bf16(w_qkv, wqkvT, 3 * C, C, s);
+  if (e == hipSuccess) e = trace_mark(s);
   // proj backward: dO = gather(dy) W_proj (head-split), dW_proj = gather(dy)^T o, db_proj
   if (e == hipSuccess) e = launch_dproj_bf16(p, dy, wprojT, dO, s);
+  if (e == hipSuccess) e = trace_mark(s);
   if (e == hipSuccess)
     e = launch_wgrad_bf16((const bf16*)dy, C, p->dev.perm, o, C, nullptr, p->n_tok, C, C, p->wgrad_splits_proj,
                           p->wgrad_chunk_proj, part, dw_proj, db_proj, s);
+  if (e == hipSuccess) e = trace_mark(s);
   if (e != hipSuccess) return e;
   // attention core backward
   BwdArgs a{};
@@ -377,17 +381,21 @@ hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* 
     kBwd[r.nqt](a, r.count, p->nh, dyn, s);
   }
   e = hipGetLastError();
+  if (e == hipSuccess) e = trace_mark(s);
   if (e != hipSuccess) return e;
   const int per_item = p->nh * p->nbins;
   k_dbias_reduce<<<(unsigned)((per_item + 255) / 256), 256, 0, s>>>(dbias_part, (int)p->bwd_work.size(), per_item,
                                                                      dtable);
   e = hipGetLastError();
+  if (e == hipSuccess) e = trace_mark(s);
   if (e != hipSuccess) return e;
   // QKV backward: dx = scatter(dqkv W_qkv), dW_qkv = dqkv^T gather(x), db_qkv
   e = launch_dgrad_qkv_bf16(p, dqkv, wqkvT, dx, s);
+  if (e == hipSuccess) e = trace_mark(s);
   if (e == hipSuccess)
     e = launch_wgrad_bf16(dqkv, 3 * C, nullptr, (const bf16*)x, C, p->dev.perm, p->n_tok, 3 * C, C,
                           p->wgrad_splits_qkv, p->wgrad_chunk_qkv, part, dw_qkv, db_qkv, s);
+  if (e == hipSuccess) e = trace_mark(s);
   return e;
 }
 

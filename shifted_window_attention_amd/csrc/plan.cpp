@@ -25,6 +25,18 @@ static thread_local std::string g_last_error;
 
 void set_error(const std::string& msg) { g_last_error = msg; }
 
+struct TraceState {
+  void* const* events = nullptr;
+  int capacity = 0;
+  int cursor = 0;
+};
+static thread_local TraceState g_trace;
+
+hipError_t trace_mark(hipStream_t s) {
+  if (!g_trace.events || g_trace.cursor >= g_trace.capacity) return hipSuccess;
+  return hipEventRecord((hipEvent_t)g_trace.events[g_trace.cursor++], s);
+}
+
 static swin_status fail(swin_status st, const std::string& msg) {
   set_error(msg);
   return st;
@@ -238,6 +250,16 @@ const char* swin_status_string(swin_status st) {
 
 const char* swin_attn_last_error(void) { return g_last_error.c_str(); }
 
+swin_status swin_attn_trace_events(void* const* events, int capacity) {
+  if (events && capacity < 0) return fail(SWIN_ERR_ARG, "negative trace capacity");
+  g_trace.events = events;
+  g_trace.capacity = events ? capacity : 0;
+  g_trace.cursor = 0;
+  return SWIN_OK;
+}
+
+int swin_attn_trace_cursor(void) { return g_trace.cursor; }
+
 swin_status swin_attn_host_index_map(const swin_attn_desc* desc, int64_t* map, uint8_t* labels) {
   swin_status st = validate(desc);
   if (st != SWIN_OK) return st;
@@ -408,9 +430,13 @@ swin_status swin_attn_fwd(const swin_attn_plan* plan, const void* x, const void*
   void* qkv = base;
   void* o = base + plan->saved_qkv;
   float* lse = (float*)(base + plan->saved_qkv + plan->saved_o);
-  hipError_t e = launch_qkv_fwd_bf16(plan, x, w_qkv, b_qkv, qkv, s);
+  hipError_t e = trace_mark(s);
+  if (e == hipSuccess) e = launch_qkv_fwd_bf16(plan, x, w_qkv, b_qkv, qkv, s);
+  if (e == hipSuccess) e = trace_mark(s);
   if (e == hipSuccess) e = launch_attn_fwd_bf16(plan, qkv, bias_table, o, lse, s);
+  if (e == hipSuccess) e = trace_mark(s);
   if (e == hipSuccess) e = launch_proj_fwd_bf16(plan, o, w_proj, b_proj, y, s);
+  if (e == hipSuccess) e = trace_mark(s);
   return hip_status(e, "bf16 forward");
 }
 

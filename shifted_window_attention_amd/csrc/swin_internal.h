@@ -76,6 +76,9 @@ namespace swin {
 
 void set_error(const std::string& msg);
 
+// Records the next installed trace event (if any) on stream s; see swin_attn_trace_events.
+hipError_t trace_mark(hipStream_t s);
+
 // ---- kernel launchers (return hipSuccess or the launch error) ----
 hipError_t launch_gather(const swin_attn_plan* p, const void* x, void* xw, bool scatter, hipStream_t s);
 

@@ -45,7 +45,7 @@ class SwinAttnStats(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libswinattn.so is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
-                          "or `python -m shifted_window_attention_amd.build_lib`")
+                          "or `python shifted_window_attention_amd/build_lib.py`")
     L = ctypes.CDLL(LIB_PATH)
     vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     P = ctypes.POINTER
@@ -60,6 +60,8 @@ def _load():
         "swin_attn_bwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "swin_window_gather": (st, [vp, vp, vp, vp]),
         "swin_window_scatter": (st, [vp, vp, vp, vp]),
+        "swin_attn_trace_events": (st, [P(vp), st]),
+        "swin_attn_trace_cursor": (st, []),
         "swin_status_string": (ctypes.c_char_p, [st]),
         "swin_attn_last_error": (ctypes.c_char_p, []),
     }
@@ -167,6 +169,18 @@ def swin_attn_bwd(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_
     _check(lib.swin_attn_bwd(plan, _ptr(dy), _ptr(x), _ptr(w_qkv), _ptr(w_proj), _ptr(bias_table), _ptr(saved),
                              _ptr(dx), _ptr(dw_qkv), _ptr(db_qkv), _ptr(dw_proj), _ptr(db_proj), _ptr(dbias_table),
                              _ptr(ws), ws_bytes, _stream(stream)), "swin_attn_bwd")
+
+
+def swin_attn_trace_events(events):
+    """events: a ctypes array of hipEvent_t handles (or None to uninstall)."""
+    if events is None:
+        _check(lib.swin_attn_trace_events(None, 0), "swin_attn_trace_events")
+    else:
+        _check(lib.swin_attn_trace_events(events, len(events)), "swin_attn_trace_events")
+
+
+def swin_attn_trace_cursor():
+    return int(lib.swin_attn_trace_cursor())
 
 
 def swin_window_gather(plan, x, xw, stream=None):
