@@ -6,8 +6,11 @@
 // (q' = tau log2(e) q is the stored query). The inverse routes carry these gradients
 // back to their sources (TERRA section IV-D).
 //
+// D = rowsum(dO * O) comes from the epilogue of the GEMM that produces dO.
+//
 // Work decomposition: one workgroup per (chunk of windows of one class, head), one wave
-// per 16-key tile. A lane holds one key and 4 consecutive queries of every 16-query tile
+// per 16-key tile. Each window's Q', dO, K, V, lse and D are staged in LDS by direct
+// global->LDS copies, double-buffered so window w+1 is copied while window w is computed. A lane holds one key and 4 consecutive queries of every 16-query tile
 // (S = Q K^T on v_mfma_f32_16x16x32_bf16), so dV^T = dO^T P and dK^T = Q'^T dS contract
 // over queries inside the wave: P and dS of two adjacent query tiles are directly the B
 // operand, and dO^T, Q'^T come from the row-major LDS tiles through gfx950's transposing
@@ -26,25 +29,12 @@
 
 namespace swin {
 
-__device__ __forceinline__ bf16x4 lds_tr4b(const bf16* p) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
-
-__device__ __forceinline__ bf16x8 tr_frag(const bf16* tile, int pitch, int row0, int col0, int g, int li) {
-  // 8 k values for column col0 + li: rows row0 + 4g + r (r < 4) and row0 + 16 + 4g + r
-  const bf16* base = tile + (row0 + 4 * g + (li >> 2)) * pitch + col0 + 4 * (li & 3);
-  const bf16x4 lo = lds_tr4b(base);
-  const bf16x4 hi = lds_tr4b(base + 16 * pitch);
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
 struct BwdArgs {
   const bf16* qkv;          // saved [3][nh][n_tok][32] (q pre-scaled)
   const bf16* o;            // saved [n_tok][C]
   const float* lse;         // saved [nh][n_tok] (log2 units)
   const bf16* dO;           // [nh][n_tok][32]
+  const float* dd;          // [nh][n_tok]: D = rowsum(dO * O)
   const float* table;       // [nh][nbins]
   bf16* dqkv;               // [n_tok][3C]
   float* dbias_part;        // [n_items_total][nh][nbins]
@@ -80,113 +70,112 @@ __device__ __forceinline__ float bias2_of(const ClassInfo& ci, const float* __re
 }
 
 template <int NKT>
-struct BwdLds {
-  static constexpr int NKC = (NKT + 1) / 2;
-  static constexpr int ROWS = NKC * 32;      // staged query/key rows (zero beyond n)
-  static constexpr int QP = 40;              // Q', dO pitch (bf16)
-  static constexpr int KP = 48;              // K pitch (bf16), read transposed only
-  static constexpr int SP = ROWS + 4;        // dS pitch (bf16)
-  static constexpr int Q_OFF = 0;
-  static constexpr int DO_OFF = Q_OFF + ROWS * QP * 2;
-  static constexpr int K_OFF = DO_OFF + ROWS * QP * 2;
-  static constexpr int S_OFF = K_OFF + ROWS * KP * 2;
-  static constexpr int L_OFF = S_OFF + ROWS * SP * 2;
-  static constexpr int D_OFF = L_OFF + ROWS * 4;
-  static constexpr int ARENA = D_OFF + ROWS * 4;   // bytes reused by the dbias binning
-  static constexpr int SLAB = (ARENA / (NKT * 16 * 4)) / 16 * 16;  // query rows per binning slab
+struct BwdBuf {
+  static constexpr int ROWS = (NKT + 1) / 2 * 32;  // staged rows per tile (32-row chunks)
+  static constexpr int FROWS = (ROWS + 63) / 64 * 64;  // float rows: whole 64-lane copies
+  unsigned char q[ROWS * 64], dO[ROWS * 64], k[ROWS * 64], v[ROWS * 64];
+  float lse[FROWS], dd[FROWS];
 };
 
 template <int NKT>
-__global__ __launch_bounds__(64 * NKT) void k_attn_bwd(BwdArgs a) {
-  using L = BwdLds<NKT>;
-  constexpr int NKC = L::NKC;
+__global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
+  constexpr int NKC = (NKT + 1) / 2;
   constexpr int NT = 64 * NKT;
-  static_assert(L::SLAB >= 16, "LDS arena too small for the bias-gradient slab");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[L::ARENA];
+  constexpr int ROWS = BwdBuf<NKT>::ROWS;
+  constexpr int SP = ROWS + 4;                        // dS row pitch (bf16)
+  constexpr int SLAB = ((int)sizeof(BwdBuf<NKT>) / (NKT * 16 * 4)) / 16 * 16;  // rows per pass in bufA
+  static_assert(SLAB >= 16, "LDS too small for the bias-gradient slab");
+  static_assert(BwdBuf<NKT>::FROWS % 64 == 0 && BwdBuf<NKT>::FROWS >= ROWS, "float rows are whole copies");
+  static_assert(SLAB * NKT * 16 * 4 <= (int)sizeof(BwdBuf<NKT>), "binning slab fits in one buffer");
+  // Two staging buffers (separate objects, loop unrolled by two, see the forward kernel)
+  // filled by direct global->LDS copies while the other one is computed, dS for dQ, and
+  // the per-bin partial sums.
+  __shared__ __attribute__((aligned(1024))) BwdBuf<NKT> bufA;
+  __shared__ __attribute__((aligned(1024))) BwdBuf<NKT> bufB;
+  __shared__ __attribute__((aligned(16))) bf16 dSs[16 * NKT * SP];
+  __shared__ int offs[kMaxChunk];
   extern __shared__ float bins_lds[];  // [nbins], dynamic
-  bf16* Qs = (bf16*)(lds + L::Q_OFF);
-  bf16* dOs = (bf16*)(lds + L::DO_OFF);
-  bf16* Ks = (bf16*)(lds + L::K_OFF);
-  bf16* dSs = (bf16*)(lds + L::S_OFF);
-  float* LSEs = (float*)(lds + L::L_OFF);
-  float* Ds = (float*)(lds + L::D_OFF);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, kt = tid >> 6;
+  const int lane = tid & 63;
+  const int kt = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, li = lane & 15;
   const WorkItem wk = a.work[blockIdx.x];
   const int h = blockIdx.y;
   const ClassInfo ci = a.classes[wk.cls];
   const int n = ci.n;
-  const int nqt = ci.nqt;  // == NKT
   const int key = 16 * kt + li;
   const float* tab = a.table + (int64_t)h * a.nbins;
-
-  // lane's bias + mask for every query tile (S layout: key fixed, queries 16 qt + 4 g + i)
-  f32x4 bias[NKT], dbacc[NKT];
-#pragma unroll
-  for (int qt = 0; qt < NKT; ++qt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bias[qt][i] = bias2_of(ci, tab, a.win, 16 * qt + 4 * g + i, key);
-      dbacc[qt][i] = 0.f;
-    }
-  for (int i = tid; i < a.nbins; i += NT) bins_lds[i] = 0.f;
+  if (tid < wk.count) offs[tid] = a.win_off[a.class_win[wk.first + tid]];
+  const int64_t off0 = a.win_off[a.class_win[wk.first]];
 
   const bf16* Qh = a.qkv + ((int64_t)(0 * a.nh + h) * a.n_tok) * 32;
   const bf16* Kh = a.qkv + ((int64_t)(1 * a.nh + h) * a.n_tok) * 32;
   const bf16* Vh = a.qkv + ((int64_t)(2 * a.nh + h) * a.n_tok) * 32;
   const bf16* dOh = a.dO + ((int64_t)h * a.n_tok) * 32;
   const float* LSEh = a.lse + (int64_t)h * a.n_tok;
+  const float* Dh = a.dd + (int64_t)h * a.n_tok;
+  // rows past n arrive as zeros (buffer range = the window's n rows)
+  auto stage = [&](int64_t off, BwdBuf<NKT>& b) {
+    const uint32_t bytes = (uint32_t)n * 64;
+    stage_rows(make_rsrc(Qh + off * 32, bytes), b.q, ROWS, kt, NKT, lane);
+    stage_rows(make_rsrc(dOh + off * 32, bytes), b.dO, ROWS, kt, NKT, lane);
+    stage_rows(make_rsrc(Kh + off * 32, bytes), b.k, ROWS, kt, NKT, lane);
+    stage_rows(make_rsrc(Vh + off * 32, bytes), b.v, ROWS, kt, NKT, lane);
+    stage_floats(make_rsrc(LSEh + off, (uint32_t)n * 4), b.lse, BwdBuf<NKT>::FROWS, kt, NKT, lane);
+    stage_floats(make_rsrc(Dh + off, (uint32_t)n * 4), b.dd, BwdBuf<NKT>::FROWS, kt, NKT, lane);
+  };
+  // key columns of dS that no wave owns (odd tile count) are read by dQ: keep them zero
+  if constexpr (ROWS > 16 * NKT) {
+    constexpr int EXTRA = ROWS - 16 * NKT;
+    for (int c = tid; c < 16 * NKT * EXTRA; c += NT) dSs[(c / EXTRA) * SP + 16 * NKT + c % EXTRA] = to_bf16(0.f);
+  }
+  for (int i = tid; i < a.nbins; i += NT) bins_lds[i] = 0.f;
+  stage(off0, bufA);
+
+  // lane's bias + mask for every query tile (S layout: key fixed, queries 16 qt + 4 g + i),
+  // held as fp16 to leave registers for the dS sums: |error| <= 2^-11 |bias|, -inf exact
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  h4 bias[NKT];
+  f32x4 dbacc[NKT];
+#pragma unroll
+  for (int qt = 0; qt < NKT; ++qt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bias[qt][i] = (_Float16)bias2_of(ci, tab, a.win, 16 * qt + 4 * g + i, key);
+      dbacc[qt][i] = 0.f;
+    }
   const int C = a.C;
   const float inv_log2e = 1.f / kLog2e;
-  // key columns of dS that no wave owns (odd tile count) are read by dQ: keep them zero
-  if constexpr (L::ROWS > 16 * NKT) {
-    constexpr int EXTRA = L::ROWS - 16 * NKT;
-    for (int c = tid; c < L::ROWS * EXTRA; c += NT) dSs[(c / EXTRA) * L::SP + 16 * NKT + c % EXTRA] = to_bf16(0.f);
-  }
+  __syncthreads();
 
-  for (int w = 0; w < wk.count; ++w) {
-    const int64_t off = a.win_off[a.class_win[wk.first + w]];
-    __syncthreads();
-    // stage Q', dO, K (zero beyond n), lse2 and D = rowsum(dO * O)
-    for (int c = tid; c < L::ROWS * 4; c += NT) {
-      const int row = c >> 2, part = (c & 3) * 8;
-      bf16x8 qv = {}, dv = {}, kv = {};
-      if (row < n) {
-        qv = *(const bf16x8*)(Qh + (off + row) * 32 + part);
-        dv = *(const bf16x8*)(dOh + (off + row) * 32 + part);
-        kv = *(const bf16x8*)(Kh + (off + row) * 32 + part);
-      }
-      *(bf16x8*)(Qs + row * L::QP + part) = qv;
-      *(bf16x8*)(dOs + row * L::QP + part) = dv;
-      *(bf16x8*)(Ks + row * L::KP + part) = kv;
+  // A barrier's release fence waits for outstanding global stores, and that wait also
+  // covers the copies in flight. So no store is outstanding at the mid-window barrier: dK
+  // and dV are stored right after it, and dq at the start of the next window, after the
+  // next copies are issued.
+  bf16x4 pq[2] = {};
+  int64_t prev_off = -1;
+  auto flush = [&]() {
+    if (prev_off < 0) return;
+    const int q = 16 * kt + li;
+    if (q < n) {
+      bf16* row = a.dqkv + (prev_off + q) * (3 * C) + h * 32;
+      *(bf16x4*)(row + 4 * g) = pq[0];
+      *(bf16x4*)(row + 16 + 4 * g) = pq[1];
     }
-    for (int r = tid; r < L::ROWS; r += NT) {
-      float lv = 0.f, dv = 0.f;
-      if (r < n) {
-        lv = LSEh[off + r];
-        const bf16* orow = a.o + (off + r) * C + h * 32;
-        const bf16* drow = dOh + (off + r) * 32;
+  };
+
+  auto window = [&](int w, const BwdBuf<NKT>& cur, BwdBuf<NKT>& nxt) {
+    const int64_t off = offs[w];
+    if (w + 1 < wk.count) stage(offs[w + 1], nxt);  // overlaps with this window's compute
+    flush();
+    // keep the packed fp16 bias opaque per window so its fp32 expansion is not hoisted out
+    // of the loop (that would cost the registers the packing saves)
 #pragma unroll
-        for (int d8 = 0; d8 < 32; d8 += 8) {
-          const bf16x8 ov = *(const bf16x8*)(orow + d8);
-          const bf16x8 gv = *(const bf16x8*)(drow + d8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) dv += to_f32(ov[e]) * to_f32(gv[e]);
-        }
-      }
-      LSEs[r] = lv;
-      Ds[r] = dv;
-    }
+    for (int qt = 0; qt < NKT; ++qt) asm volatile("" : "+v"(bias[qt]));
     // the wave's own key tile as B operands (K^T for S, V^T for dP)
-    bf16x8 kb = {}, vb = {};
-    if (key < n) {
-      kb = *(const bf16x8*)(Kh + (off + key) * 32 + 8 * g);
-      vb = *(const bf16x8*)(Vh + (off + key) * 32 + 8 * g);
-    }
-    __syncthreads();
-
+    const bf16x8 kb = tile_frag(cur.k, key, g);
+    const bf16x8 vb = tile_frag(cur.v, key, g);
     f32x4 dvacc[2] = {f32x4{}, f32x4{}}, dkacc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
     for (int c = 0; c < NKC; ++c) {
@@ -195,12 +184,11 @@ __global__ __launch_bounds__(64 * NKT) void k_attn_bwd(BwdArgs a) {
       for (int u = 0; u < 2; ++u) {
         const int qt = 2 * c + u;
         if (qt < NKT) {
-          const bf16x8 qa = *(const bf16x8*)(Qs + (16 * qt + li) * L::QP + 8 * g);
-          const f32x4 s = mfma16(qa, kb, bias[qt]);
-          const bf16x8 da = *(const bf16x8*)(dOs + (16 * qt + li) * L::QP + 8 * g);
-          const f32x4 dp = mfma16(da, vb, f32x4{});
-          const f32x4 l4 = *(const f32x4*)(LSEs + 16 * qt + 4 * g);
-          const f32x4 d4 = *(const f32x4*)(Ds + 16 * qt + 4 * g);
+          const f32x4 b4 = {(float)bias[qt][0], (float)bias[qt][1], (float)bias[qt][2], (float)bias[qt][3]};
+          const f32x4 s = mfma16(tile_frag(cur.q, 16 * qt + li, g), kb, b4);
+          const f32x4 dp = mfma16(tile_frag(cur.dO, 16 * qt + li, g), vb, f32x4{});
+          const f32x4 l4 = *(const f32x4*)(cur.lse + 16 * qt + 4 * g);
+          const f32x4 d4 = *(const f32x4*)(cur.dd + 16 * qt + 4 * g);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float p = fast_exp2(s[i] - l4[i]);
@@ -208,34 +196,34 @@ __global__ __launch_bounds__(64 * NKT) void k_attn_bwd(BwdArgs a) {
             dbacc[qt][i] += ds;
             pb[4 * u + i] = to_bf16(p);
             sb[4 * u + i] = to_bf16(ds);
-            dSs[(16 * qt + 4 * g + i) * L::SP + key] = sb[4 * u + i];
+            dSs[(16 * qt + 4 * g + i) * SP + key] = sb[4 * u + i];
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
-        const bf16x8 doT = tr_frag(dOs, L::QP, 32 * c, 16 * dt, g, li);
-        dvacc[dt] = mfma16(doT, pb, dvacc[dt]);
-        const bf16x8 qT = tr_frag(Qs, L::QP, 32 * c, 16 * dt, g, li);
-        dkacc[dt] = mfma16(qT, sb, dkacc[dt]);
+        dvacc[dt] = mfma16(tile_frag_tr(cur.dO, 32 * c, 16 * dt, g, li), pb, dvacc[dt]);
+        dkacc[dt] = mfma16(tile_frag_tr(cur.q, 32 * c, 16 * dt, g, li), sb, dkacc[dt]);
       }
+      __builtin_amdgcn_sched_barrier(0);  // bound live ranges to one query chunk
     }
+    __syncthreads();  // dS complete (no stores are outstanding here, so copies stay in flight)
     if (key < n) {
       bf16* row = a.dqkv + (off + key) * (3 * C) + h * 32;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
-        bf16x4 kv4, vv4;
+        bf16x4 k4, v4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          kv4[i] = to_bf16(dkacc[dt][i] * inv_log2e);
-          vv4[i] = to_bf16(dvacc[dt][i]);
+          k4[i] = to_bf16(dkacc[dt][i] * inv_log2e);
+          v4[i] = to_bf16(dvacc[dt][i]);
         }
-        *(bf16x4*)(row + C + 16 * dt + 4 * g) = kv4;
-        *(bf16x4*)(row + 2 * C + 16 * dt + 4 * g) = vv4;
+        *(bf16x4*)(row + C + 16 * dt + 4 * g) = k4;
+        *(bf16x4*)(row + 2 * C + 16 * dt + 4 * g) = v4;
       }
     }
-    __syncthreads();  // dS complete
-    // dQ^T for query tile qt = kt: K^T (transposed read of K) times dS^T (rows of dS)
+    // dQ^T for query tile kt: K^T (transposed read of K) times dS^T (rows of dS)
     {
       const int q = 16 * kt + li;
 #pragma unroll
@@ -243,33 +231,34 @@ __global__ __launch_bounds__(64 * NKT) void k_attn_bwd(BwdArgs a) {
         f32x4 dq = f32x4{};
 #pragma unroll
         for (int c = 0; c < NKC; ++c) {
-          const bf16x8 kT = tr_frag(Ks, L::KP, 32 * c, 16 * dt, g, li);
-          const bf16x4 lo = *(const bf16x4*)(dSs + q * L::SP + 32 * c + 4 * g);
-          const bf16x4 hi = *(const bf16x4*)(dSs + q * L::SP + 32 * c + 16 + 4 * g);
-          const bf16x8 sb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          dq = mfma16(kT, sb, dq);
+          const bf16x4 lo = *(const bf16x4*)(dSs + q * SP + 32 * c + 4 * g);
+          const bf16x4 hi = *(const bf16x4*)(dSs + q * SP + 32 * c + 16 + 4 * g);
+          const bf16x8 sq = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          dq = mfma16(tile_frag_tr(cur.k, 32 * c, 16 * dt, g, li), sq, dq);
         }
-        if (q < n) {
-          bf16x4 v4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v4[i] = to_bf16(dq[i] * a.tau);
-          *(bf16x4*)(a.dqkv + (off + q) * (3 * C) + h * 32 + 16 * dt + 4 * g) = v4;
-        }
+        for (int i = 0; i < 4; ++i) pq[dt][i] = to_bf16(dq[i] * a.tau);
       }
     }
+    prev_off = off;
+    __syncthreads();  // window w+1 staged; this buffer and dS are free
+  };
+  for (int w = 0; w < wk.count; w += 2) {
+    window(w, bufA, bufB);
+    if (w + 1 < wk.count) window(w + 1, bufB, bufA);
   }
+  flush();
 
   // bin the chunk's per-position dS sums into the relative-position table, slab by slab
-  __syncthreads();
-  float* acc = (float*)lds;  // [SLAB][16 NKT] fp32
+  float* acc = (float*)&bufA;  // [SLAB][16 NKT] fp32 inside the first staging buffer
   const int kcols = 16 * NKT;
-  for (int q0 = 0; q0 < 16 * NKT; q0 += L::SLAB) {
+  for (int q0 = 0; q0 < 16 * NKT; q0 += SLAB) {
 #pragma unroll
     for (int qt = 0; qt < NKT; ++qt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = 16 * qt + 4 * g + i;
-        if (q >= q0 && q < q0 + L::SLAB) acc[(q - q0) * kcols + key] = dbacc[qt][i];
+        if (q >= q0 && q < q0 + SLAB) acc[(q - q0) * kcols + key] = dbacc[qt][i];
       }
     __syncthreads();
     for (int b = tid; b < a.nbins; b += NT) {
@@ -279,7 +268,7 @@ __global__ __launch_bounds__(64 * NKT) void k_attn_bwd(BwdArgs a) {
       const int rh = (b / tw) % th - (a.win[1] - 1);
       const int rd = b / (tw * th) - (a.win[0] - 1);
       float sum = bins_lds[b];
-      const int q1 = q0 + L::SLAB < n ? q0 + L::SLAB : n;
+      const int q1 = q0 + SLAB < n ? q0 + SLAB : n;
       for (int q = q0; q < q1; ++q) {
         const int qw = q % ci.ext[2], qr = q / ci.ext[2];
         const int qh = qr % ci.ext[1], qd = qr / ci.ext[1];
@@ -294,7 +283,6 @@ __global__ __launch_bounds__(64 * NKT) void k_attn_bwd(BwdArgs a) {
   }
   float* part = a.dbias_part + ((int64_t)(a.item_base + blockIdx.x) * a.nh + h) * a.nbins;
   for (int b = tid; b < a.nbins; b += NT) part[b] = bins_lds[b];
-  (void)nqt;
 }
 
 // dT[h][b] = sum over work items (in order) of the partial tables.
@@ -311,15 +299,15 @@ static void launch_bwd_one(const BwdArgs& a, int n_items, int nh, size_t dyn, hi
   k_attn_bwd<NKT><<<dim3((unsigned)n_items, (unsigned)nh), 64 * NKT, dyn, s>>>(a);
 }
 
-// The staged Q', dO, K and dS tiles fit the 160 KB of LDS up to 12 key tiles (192 tokens).
+// Two staging buffers of Q', dO, K, V plus dS fit the 160 KB of LDS up to 10 key tiles.
 typedef void (*bwd_launcher)(const BwdArgs&, int, int, size_t, hipStream_t);
 static const bwd_launcher kBwd[kMaxBwdTiles + 1] = {nullptr,           launch_bwd_one<1>, launch_bwd_one<2>,
                                                     launch_bwd_one<3>, launch_bwd_one<4>, launch_bwd_one<5>,
                                                     launch_bwd_one<6>, launch_bwd_one<7>, launch_bwd_one<8>,
-                                                    launch_bwd_one<9>, launch_bwd_one<10>, launch_bwd_one<11>,
-                                                    launch_bwd_one<12>};
+                                                    launch_bwd_one<9>, launch_bwd_one<10>};
 
-hipError_t launch_dproj_bf16(const swin_attn_plan* p, const void* dy, const void* wprojT, void* dO, hipStream_t s);
+hipError_t launch_dproj_bf16(const swin_attn_plan* p, const void* dy, const void* wprojT, void* dO, const void* o,
+                             float* dd, hipStream_t s);
 hipError_t launch_dgrad_qkv_bf16(const swin_attn_plan* p, const void* dqkv, const void* wqkvT, void* dx,
                                  hipStream_t s);
 hipError_t launch_wgrad_bf16(const bf16* A, int64_t lda, const int32_t* a_rows, const bf16* B, int64_t ldb,
@@ -343,13 +331,14 @@ hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* 
   bf16* wqkvT = wprojT + (size_t)C * C;
   float* part = (float*)(w + p->bwd_do + p->bwd_dqkv + p->bwd_wt);
   float* dbias_part = (float*)(w + p->bwd_do + p->bwd_dqkv + p->bwd_wt + p->bwd_part);
+  float* dd = (float*)(w + p->bwd_do + p->bwd_dqkv + p->bwd_wt + p->bwd_part + p->bwd_dbias_part);
 
   hipError_t e = trace_mark(s);
   if (e == hipSuccess) e = launch_transpose_bf16(w_proj, wprojT, C, C, s);
   if (e == hipSuccess) e = launch_transpose_bf16(w_qkv, wqkvT, 3 * C, C, s);
   if (e == hipSuccess) e = trace_mark(s);
   // proj backward: dO = gather(dy) W_proj (head-split), dW_proj = gather(dy)^T o, db_proj
-  if (e == hipSuccess) e = launch_dproj_bf16(p, dy, wprojT, dO, s);
+  if (e == hipSuccess) e = launch_dproj_bf16(p, dy, wprojT, dO, o, dd, s);
   if (e == hipSuccess) e = trace_mark(s);
   if (e == hipSuccess)
     e = launch_wgrad_bf16((const bf16*)dy, C, p->dev.perm, o, C, nullptr, p->n_tok, C, C, p->wgrad_splits_proj,
@@ -362,6 +351,7 @@ hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* 
   a.o = o;
   a.lse = lse;
   a.dO = dO;
+  a.dd = dd;
   a.table = table;
   a.dqkv = dqkv;
   a.dbias_part = dbias_part;

@@ -10,8 +10,9 @@
 // per 16-query tile. Every window of a class has the same extent and label split, so a
 // lane's bias + mask values (its query against every key) are computed once per
 // workgroup and then serve as the initial accumulator of the Q K^T MFMA for every window
-// of the chunk. A window's K and V (n x 32 bf16 each) are staged in LDS; Q comes straight
-// from HBM into the MFMA operand registers.
+// of the chunk. A window's Q, K and V (n x 32 bf16 each) are staged in LDS by direct
+// global->LDS copies into one of two buffers, so the copies for window w+1 run while
+// window w is computed (one barrier per window).
 //
 // The logits are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16), so a lane
 // holds one query and 4 consecutive keys of every 16-key tile: the row max and row sum
@@ -24,12 +25,6 @@
 #include "swin_internal.h"
 
 namespace swin {
-
-__device__ __forceinline__ bf16x4 lds_tr4(const bf16* p) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
 
 struct AttnArgs {
   const bf16* qkv;          // [3][nh][n_tok][32]
@@ -68,15 +63,25 @@ __device__ __forceinline__ float pair_bias2(const ClassInfo& ci, const float* __
 }
 
 template <int NKT>
-__global__ __launch_bounds__(64 * NKT) void k_attn_fwd(AttnArgs a) {
-  constexpr int NKC = (NKT + 1) / 2;   // 32-key chunks of the PV product
-  constexpr int KROWS = NKC * 32;      // staged key rows (zero beyond n)
-  constexpr int KP = 40;               // K row pitch (bf16): conflict-free 16-byte fragment reads
-  constexpr int VP = 48;               // V row pitch (bf16): conflict-free transposed reads
-  __shared__ __attribute__((aligned(16))) bf16 Ks[KROWS * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[KROWS * VP];
+struct FwdBuf {
+  static constexpr int ROWS = (NKT + 1) / 2 * 32;  // staged rows per tile (32-key chunks)
+  unsigned char q[ROWS * 64], k[ROWS * 64], v[ROWS * 64];
+};
 
-  const int lane = threadIdx.x & 63, qt = threadIdx.x >> 6;
+template <int NKT>
+__global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
+  constexpr int NKC = (NKT + 1) / 2;   // 32-key chunks of the PV product
+  constexpr int ROWS = FwdBuf<NKT>::ROWS;
+  // Two buffers, filled by direct global->LDS copies: window w is computed from one while
+  // window w+1 is copied into the other. They are separate objects (and the window loop is
+  // unrolled by two) so the compiler can tell the copies never touch the buffer being read
+  // and leaves them in flight until the end-of-window barrier.
+  __shared__ __attribute__((aligned(1024))) FwdBuf<NKT> bufA;
+  __shared__ __attribute__((aligned(1024))) FwdBuf<NKT> bufB;
+  __shared__ int offs[kMaxChunk];
+
+  const int lane = threadIdx.x & 63;
+  const int qt = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, li = lane & 15;
   const WorkItem wk = a.work[blockIdx.x];
   const int h = blockIdx.y;
@@ -85,40 +90,49 @@ __global__ __launch_bounds__(64 * NKT) void k_attn_fwd(AttnArgs a) {
   const int q = qt * 16 + li;
   const bool qv = q < n;
   const float* tab = a.table + (int64_t)h * a.nbins;
+  if (threadIdx.x < wk.count) offs[threadIdx.x] = a.win_off[a.class_win[wk.first + threadIdx.x]];
+  const int64_t off0 = a.win_off[a.class_win[wk.first]];
+
+  const bf16* Qh = a.qkv + ((int64_t)(0 * a.nh + h) * a.n_tok) * 32;
+  const bf16* Kh = a.qkv + ((int64_t)(1 * a.nh + h) * a.n_tok) * 32;
+  const bf16* Vh = a.qkv + ((int64_t)(2 * a.nh + h) * a.n_tok) * 32;
+  // rows past n arrive as zeros (buffer range = the window's n rows)
+  auto stage = [&](int64_t off, FwdBuf<NKT>& b) {
+    const uint32_t bytes = (uint32_t)n * 64;
+    stage_rows(make_rsrc(Qh + off * 32, bytes), b.q, ROWS, qt, NKT, lane);
+    stage_rows(make_rsrc(Kh + off * 32, bytes), b.k, ROWS, qt, NKT, lane);
+    stage_rows(make_rsrc(Vh + off * 32, bytes), b.v, ROWS, qt, NKT, lane);
+  };
+  stage(off0, bufA);
 
   f32x4 bias[NKT];
 #pragma unroll
   for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) bias[kt][i] = qv ? pair_bias2(ci, tab, a.win, q, 16 * kt + 4 * g + i) : 0.f;
+  __syncthreads();
 
-  const bf16* Qh = a.qkv + ((int64_t)(0 * a.nh + h) * a.n_tok) * 32;
-  const bf16* Kh = a.qkv + ((int64_t)(1 * a.nh + h) * a.n_tok) * 32;
-  const bf16* Vh = a.qkv + ((int64_t)(2 * a.nh + h) * a.n_tok) * 32;
-
-  for (int w = 0; w < wk.count; ++w) {
-    const int64_t off = a.win_off[a.class_win[wk.first + w]];
-    __syncthreads();  // previous window's LDS reads are done
-    for (int c = threadIdx.x; c < KROWS * 4; c += 64 * NKT) {
-      const int row = c >> 2, part = (c & 3) * 8;
-      bf16x8 kv = {}, vv = {};
-      if (row < n) {
-        kv = *(const bf16x8*)(Kh + (off + row) * 32 + part);
-        vv = *(const bf16x8*)(Vh + (off + row) * 32 + part);
-      }
-      *(bf16x8*)(Ks + row * KP + part) = kv;
-      *(bf16x8*)(Vs + row * VP + part) = vv;
+  // a window's results are stored at the start of the next iteration, after the next
+  // copies are issued, so the end-of-window barrier does not wait for them
+  bf16x4 ov[2] = {};
+  float lse_v = 0.f;
+  int64_t prev_off = -1;
+  auto flush = [&]() {
+    if (prev_off >= 0 && qv) {
+      bf16* orow = a.o + (prev_off + q) * a.C + h * 32;
+      *(bf16x4*)(orow + 4 * g) = ov[0];
+      *(bf16x4*)(orow + 16 + 4 * g) = ov[1];
+      if (g == 0) a.lse[(int64_t)h * a.n_tok + prev_off + q] = lse_v;
     }
-    bf16x8 bq = {};
-    if (qv) bq = *(const bf16x8*)(Qh + (off + q) * 32 + 8 * g);
-    __syncthreads();
-
+  };
+  auto window = [&](int w, const FwdBuf<NKT>& cur, FwdBuf<NKT>& nxt) {
+    const int64_t off = offs[w];
+    if (w + 1 < wk.count) stage(offs[w + 1], nxt);  // overlaps with this window's compute
+    flush();
+    const bf16x8 bq = tile_frag(cur.q, q, g);
     f32x4 s[NKT];
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      const bf16x8 ka = *(const bf16x8*)(Ks + (16 * kt + li) * KP + 8 * g);
-      s[kt] = mfma16(ka, bq, bias[kt]);
-    }
+    for (int kt = 0; kt < NKT; ++kt) s[kt] = mfma16(tile_frag(cur.k, 16 * kt + li, g), bq, bias[kt]);
     float m = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
@@ -146,27 +160,22 @@ __global__ __launch_bounds__(64 * NKT) void k_attn_fwd(AttnArgs a) {
         pb[4 + i] = (2 * c + 1 < NKT) ? to_bf16(s[2 * c + 1][i]) : to_bf16(0.f);
       }
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const bf16* base = Vs + (32 * c + 4 * g + (li >> 2)) * VP + 16 * dt + 4 * (li & 3);
-        const bf16x4 lo = lds_tr4(base);
-        const bf16x4 hi = lds_tr4(base + 16 * VP);
-        const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[dt] = mfma16(va, pb, oacc[dt]);
-      }
+      for (int dt = 0; dt < 2; ++dt) oacc[dt] = mfma16(tile_frag_tr(cur.v, 32 * c, 16 * dt, g, li), pb, oacc[dt]);
     }
-    if (qv) {
-      const float inv = 1.f / l;
-      bf16* orow = a.o + (off + q) * a.C + h * 32;
+    const float inv = 1.f / l;
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        bf16x4 ov;
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = to_bf16(oacc[dt][i] * inv);
-        *(bf16x4*)(orow + 16 * dt + 4 * g) = ov;
-      }
-      if (g == 0) a.lse[(int64_t)h * a.n_tok + off + q] = m + fast_log2(l);
-    }
+      for (int i = 0; i < 4; ++i) ov[dt][i] = to_bf16(oacc[dt][i] * inv);
+    lse_v = m + fast_log2(l);
+    prev_off = off;
+    __syncthreads();  // window w+1 staged; this buffer is free
+  };
+  for (int w = 0; w < wk.count; w += 2) {
+    window(w, bufA, bufB);
+    if (w + 1 < wk.count) window(w + 1, bufB, bufA);
   }
+  flush();
 }
 
 template <int NKT>

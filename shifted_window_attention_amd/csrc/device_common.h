@@ -46,9 +46,67 @@ __device__ __forceinline__ float wave_sum_xor16_32(float v) {
   return v;
 }
 
-template <class T>
-__device__ __forceinline__ T ldg(const T* p) {
-  return *p;
+// ---- LDS tiles of 32-element bf16 head rows (64 bytes per row) ----
+// A tile row holds four 16-byte chunks; physical slot s of row r holds logical chunk
+// s ^ swz(r). With this swizzle the 16-byte fragment reads of 8 or 16 consecutive rows at
+// one logical chunk touch distinct banks.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// Byte offset of element `col` (multiple of 4) of row r in a swizzled tile.
+__device__ __forceinline__ int swz_off(int r, int col) {
+  return r * 64 + 16 * ((col >> 3) ^ swz(r)) + 2 * (col & 7);
+}
+
+// 16-byte fragment (logical chunk c, i.e. columns 8c..8c+7) of row r.
+__device__ __forceinline__ bf16x8 tile_frag(const unsigned char* tile, int r, int c) {
+  return *(const bf16x8*)(tile + r * 64 + 16 * (c ^ swz(r)));
+}
+
+// Four bf16 through gfx950's transposing LDS read: lane i of each 16-lane group receives
+// element (i % 4) of the 8-byte pieces addressed by lanes 4r + i/4, r = 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const void* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// MFMA 16x16x32 operand with 8 k values for column col0 + li of a swizzled tile whose rows
+// are k: rows row0 + 4g + r (r < 4) and row0 + 16 + 4g + r.
+__device__ __forceinline__ bf16x8 tile_frag_tr(const unsigned char* tile, int row0, int col0, int g, int li) {
+  const int r = row0 + 4 * g + (li >> 2);
+  const int col = col0 + 4 * (li & 3);
+  const bf16x4 lo = lds_read_tr(tile + swz_off(r, col));
+  const bf16x4 hi = lds_read_tr(tile + swz_off(r + 16, col));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw buffer, 32-bit elements format as the
+// CDNA buffer descriptor expects). Loads past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Asynchronous copy of `rows` (multiple of 16) rows of 64 bytes from a buffer resource
+// into a swizzled LDS tile, without staging through registers (buffer_load ... lds). Rows
+// past the resource's range arrive as zeros. Wave w of nw issues instructions w, w + nw,
+// ...; each instruction fills 16 rows (1 KB; lane l -> row l/4, slot l%4).
+__device__ __forceinline__ void stage_rows(__amdgpu_buffer_rsrc_t src, unsigned char* tile, int rows, int w, int nw,
+                                           int lane) {
+  for (int j = w; j < rows / 16; j += nw) {
+    const int r = 16 * j + (lane >> 2);
+    const int c = (lane & 3) ^ swz(r);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(tile + 1024 * j), 16,
+                                             r * 64 + 16 * c, 0, 0, 0);
+  }
+}
+
+// Asynchronous copy of `rows` floats (a multiple of 64: every copy writes 64 lanes) from a
+// buffer resource into LDS (zeros past its range).
+__device__ __forceinline__ void stage_floats(__amdgpu_buffer_rsrc_t src, float* dst, int rows, int w, int nw,
+                                             int lane) {
+  for (int j = w; j < rows / 64; j += nw)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(dst + 64 * j), 4,
+                                             4 * (64 * j + lane), 0, 0, 0);
 }
 
 }  // namespace swin

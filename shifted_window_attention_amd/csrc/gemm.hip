@@ -26,6 +26,8 @@ struct EpiParams {
   float qscale;              // mode 1: factor for columns < C (the q block)
   int C, nh, hd;
   int64_t n_tok;
+  const bf16* dot_o;         // mode 1, one plane: if set, also write dot_out[head][m] =
+  float* dot_out;            //   sum over the head's columns of C[m, :] * dot_o[m, :]
 };
 
 template <int BM, int BN>
@@ -167,25 +169,40 @@ __global__ __launch_bounds__(256, 2) void k_gemm_nt(const bf16* __restrict__ A, 
   }
   __syncthreads();
   constexpr int CH_PER_ROW = BN / 8;
+  static_assert((BM * CH_PER_ROW) % Cfg::NT == 0, "uniform copy-out loop");
   for (int c = tid; c < BM * CH_PER_ROW; c += Cfg::NT) {
     const int row = c / CH_PER_ROW;
     const int cc = (c % CH_PER_ROW) * 8;
     const int64_t m = m0 + row;
     const int n = n0 + cc;
-    if (m >= M || n >= N) continue;
+    const bool valid = m < M && n < N;
     const bf16x8 v = *(const bf16x8*)(Cs + row * Cfg::CPITCH + cc);
-    bf16* dst;
-    if (ep.mode == 1) {
-      const int plane = n / ep.C;
-      const int rem = n - plane * ep.C;
-      const int head = rem / ep.hd;
-      const int d = rem - head * ep.hd;
-      dst = ep.out + (((int64_t)plane * ep.nh + head) * ep.n_tok + m) * ep.hd + d;
-    } else {
-      const int64_t orow = ep.out_rows ? (int64_t)ep.out_rows[m] : m;
-      dst = ep.out + orow * ep.ldc + n;
+    float dot = 0.f;
+    if (valid) {
+      bf16* dst;
+      if (ep.mode == 1) {
+        const int plane = n / ep.C;
+        const int rem = n - plane * ep.C;
+        const int head = rem / ep.hd;
+        const int d = rem - head * ep.hd;
+        dst = ep.out + (((int64_t)plane * ep.nh + head) * ep.n_tok + m) * ep.hd + d;
+      } else {
+        const int64_t orow = ep.out_rows ? (int64_t)ep.out_rows[m] : m;
+        dst = ep.out + orow * ep.ldc + n;
+      }
+      *(bf16x8*)dst = v;
+      if (ep.dot_o) {
+        const bf16x8 ov = *(const bf16x8*)(ep.dot_o + m * ep.C + n);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot += to_f32(v[e]) * to_f32(ov[e]);
+      }
     }
-    *(bf16x8*)dst = v;
+    if (ep.dot_o) {
+      // the 4 chunks of one (row, head) sit in 4 consecutive lanes (head_dim 32)
+      dot += __shfl_xor(dot, 1);
+      dot += __shfl_xor(dot, 2);
+      if (valid && (c & 3) == 0) ep.dot_out[(int64_t)(n / ep.hd) * ep.n_tok + m] = dot;
+    }
   }
 }
 
@@ -401,10 +418,13 @@ hipError_t launch_proj_fwd_bf16(const swin_attn_plan* p, const void* o, const vo
 }
 
 // Backward GEMM pieces, used by the backward driver.
-hipError_t launch_dproj_bf16(const swin_attn_plan* p, const void* dy, const void* wprojT, void* dO, hipStream_t s) {
+hipError_t launch_dproj_bf16(const swin_attn_plan* p, const void* dy, const void* wprojT, void* dO, const void* o,
+                             float* dd, hipStream_t s) {
   EpiParams ep{};
-  ep.mode = 1;  // head-split, one plane
+  ep.mode = 1;  // head-split, one plane, plus D = rowsum(dO * O) per head
   ep.out = (bf16*)dO;
+  ep.dot_o = (const bf16*)o;
+  ep.dot_out = dd;
   ep.qscale = 1.f;
   ep.C = p->C;
   ep.nh = p->nh;

@@ -321,7 +321,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
     }
   }
   build_work(p->classes, p->nh, 4096, 16, p->fwd_work, p->fwd_ranges);
-  build_work(p->classes, p->nh, 2048, 32, p->bwd_work, p->bwd_ranges);
+  build_work(p->classes, p->nh, 2048, kMaxChunk, p->bwd_work, p->bwd_ranges);
 
   // saved state and workspace layout
   const size_t es = desc->dtype == SWIN_BF16 ? 2 : 4;
@@ -353,7 +353,8 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
     const size_t part_proj = (size_t)p->wgrad_splits_proj * (C * C + C);
     p->bwd_part = align256(std::max(part_qkv, part_proj) * 4);
     p->bwd_dbias_part = align256(p->bwd_work.size() * (size_t)p->nh * (size_t)p->nbins * 4);
-    p->bwd_total = p->bwd_do + p->bwd_dqkv + p->bwd_wt + p->bwd_part + p->bwd_dbias_part;
+    p->bwd_dd = align256(nt * (size_t)p->nh * 4);
+    p->bwd_total = p->bwd_do + p->bwd_dqkv + p->bwd_wt + p->bwd_part + p->bwd_dbias_part + p->bwd_dd;
   }
 
   hipError_t e = hipGetDevice(&p->device);
@@ -450,7 +451,7 @@ swin_status swin_attn_bwd(const swin_attn_plan* plan, const void* dy, const void
     return fail(SWIN_ERR_ARG, "NULL input or output pointer");
   if (dx == dy || dx == x) return fail(SWIN_ERR_ARG, "dx must not alias dy or x");
   if (plan->stats.max_tokens > 16 * kMaxBwdTiles)
-    return fail(SWIN_ERR_UNSUPPORTED, "backward supports windows of at most 192 tokens");
+    return fail(SWIN_ERR_UNSUPPORTED, "backward supports windows of at most 160 tokens");
   if (!ws || ws_bytes < plan->bwd_total) return fail(SWIN_ERR_WORKSPACE, "backward workspace too small");
   return hip_status(launch_bwd_bf16(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_qkv, dw_proj,
                                     db_proj, dbias_table, ws, (hipStream_t)stream),

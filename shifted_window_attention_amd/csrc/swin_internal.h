@@ -39,7 +39,8 @@ struct WorkRange {
 };
 
 constexpr int kMaxFwdTiles = 16;  // forward: windows of up to 256 tokens
-constexpr int kMaxBwdTiles = 12;  // backward: windows of up to 192 tokens (LDS budget)
+constexpr int kMaxBwdTiles = 10;  // backward: windows of up to 160 tokens (LDS budget)
+constexpr int kMaxChunk = 32;     // windows per attention work item
 
 struct DevTables {
   int32_t* perm = nullptr;       // [n_tok] window-major slot -> grid row
