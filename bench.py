@@ -153,6 +153,31 @@ def cpu_baseline(cfg, inp, seconds):
             "seconds": round(elapsed, 2)}
 
 
+def _device_inputs(cfg):
+    """Inputs of the same shapes and scales as the seeded recipe, drawn on the GPU."""
+    import types
+    import numpy as np
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    C = cfg.channels
+    D, H, W = cfg.grid
+    shape = (cfg.batch, D, H, W, C)
+
+    def bits(t):
+        return t.to(torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16)
+    mods = []
+    for _ in range(cfg.modules):
+        wq = torch.randn(3 * C, C, device="cuda", generator=g) * (2.0 / (4 * C)) ** 0.5
+        wp = torch.randn(C, C, device="cuda", generator=g) * (1.0 / C) ** 0.5
+        t = (torch.randn(cfg.bias_table_shape(), device="cuda", generator=g) * 0.02).cpu().numpy()
+        mods.append(types.SimpleNamespace(w_qkv_dev=bits(wq), b_qkv_dev=np.zeros(3 * C, np.uint16),
+                                          w_proj_dev=bits(wp), b_proj_dev=np.zeros(C, np.uint16), table_dev=t))
+    x = torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16)
+    dy = torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16)
+    return types.SimpleNamespace(modules=mods, x_t=x, dy_t=dy)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,6 +185,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--device-inputs", action="store_true",
+                    help="draw inputs on the GPU (torch generator, same shapes and scales) instead of the seeded "
+                         "host recipe: starts in seconds, for profiler runs; implies --no-cpu-baseline")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
@@ -175,12 +203,18 @@ def main():
     from workloads import get_config, make_inputs
 
     cfg = get_config("highres")
-    log("bench: generating inputs", cfg.description)
-    inp = make_inputs(cfg, bias_scale=0.0)
     torch.cuda.set_device(0)
+    if args.device_inputs:
+        args.no_cpu_baseline = True
+        log("bench: drawing inputs on the device", cfg.description)
+        inp = _device_inputs(cfg)
+        x, dy = inp.x_t, inp.dy_t
+    else:
+        log("bench: generating inputs", cfg.description)
+        inp = make_inputs(cfg, bias_scale=0.0)
+        x = to_dev(inp.x_dev, "bf16")
+        dy = to_dev(inp.dy_dev, "bf16")
     mods = [ModuleOnDevice(cfg, i, p) for i, p in enumerate(inp.modules)]
-    x = to_dev(inp.x_dev, "bf16")
-    dy = to_dev(inp.dy_dev, "bf16")
     C = cfg.channels
     y1 = torch.empty_like(x)
     y2 = torch.empty_like(x)

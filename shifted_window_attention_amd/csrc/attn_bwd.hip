@@ -49,26 +49,6 @@ struct BwdArgs {
   float tau;
 };
 
-__device__ __forceinline__ void coords_of(const ClassInfo& ci, int j, int& ld, int& lh, int& lw, int& lab) {
-  lw = j % ci.ext[2];
-  const int r = j / ci.ext[2];
-  lh = r % ci.ext[1];
-  ld = r / ci.ext[1];
-  lab = (ld >= ci.split[0] ? 1 : 0) | (lh >= ci.split[1] ? 2 : 0) | (lw >= ci.split[2] ? 4 : 0);
-}
-
-__device__ __forceinline__ float bias2_of(const ClassInfo& ci, const float* __restrict__ tab, const int* win, int q,
-                                          int k) {
-  if (q >= ci.n || k >= ci.n) return -INFINITY;
-  int qd, qh, qw, ql, kd, kh, kw, kl;
-  coords_of(ci, q, qd, qh, qw, ql);
-  coords_of(ci, k, kd, kh, kw, kl);
-  if (ql != kl) return -INFINITY;
-  const int bin = ((qd - kd + win[0] - 1) * (2 * win[1] - 1) + (qh - kh + win[1] - 1)) * (2 * win[2] - 1) +
-                  (qw - kw + win[2] - 1);
-  return tab[bin] * kLog2e;
-}
-
 template <int NKT>
 struct BwdBuf {
   static constexpr int ROWS = (NKT + 1) / 2 * 32;  // staged rows per tile (32-row chunks)
@@ -94,7 +74,10 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) BwdBuf<NKT> bufB;
   __shared__ __attribute__((aligned(16))) bf16 dSs[16 * NKT * SP];
   __shared__ int offs[kMaxChunk];
-  extern __shared__ float bins_lds[];  // [nbins], dynamic
+  __shared__ int codes[16 * NKT];  // per-token local-offset codes and wrap labels
+  extern __shared__ float dyn_lds[];   // [2 nbins]: bias-gradient bins, then the scaled table
+  float* bins_lds = dyn_lds;
+  float* tab_lds = dyn_lds + a.nbins;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -107,6 +90,7 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
   const int key = 16 * kt + li;
   const float* tab = a.table + (int64_t)h * a.nbins;
   if (tid < wk.count) offs[tid] = a.win_off[a.class_win[wk.first + tid]];
+  if (tid < 16 * NKT) codes[tid] = tid < n ? token_code(tid, ci.ext, ci.split, a.win) : 0;
   const int64_t off0 = a.win_off[a.class_win[wk.first]];
 
   const bf16* Qh = a.qkv + ((int64_t)(0 * a.nh + h) * a.n_tok) * 32;
@@ -130,21 +114,31 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
     constexpr int EXTRA = ROWS - 16 * NKT;
     for (int c = tid; c < 16 * NKT * EXTRA; c += NT) dSs[(c / EXTRA) * SP + 16 * NKT + c % EXTRA] = to_bf16(0.f);
   }
-  for (int i = tid; i < a.nbins; i += NT) bins_lds[i] = 0.f;
+  for (int i = tid; i < a.nbins; i += NT) {
+    bins_lds[i] = 0.f;
+    tab_lds[i] = tab[i] * kLog2e;
+  }
   stage(off0, bufA);
+  __syncthreads();  // table, offsets and zeroed regions in LDS
 
   // lane's bias + mask for every query tile (S layout: key fixed, queries 16 qt + 4 g + i),
   // held as fp16 to leave registers for the dS sums: |error| <= 2^-11 |bias|, -inf exact
   typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  const int code0 = code0_of(a.win);
+  const int ckey = codes[key];
   h4 bias[NKT];
   f32x4 dbacc[NKT];
 #pragma unroll
-  for (int qt = 0; qt < NKT; ++qt)
+  for (int qt = 0; qt < NKT; ++qt) {
+    const int4 cq = *(const int4*)(codes + 16 * qt + 4 * g);
+    const int qq[4] = {cq.x, cq.y, cq.z, cq.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      bias[qt][i] = (_Float16)bias2_of(ci, tab, a.win, 16 * qt + 4 * g + i, key);
+      const int q = 16 * qt + 4 * g + i;
+      bias[qt][i] = (_Float16)((q >= n || key >= n) ? -INFINITY : pair_bias_codes(qq[i], ckey, code0, tab_lds));
       dbacc[qt][i] = 0.f;
     }
+  }
   const int C = a.C;
   const float inv_log2e = 1.f / kLog2e;
   __syncthreads();
@@ -262,21 +256,24 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
       }
     __syncthreads();
     for (int b = tid; b < a.nbins; b += NT) {
-      // bin b <-> offset (query minus key) along each axis
+      // bin b <-> offset (query minus key) along each axis; its pairs are (q, q - offset)
       const int tw = 2 * a.win[2] - 1, th = 2 * a.win[1] - 1;
       const int rw = b % tw - (a.win[2] - 1);
       const int rh = (b / tw) % th - (a.win[1] - 1);
       const int rd = b / (tw * th) - (a.win[0] - 1);
+      const int dk = (rd * ci.ext[1] + rh) * ci.ext[2] + rw;  // token-index offset of the pair
       float sum = bins_lds[b];
       const int q1 = q0 + SLAB < n ? q0 + SLAB : n;
-      for (int q = q0; q < q1; ++q) {
-        const int qw = q % ci.ext[2], qr = q / ci.ext[2];
-        const int qh = qr % ci.ext[1], qd = qr / ci.ext[1];
-        const int kw = qw - rw, kh = qh - rh, kd = qd - rd;
-        if (kw < 0 || kw >= ci.ext[2] || kh < 0 || kh >= ci.ext[1] || kd < 0 || kd >= ci.ext[0]) continue;
-        const int k = (kd * ci.ext[1] + kh) * ci.ext[2] + kw;
-        sum += acc[(q - q0) * kcols + k];
-      }
+      // queries whose key (q - offset) lies inside the window extent, walked row by row
+      for (int qd = rd > 0 ? rd : 0; qd < ci.ext[0] + (rd < 0 ? rd : 0); ++qd)
+        for (int qh = rh > 0 ? rh : 0; qh < ci.ext[1] + (rh < 0 ? rh : 0); ++qh) {
+          const int row = (qd * ci.ext[1] + qh) * ci.ext[2];
+          const int w0 = rw > 0 ? rw : 0, w1 = ci.ext[2] + (rw < 0 ? rw : 0);
+          for (int qw = w0; qw < w1; ++qw) {
+            const int q = row + qw;
+            if (q >= q0 && q < q1) sum += acc[(q - q0) * kcols + (q - dk)];
+          }
+        }
       bins_lds[b] = sum;
     }
     __syncthreads();
@@ -364,7 +361,7 @@ hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* 
   a.nbins = p->nbins;
   for (int i = 0; i < 3; ++i) a.win[i] = p->d.window[i];
   a.tau = p->tau;
-  const size_t dyn = (size_t)p->nbins * sizeof(float);
+  const size_t dyn = 2 * (size_t)p->nbins * sizeof(float);
   for (const auto& r : p->bwd_ranges) {
     a.work = p->dev.bwd_work + r.begin;
     a.item_base = r.begin;

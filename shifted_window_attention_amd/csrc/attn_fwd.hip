@@ -15,11 +15,12 @@
 // window w is computed (one barrier per window).
 //
 // The logits are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16), so a lane
-// holds one query and 4 consecutive keys of every 16-key tile: the row max and row sum
-// are in-register reductions plus two cross-lane steps, and the probabilities of two
-// adjacent key tiles are already the B operand of O^T = V^T P^T. The V^T operand is read
-// from the row-major V tile with gfx950's transposing LDS read. A window has at most 256
-// tokens, so a query's whole key row lives in registers and the softmax is exact in a
+// holds one query and 4 consecutive keys of every 16-key tile. The row max is an
+// in-register reduction plus two cross-lane steps; the row sum comes from the matrix core
+// (an all-ones operand against the same bf16 P as the PV product); and the probabilities
+// of two adjacent key tiles are already the B operand of O^T = V^T P^T. The V^T operand is
+// read from the row-major V tile with gfx950's transposing LDS read. A window has at most
+// 256 tokens, so a query's whole key row lives in registers and the softmax is exact in a
 // single pass (no online rescaling).
 #include "device_common.h"
 #include "swin_internal.h"
@@ -40,28 +41,6 @@ struct AttnArgs {
   int win[3];               // nominal window (wd, wh, ww)
 };
 
-// Local coordinates and label bits of token j of a window class.
-__device__ __forceinline__ void token_coords(const ClassInfo& ci, int j, int& ld, int& lh, int& lw, int& lab) {
-  lw = j % ci.ext[2];
-  const int r = j / ci.ext[2];
-  lh = r % ci.ext[1];
-  ld = r / ci.ext[1];
-  lab = (ld >= ci.split[0] ? 1 : 0) | (lh >= ci.split[1] ? 2 : 0) | (lw >= ci.split[2] ? 4 : 0);
-}
-
-// Logit offset (log2 units) of query q against key k, or -inf if the pair is not allowed.
-__device__ __forceinline__ float pair_bias2(const ClassInfo& ci, const float* __restrict__ tab, const int* win,
-                                            int q, int k) {
-  if (k >= ci.n) return -INFINITY;
-  int qd, qh, qw, ql, kd, kh, kw, kl;
-  token_coords(ci, q, qd, qh, qw, ql);
-  token_coords(ci, k, kd, kh, kw, kl);
-  if (ql != kl) return -INFINITY;
-  const int bin = ((qd - kd + win[0] - 1) * (2 * win[1] - 1) + (qh - kh + win[1] - 1)) * (2 * win[2] - 1) +
-                  (qw - kw + win[2] - 1);
-  return tab[bin] * kLog2e;
-}
-
 template <int NKT>
 struct FwdBuf {
   static constexpr int ROWS = (NKT + 1) / 2 * 32;  // staged rows per tile (32-key chunks)
@@ -79,6 +58,8 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) FwdBuf<NKT> bufA;
   __shared__ __attribute__((aligned(1024))) FwdBuf<NKT> bufB;
   __shared__ int offs[kMaxChunk];
+  __shared__ int codes[16 * NKT];     // per-token local-offset codes and wrap labels
+  extern __shared__ float tab_lds[];  // [nbins]: the head's bias table times log2(e)
 
   const int lane = threadIdx.x & 63;
   const int qt = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -90,7 +71,9 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
   const int q = qt * 16 + li;
   const bool qv = q < n;
   const float* tab = a.table + (int64_t)h * a.nbins;
+  for (int i = threadIdx.x; i < a.nbins; i += 64 * NKT) tab_lds[i] = tab[i] * kLog2e;
   if (threadIdx.x < wk.count) offs[threadIdx.x] = a.win_off[a.class_win[wk.first + threadIdx.x]];
+  if (threadIdx.x < 16 * NKT) codes[threadIdx.x] = threadIdx.x < n ? token_code(threadIdx.x, ci.ext, ci.split, a.win) : 0;
   const int64_t off0 = a.win_off[a.class_win[wk.first]];
 
   const bf16* Qh = a.qkv + ((int64_t)(0 * a.nh + h) * a.n_tok) * 32;
@@ -104,12 +87,23 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
     stage_rows(make_rsrc(Vh + off * 32, bytes), b.v, ROWS, qt, NKT, lane);
   };
   stage(off0, bufA);
+  __syncthreads();  // table and offsets in LDS
 
+  // bias + mask of this lane's query against every key; keys past n are masked, and
+  // queries past n (whose outputs are dropped) get finite zeros
+  const int code0 = code0_of(a.win);
+  const int cq = codes[q];
   f32x4 bias[NKT];
 #pragma unroll
-  for (int kt = 0; kt < NKT; ++kt)
+  for (int kt = 0; kt < NKT; ++kt) {
+    const int4 ck = *(const int4*)(codes + 16 * kt + 4 * g);
+    const int kk[4] = {ck.x, ck.y, ck.z, ck.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bias[kt][i] = qv ? pair_bias2(ci, tab, a.win, q, 16 * kt + 4 * g + i) : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int k = 16 * kt + 4 * g + i;
+      bias[kt][i] = !qv ? 0.f : (k >= n ? -INFINITY : pair_bias_codes(cq, kk[i], code0, tab_lds));
+    }
+  }
   __syncthreads();
 
   // a window's results are stored at the start of the next iteration, after the next
@@ -125,6 +119,9 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
       if (g == 0) a.lse[(int64_t)h * a.n_tok + prev_off + q] = lse_v;
     }
   };
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = to_bf16(1.f);
   auto window = [&](int w, const FwdBuf<NKT>& cur, FwdBuf<NKT>& nxt) {
     const int64_t off = offs[w];
     if (w + 1 < wk.count) stage(offs[w + 1], nxt);  // overlaps with this window's compute
@@ -139,18 +136,15 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) m = fmaxf(m, s[kt][i]);
     m = wave_max_xor16_32(m);
-    float l = 0.f;
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(s[kt][i] - m);
-        s[kt][i] = p;
-        l += p;
-      }
-    l = wave_sum_xor16_32(l);
+      for (int i = 0; i < 4; ++i) s[kt][i] = fast_exp2(s[kt][i] - m);
 
+    // O^T = V^T P^T, and the row sums of the same bf16 P from an all-ones A operand: every row
+    // of that product is the lane's query sum, so no cross-lane reduction is needed
     f32x4 oacc[2] = {f32x4{}, f32x4{}};
+    f32x4 lacc = f32x4{};
 #pragma unroll
     for (int c = 0; c < NKC; ++c) {
       bf16x8 pb;
@@ -161,7 +155,9 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
       }
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) oacc[dt] = mfma16(tile_frag_tr(cur.v, 32 * c, 16 * dt, g, li), pb, oacc[dt]);
+      lacc = mfma16(ones, pb, lacc);
     }
+    const float l = lacc[0];
     const float inv = 1.f / l;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
@@ -180,7 +176,7 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
 
 template <int NKT>
 static void launch_one(const AttnArgs& a, int n_items, int nh, hipStream_t s) {
-  k_attn_fwd<NKT><<<dim3((unsigned)n_items, (unsigned)nh), 64 * NKT, 0, s>>>(a);
+  k_attn_fwd<NKT><<<dim3((unsigned)n_items, (unsigned)nh), 64 * NKT, (size_t)a.nbins * sizeof(float), s>>>(a);
 }
 
 typedef void (*fwd_launcher)(const AttnArgs&, int, int, hipStream_t);

@@ -170,6 +170,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_nt(const bf16* __restrict__ A, 
   __syncthreads();
   constexpr int CH_PER_ROW = BN / 8;
   static_assert((BM * CH_PER_ROW) % Cfg::NT == 0, "uniform copy-out loop");
+#pragma unroll 4
   for (int c = tid; c < BM * CH_PER_ROW; c += Cfg::NT) {
     const int row = c / CH_PER_ROW;
     const int cc = (c % CH_PER_ROW) * 8;
