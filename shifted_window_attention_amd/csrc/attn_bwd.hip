@@ -31,12 +31,13 @@ namespace swin {
 
 struct BwdArgs {
   const bf16* qkv;          // saved [3][nh][n_tok][32] (q pre-scaled)
-  const bf16* o;            // saved [n_tok][C]
+  const bf16* o;            // saved [n_tok][C], grid order
   const float* lse;         // saved [nh][n_tok] (log2 units)
   const bf16* dO;           // [nh][n_tok][32]
   const float* dd;          // [nh][n_tok]: D = rowsum(dO * O)
   const float* table;       // [nh][nbins]
-  bf16* dqkv;               // [n_tok][3C]
+  bf16* dqkv;               // [n_tok][3C], grid order (row perm[slot])
+  const int32_t* perm;      // window-major slot -> grid row
   float* dbias_part;        // [n_items_total][nh][nbins]
   const WorkItem* work;     // this launch's items
   int item_base;            // index of work[0] among all backward work items
@@ -55,6 +56,7 @@ struct BwdBuf {
   static constexpr int FROWS = (ROWS + 63) / 64 * 64;  // float rows: whole 64-lane copies
   unsigned char q[ROWS * 64], dO[ROWS * 64], k[ROWS * 64], v[ROWS * 64];
   float lse[FROWS], dd[FROWS];
+  int grow[FROWS];  // grid row of each token of the window
 };
 
 template <int NKT>
@@ -108,6 +110,7 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
     stage_rows(make_rsrc(Vh + off * 32, bytes), b.v, ROWS, kt, NKT, lane);
     stage_floats(make_rsrc(LSEh + off, (uint32_t)n * 4), b.lse, BwdBuf<NKT>::FROWS, kt, NKT, lane);
     stage_floats(make_rsrc(Dh + off, (uint32_t)n * 4), b.dd, BwdBuf<NKT>::FROWS, kt, NKT, lane);
+    stage_floats(make_rsrc(a.perm + off, (uint32_t)n * 4), (float*)b.grow, BwdBuf<NKT>::FROWS, kt, NKT, lane);
   };
   // key columns of dS that no wave owns (odd tile count) are read by dQ: keep them zero
   if constexpr (ROWS > 16 * NKT) {
@@ -149,11 +152,12 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
   // next copies are issued.
   bf16x4 pq[2] = {};
   int64_t prev_off = -1;
+  int prev_row = 0;  // grid row of this lane's dq row in the previous window
   auto flush = [&]() {
     if (prev_off < 0) return;
     const int q = 16 * kt + li;
     if (q < n) {
-      bf16* row = a.dqkv + (prev_off + q) * (3 * C) + h * 32;
+      bf16* row = a.dqkv + (int64_t)prev_row * (3 * C) + h * 32;
       *(bf16x4*)(row + 4 * g) = pq[0];
       *(bf16x4*)(row + 16 + 4 * g) = pq[1];
     }
@@ -204,7 +208,7 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
     }
     __syncthreads();  // dS complete (no stores are outstanding here, so copies stay in flight)
     if (key < n) {
-      bf16* row = a.dqkv + (off + key) * (3 * C) + h * 32;
+      bf16* row = a.dqkv + (int64_t)cur.grow[key] * (3 * C) + h * 32;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         bf16x4 k4, v4;
@@ -235,6 +239,7 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
       }
     }
     prev_off = off;
+    prev_row = cur.grow[16 * kt + li];
     __syncthreads();  // window w+1 staged; this buffer and dS are free
   };
   for (int w = 0; w < wk.count; w += 2) {
@@ -307,9 +312,8 @@ hipError_t launch_dproj_bf16(const swin_attn_plan* p, const void* dy, const void
                              float* dd, hipStream_t s);
 hipError_t launch_dgrad_qkv_bf16(const swin_attn_plan* p, const void* dqkv, const void* wqkvT, void* dx,
                                  hipStream_t s);
-hipError_t launch_wgrad_bf16(const bf16* A, int64_t lda, const int32_t* a_rows, const bf16* B, int64_t ldb,
-                             const int32_t* b_rows, int64_t T, int M, int N, int splits, int64_t chunk, float* part,
-                             float* dw, float* db, hipStream_t s);
+hipError_t launch_wgrad_bf16(const bf16* A, int64_t lda, const bf16* B, int64_t ldb, int64_t T, int M, int N,
+                             int splits, int64_t chunk, float* part, float* dw, float* db, hipStream_t s);
 hipError_t launch_transpose_bf16(const void* in, void* out, int R, int Cn, hipStream_t s);
 
 hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* x, const void* w_qkv,
@@ -338,8 +342,8 @@ hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* 
   if (e == hipSuccess) e = launch_dproj_bf16(p, dy, wprojT, dO, o, dd, s);
   if (e == hipSuccess) e = trace_mark(s);
   if (e == hipSuccess)
-    e = launch_wgrad_bf16((const bf16*)dy, C, p->dev.perm, o, C, nullptr, p->n_tok, C, C, p->wgrad_splits_proj,
-                          p->wgrad_chunk_proj, part, dw_proj, db_proj, s);
+    e = launch_wgrad_bf16((const bf16*)dy, C, o, C, p->n_tok, C, C, p->wgrad_splits_proj, p->wgrad_chunk_proj, part,
+                          dw_proj, db_proj, s);
   if (e == hipSuccess) e = trace_mark(s);
   if (e != hipSuccess) return e;
   // attention core backward
@@ -351,6 +355,7 @@ hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* 
   a.dd = dd;
   a.table = table;
   a.dqkv = dqkv;
+  a.perm = p->dev.perm;
   a.dbias_part = dbias_part;
   a.classes = p->dev.classes;
   a.class_win = p->dev.class_win;
@@ -380,8 +385,8 @@ hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* 
   e = launch_dgrad_qkv_bf16(p, dqkv, wqkvT, dx, s);
   if (e == hipSuccess) e = trace_mark(s);
   if (e == hipSuccess)
-    e = launch_wgrad_bf16(dqkv, 3 * C, nullptr, (const bf16*)x, C, p->dev.perm, p->n_tok, 3 * C, C,
-                          p->wgrad_splits_qkv, p->wgrad_chunk_qkv, part, dw_qkv, db_qkv, s);
+    e = launch_wgrad_bf16(dqkv, 3 * C, (const bf16*)x, C, p->n_tok, 3 * C, C, p->wgrad_splits_qkv,
+                          p->wgrad_chunk_qkv, part, dw_qkv, db_qkv, s);
   if (e == hipSuccess) e = trace_mark(s);
   return e;
 }

@@ -30,7 +30,8 @@ namespace swin {
 struct AttnArgs {
   const bf16* qkv;          // [3][nh][n_tok][32]
   const float* table;       // [nh][nbins]
-  bf16* o;                  // [n_tok][C]
+  bf16* o;                  // [n_tok][C], grid order (row perm[slot])
+  const int32_t* perm;      // window-major slot -> grid row
   float* lse;               // [nh][n_tok]
   const WorkItem* work;
   const ClassInfo* classes;
@@ -43,8 +44,10 @@ struct AttnArgs {
 
 template <int NKT>
 struct FwdBuf {
-  static constexpr int ROWS = (NKT + 1) / 2 * 32;  // staged rows per tile (32-key chunks)
+  static constexpr int ROWS = (NKT + 1) / 2 * 32;      // staged rows per tile (32-key chunks)
+  static constexpr int FROWS = (ROWS + 63) / 64 * 64;  // word rows: whole 64-lane copies
   unsigned char q[ROWS * 64], k[ROWS * 64], v[ROWS * 64];
+  int grow[FROWS];  // grid row of each token of the window
 };
 
 template <int NKT>
@@ -85,6 +88,7 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
     stage_rows(make_rsrc(Qh + off * 32, bytes), b.q, ROWS, qt, NKT, lane);
     stage_rows(make_rsrc(Kh + off * 32, bytes), b.k, ROWS, qt, NKT, lane);
     stage_rows(make_rsrc(Vh + off * 32, bytes), b.v, ROWS, qt, NKT, lane);
+    stage_floats(make_rsrc(a.perm + off, (uint32_t)n * 4), (float*)b.grow, FwdBuf<NKT>::FROWS, qt, NKT, lane);
   };
   stage(off0, bufA);
   __syncthreads();  // table and offsets in LDS
@@ -111,9 +115,10 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
   bf16x4 ov[2] = {};
   float lse_v = 0.f;
   int64_t prev_off = -1;
+  int prev_row = 0;  // grid row of this lane's query in the previous window
   auto flush = [&]() {
     if (prev_off >= 0 && qv) {
-      bf16* orow = a.o + (prev_off + q) * a.C + h * 32;
+      bf16* orow = a.o + (int64_t)prev_row * a.C + h * 32;
       *(bf16x4*)(orow + 4 * g) = ov[0];
       *(bf16x4*)(orow + 16 + 4 * g) = ov[1];
       if (g == 0) a.lse[(int64_t)h * a.n_tok + prev_off + q] = lse_v;
@@ -165,6 +170,7 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
       for (int i = 0; i < 4; ++i) ov[dt][i] = to_bf16(oacc[dt][i] * inv);
     lse_v = m + fast_log2(l);
     prev_off = off;
+    prev_row = cur.grow[q];
     __syncthreads();  // window w+1 staged; this buffer is free
   };
   for (int w = 0; w < wk.count; w += 2) {
@@ -192,6 +198,7 @@ hipError_t launch_attn_fwd_bf16(const swin_attn_plan* p, const void* qkv, const 
   a.qkv = (const bf16*)qkv;
   a.table = table;
   a.o = (bf16*)o;
+  a.perm = p->dev.perm;
   a.lse = lse;
   a.classes = p->dev.classes;
   a.class_win = p->dev.class_win;

@@ -27,7 +27,8 @@ struct EpiParams {
   int C, nh, hd;
   int64_t n_tok;
   const bf16* dot_o;         // mode 1, one plane: if set, also write dot_out[head][m] =
-  float* dot_out;            //   sum over the head's columns of C[m, :] * dot_o[m, :]
+  float* dot_out;            //   sum over the head's columns of C[m, :] * dot_o[row(m), :]
+  const int32_t* dot_rows;   //   with row(m) = dot_rows[m] (NULL: m)
 };
 
 template <int BM, int BN>
@@ -193,7 +194,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_nt(const bf16* __restrict__ A, 
       }
       *(bf16x8*)dst = v;
       if (ep.dot_o) {
-        const bf16x8 ov = *(const bf16x8*)(ep.dot_o + m * ep.C + n);
+        const int64_t orow = ep.dot_rows ? (int64_t)ep.dot_rows[m] : m;
+        const bf16x8 ov = *(const bf16x8*)(ep.dot_o + orow * ep.C + n);
 #pragma unroll
         for (int e = 0; e < 8; ++e) dot += to_f32(v[e]) * to_f32(ov[e]);
       }
@@ -208,148 +210,177 @@ __global__ __launch_bounds__(256, 2) void k_gemm_nt(const bf16* __restrict__ A, 
 }
 
 // ---------------------------------------------------------------------------
-// Weight-gradient GEMM: P[s][m][n] = sum over tokens t of chunk s of A[t][m] * B[t][n].
-// Both operands are token-major and are staged in LDS as loaded (token rows, 16-byte
-// coalesced pieces). The MFMA fragments need 8 consecutive tokens per lane at a fixed
-// column; gfx950's transposing LDS read (ds_read_b64_tr_b16) returns exactly that from
-// the row-major tile, so no transposed copy is made. Workgroups of the first column
-// tile also produce the column sums of A (the bias gradients) for their chunk.
+// Weight-gradient GEMM: P[s] = sum over the tokens t of chunk s of A[t, m0:m0+256]^T B[t, n0:n0+256]
+// (both operands token-major: a contraction over tokens), stored transposed per split as
+// P[s][n][m] so that each lane's four consecutive MFMA rows are one 16-byte store.
+//
+// 256 x 256 output tile, 8 waves of 128 x 64 (v_mfma_f32_32x32x16_bf16, 128 accumulators
+// per lane), 64-token steps. Both 64 x 256 operand tiles are copied straight into LDS
+// (buffer_load ... lds, no staging registers), double-buffered so step k+1 is in flight
+// while step k is computed. The copy's buffer range ends at the chunk's last token, so the
+// token tail arrives as zeros. The MFMA fragments need 8 consecutive tokens at one column:
+// gfx950's transposing LDS read returns them from the token-major tile. Within each 512-byte
+// tile row, 16-byte chunk c is stored at slot c ^ 4 (r & 3), which puts the 4 rows x 2
+// chunks that one 16-lane group reads, and the neighbouring group's, in 16 distinct banks.
+//
+// Workgroups of the first column tile also sum A's columns (the bias gradients) on the
+// vector ALUs from the same LDS tiles, combined in a fixed order.
 // ---------------------------------------------------------------------------
-struct TnCfg {
-  static constexpr int NT = 256;
-  static constexpr int BM = 128, BN = 128, BK = 64;   // BK tokens per step
-  static constexpr int PITCH = 128 + 16;               // 72 dwords: the 4 rows of a transposed read hit distinct banks
-  static constexpr int TM = 2, TN = 2;                 // 4 waves, 2x2, wave tile 64x64
-  static constexpr int CH = BK * (BM / 8) / NT;        // 16-byte chunks per thread and operand (4)
+namespace tn {
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int NT = 512, NW = NT / 64;    // threads, waves
+constexpr int WTM = 128, WTN = 64;       // per-wave tile
+constexpr int ROWB = 512;                // bytes per tile row (256 bf16)
+constexpr int TILEB = BK * ROWB;         // 32 KB per operand tile
+constexpr int CROWS = NT / 32;           // column-sum row groups (thread = 8 columns)
+struct Stage {
+  unsigned char a[TILEB], b[TILEB];
 };
+__device__ __forceinline__ int slot(int r, int c) { return c ^ (4 * (r & 3)); }
+}  // namespace tn
 
-// Four bf16 from a row-major LDS tile, transposed across each 16-lane group: lane i of the
-// group receives element (i % 4) of the 8-byte pieces addressed by lanes 4r + i/4, r = 0..3.
-__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
-
-// MFMA 32x32x16 fragment (8 consecutive k for column `col0 + lane%32`) from a [k][col] tile.
-__device__ __forceinline__ bf16x8 frag_tr(const bf16* tile, int pitch, int k0, int col0, int lane) {
+// 32x32x16 fragment: 8 consecutive tokens k0 + 8 (g>>1) + 0..7 at column col0 + lane % 32.
+__device__ __forceinline__ bf16x8 tn_frag(const unsigned char* tile, int k0, int col0, int lane) {
   const int g = lane >> 4, L = lane & 15;
-  const bf16* base = tile + (k0 + 8 * (g >> 1) + (L >> 2)) * pitch + col0 + 16 * (g & 1) + 4 * (L & 3);
-  const bf16x4 lo = lds_read_tr4(base);
-  const bf16x4 hi = lds_read_tr4(base + 4 * pitch);
+  const int r = k0 + 8 * (g >> 1) + (L >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (L & 3);
+  const int c = col >> 3, half = (L & 1) * 8;
+  const bf16x4 lo = lds_read_tr(tile + r * tn::ROWB + 16 * tn::slot(r, c) + half);
+  const bf16x4 hi = lds_read_tr(tile + (r + 4) * tn::ROWB + 16 * tn::slot(r + 4, c) + half);
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__global__ __launch_bounds__(256, 2) void k_gemm_tn(const bf16* __restrict__ A, int64_t lda,
-                                                    const int32_t* __restrict__ a_rows,
-                                                    const bf16* __restrict__ B, int64_t ldb,
-                                                    const int32_t* __restrict__ b_rows, int64_t T, int M, int N,
-                                                    int64_t chunk, int n_splits, float* __restrict__ part,
-                                                    float* __restrict__ dbpart) {
-  using Cfg = TnCfg;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * Cfg::BK * Cfg::PITCH];
-  __shared__ float colsum[16][Cfg::BM];
-  bf16* As = smem;                          // [BK tokens][PITCH]
-  bf16* Bs = smem + Cfg::BK * Cfg::PITCH;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+// Copy rows [0, 64) x 256 columns of a token-major operand (row pitch ld elements) starting
+// at `base` into a swizzled tile. The buffer range ends after column `cols` of row valid - 1
+// (the operand's last element when that row is its last), so rows past `valid` and that
+// row's columns past `cols` arrive as zeros and no copy reads past the operand. Earlier
+// rows' columns past `cols` hold the next row's values; they only feed outputs that are
+// never stored. Wave w issues 4 of the 32 one-kilobyte copies (2 rows each; lane l -> row
+// 2j + l/32, slot l%32).
+__device__ __forceinline__ void tn_stage(const bf16* base, int64_t ld, int valid, int cols, unsigned char* tile,
+                                         int w, int lane) {
+  const uint32_t bytes = (uint32_t)(((int64_t)(valid - 1) * ld + cols) * 2);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+#pragma unroll
+  for (int i = 0; i < 32 / tn::NW; ++i) {
+    const int j = w + tn::NW * i;
+    const int r = 2 * j + (lane >> 5);
+    const int c = tn::slot(r, lane & 31);  // slot lane%32 holds logical chunk slot ^ 4(r&3)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + 1024 * j), 16,
+                                             (uint32_t)(r * ld * 2 + 16 * c), 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ A, int64_t lda,
+                                                       const bf16* __restrict__ B, int64_t ldb, int64_t T, int M,
+                                                       int N, int64_t chunk, int n_splits,
+                                                       float* __restrict__ part, float* __restrict__ dbpart) {
+  __shared__ __attribute__((aligned(1024))) tn::Stage st0;
+  __shared__ __attribute__((aligned(1024))) tn::Stage st1;
+  __shared__ float colsum[tn::CROWS][tn::BM];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
   // tile order: N tile fastest, then M tile, then split (XCD-aware, see xcd_tile)
-  const int n_nt = (N + Cfg::BN - 1) / Cfg::BN, n_mt = (M + Cfg::BM - 1) / Cfg::BM;
+  const int n_nt = (N + tn::BN - 1) / tn::BN, n_mt = (M + tn::BM - 1) / tn::BM;
   int64_t ms;
   int ntile;
   if (!xcd_tile((int64_t)n_mt * n_nt * n_splits, n_nt, ms, ntile)) return;
-  const int m0 = (int)(ms % n_mt) * Cfg::BM, n0 = ntile * Cfg::BN;
+  const int m0 = (int)(ms % n_mt) * tn::BM, n0 = ntile * tn::BN;
   const int s = (int)(ms / n_mt);
   const int64_t t_begin = (int64_t)s * chunk;
   const int64_t t_end = t_begin + chunk < T ? t_begin + chunk : T;
   const bool do_db = dbpart != nullptr && ntile == 0;
+  const int steps = t_end > t_begin ? (int)((t_end - t_begin + tn::BK - 1) / tn::BK) : 0;
 
-  const int crow = tid >> 4;                // token row of chunk i: crow + 16 i
-  const int ccol = (tid & 15) * 8;          // column offset inside the tile
-  const bool a_ok = m0 + ccol < M, b_ok = n0 + ccol < N;
+  constexpr int TM = tn::WTM / 32, TN = tn::WTN / 32;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+  float csum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int crow = tid >> 5, cchunk = tid & 31;  // column sums: thread = 8 columns x 4 rows
 
-  f32x16 acc[Cfg::TM][Cfg::TN];
-#pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j) acc[i][j] = f32x16{};
-  float csum[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) csum[e] = 0.f;
-
-  bf16x8 ra[Cfg::CH], rb[Cfg::CH];
-  auto load = [&](int64_t t0) {
-#pragma unroll
-    for (int i = 0; i < Cfg::CH; ++i) {
-      const int64_t t = t0 + crow + 16 * i;
-      const bool tv = t < t_end;
-      const int64_t ga = tv ? (a_rows ? (int64_t)a_rows[t] : t) : 0;
-      const int64_t gb = tv ? (b_rows ? (int64_t)b_rows[t] : t) : 0;
-      ra[i] = (tv && a_ok) ? *(const bf16x8*)(A + ga * lda + m0 + ccol) : bf16x8{};
-      rb[i] = (tv && b_ok) ? *(const bf16x8*)(B + gb * ldb + n0 + ccol) : bf16x8{};
-    }
+  auto stage = [&](int k, tn::Stage& st) {
+    const int64_t t0 = t_begin + (int64_t)k * tn::BK;
+    const int valid = (int)(t_end - t0 < tn::BK ? t_end - t0 : tn::BK);
+    tn_stage(A + t0 * lda + m0, lda, valid, M - m0 < tn::BM ? M - m0 : tn::BM, st.a, wave, lane);
+    tn_stage(B + t0 * ldb + n0, ldb, valid, N - n0 < tn::BN ? N - n0 : tn::BN, st.b, wave, lane);
   };
-  auto store = [&]() {
+  auto compute = [&](const tn::Stage& st) {
+    // one K slice of lookahead: the fragments of slice ks+1 are read while slice ks multiplies
+    bf16x8 fa[2][TM], fb[2][TN];
 #pragma unroll
-    for (int i = 0; i < Cfg::CH; ++i) {
-      *(bf16x8*)(As + (crow + 16 * i) * Cfg::PITCH + ccol) = ra[i];
-      *(bf16x8*)(Bs + (crow + 16 * i) * Cfg::PITCH + ccol) = rb[i];
-      if (do_db) {
+    for (int i = 0; i < TM; ++i) fa[0][i] = tn_frag(st.a, 0, wm * tn::WTM + 32 * i, lane);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) csum[e] += to_f32(ra[i][e]);
+    for (int j = 0; j < TN; ++j) fb[0][j] = tn_frag(st.b, 0, wn * tn::WTN + 32 * j, lane);
+#pragma unroll
+    for (int ks = 0; ks < tn::BK / 16; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < tn::BK / 16) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = tn_frag(st.a, 16 * (ks + 1), wm * tn::WTM + 32 * i, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = tn_frag(st.b, 16 * (ks + 1), wn * tn::WTN + 32 * j, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fa[cur][i], fb[cur][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (do_db) {
+#pragma unroll
+      for (int rr = 0; rr < tn::BK / tn::CROWS; ++rr) {
+        const int r = crow + tn::CROWS * rr;
+        const bf16x8 v = *(const bf16x8*)(st.a + r * tn::ROWB + 16 * tn::slot(r, cchunk));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) csum[e] += to_f32(v[e]);
       }
     }
   };
-
-  if (t_begin < t_end) {
-    load(t_begin);
-    store();
+  if (steps > 0) stage(0, st0);
+  __syncthreads();
+  for (int k = 0; k < steps; k += 2) {
+    if (k + 1 < steps) stage(k + 1, st1);
+    compute(st0);
     __syncthreads();
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += Cfg::BK) {
-      const bool more = t0 + Cfg::BK < t_end;
-      if (more) load(t0 + Cfg::BK);
-#pragma unroll
-      for (int ks = 0; ks < Cfg::BK / 16; ++ks) {
-        bf16x8 fa[Cfg::TM], fb[Cfg::TN];
-#pragma unroll
-        for (int i = 0; i < Cfg::TM; ++i) fa[i] = frag_tr(As, Cfg::PITCH, ks * 16, wm * 64 + 32 * i, lane);
-#pragma unroll
-        for (int j = 0; j < Cfg::TN; ++j) fb[j] = frag_tr(Bs, Cfg::PITCH, ks * 16, wn * 64 + 32 * j, lane);
-#pragma unroll
-        for (int i = 0; i < Cfg::TM; ++i)
-#pragma unroll
-          for (int j = 0; j < Cfg::TN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
-      }
+    if (k + 1 < steps) {
+      if (k + 2 < steps) stage(k + 2, st0);
+      compute(st1);
       __syncthreads();
-      if (more) {
-        store();
-        __syncthreads();
-      }
     }
   }
 
+  // partial tile, transposed: P[s][n][m]; lane holds 4 consecutive m per 32x32 tile row group
   float* P = part + (int64_t)s * M * N;
   const int fr = lane & 31;
 #pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j) {
-      const int n = n0 + wn * 64 + 32 * j + fr;
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * tn::WTN + 32 * j + fr;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < M && n < N) P[(int64_t)m * N + n] = acc[i][j][r];
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + wm * tn::WTM + 32 * i + 8 * q + 4 * (lane >> 5);
+        if (n < N && m + 3 < M) {
+          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          *(f32x4*)(P + (int64_t)n * M + m) = v;
+        } else if (n < N) {
+          for (int e = 0; e < 4; ++e)
+            if (m + e < M) P[(int64_t)n * M + m + e] = acc[i][j][4 * q + e];
+        }
       }
     }
   if (do_db) {
-    // each column's 16 partial sums (one per token-row group) are combined in a fixed order
 #pragma unroll
-    for (int e = 0; e < 8; ++e) colsum[crow][ccol + e] = csum[e];
+    for (int e = 0; e < 8; ++e) colsum[crow][cchunk * 8 + e] = csum[e];
     __syncthreads();
-    if (tid < Cfg::BM) {
+    if (tid < tn::BM && m0 + tid < M) {
       float v = 0.f;
-      for (int q = 0; q < 16; ++q) v += colsum[q][tid];
-      if (m0 + tid < M) dbpart[(int64_t)s * M + m0 + tid] = v;
+      for (int q = 0; q < tn::CROWS; ++q) v += colsum[q][tid];  // fixed order
+      dbpart[(int64_t)s * M + m0 + tid] = v;
     }
   }
 }
@@ -362,6 +393,27 @@ __global__ void k_reduce_splits(const float* __restrict__ part, int S, int64_t s
   float acc = 0.f;
   for (int s = 0; s < S; ++s) acc += part[(int64_t)s * stride + i];
   out[i] = acc;
+}
+
+// out[m][n] = sum_{s < S} part[s][n][m] (transposed split partials), in order of s; a 32 x 32
+// tile per block through LDS so reads and writes are both row-contiguous.
+__global__ __launch_bounds__(256) void k_reduce_splits_t(const float* __restrict__ part, int S, int M, int N,
+                                                         float* __restrict__ out) {
+  __shared__ float tile[32][33];
+  const int m0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int k = ty; k < 32; k += 8) {
+    const int n = n0 + k, m = m0 + tx;
+    float acc = 0.f;
+    if (n < N && m < M)
+      for (int s = 0; s < S; ++s) acc += part[((int64_t)s * N + n) * M + m];
+    tile[k][tx] = acc;
+  }
+  __syncthreads();
+  for (int k = ty; k < 32; k += 8) {
+    const int m = m0 + k, n = n0 + tx;
+    if (m < M && n < N) out[(int64_t)m * N + n] = tile[tx][k];
+  }
 }
 
 // out[c][r] = in[r][c] for an R x Cn bf16 matrix.
@@ -409,8 +461,7 @@ hipError_t launch_proj_fwd_bf16(const swin_attn_plan* p, const void* o, const vo
                                 hipStream_t s) {
   EpiParams ep{};
   ep.mode = 0;
-  ep.out = (bf16*)y;
-  ep.out_rows = p->dev.perm;  // window reverse + un-shift: slot t goes back to grid row perm[t]
+  ep.out = (bf16*)y;  // o is in grid order already (the attention kernel put rows back)
   ep.ldc = p->C;
   ep.bias = (const bf16*)b;
   ep.qscale = 1.f;
@@ -425,6 +476,7 @@ hipError_t launch_dproj_bf16(const swin_attn_plan* p, const void* dy, const void
   ep.mode = 1;  // head-split, one plane, plus D = rowsum(dO * O) per head
   ep.out = (bf16*)dO;
   ep.dot_o = (const bf16*)o;
+  ep.dot_rows = p->dev.perm;  // o is in grid order
   ep.dot_out = dd;
   ep.qscale = 1.f;
   ep.C = p->C;
@@ -438,8 +490,7 @@ hipError_t launch_dgrad_qkv_bf16(const swin_attn_plan* p, const void* dqkv, cons
                                  hipStream_t s) {
   EpiParams ep{};
   ep.mode = 0;
-  ep.out = (bf16*)dx;
-  ep.out_rows = p->dev.perm;
+  ep.out = (bf16*)dx;  // dqkv is in grid order already
   ep.ldc = p->C;
   ep.qscale = 1.f;
   ep.C = p->C;
@@ -447,16 +498,15 @@ hipError_t launch_dgrad_qkv_bf16(const swin_attn_plan* p, const void* dqkv, cons
                  s);
 }
 
-hipError_t launch_wgrad_bf16(const bf16* A, int64_t lda, const int32_t* a_rows, const bf16* B, int64_t ldb,
-                             const int32_t* b_rows, int64_t T, int M, int N, int splits, int64_t chunk, float* part,
-                             float* dw, float* db, hipStream_t s) {
+hipError_t launch_wgrad_bf16(const bf16* A, int64_t lda, const bf16* B, int64_t ldb, int64_t T, int M, int N,
+                             int splits, int64_t chunk, float* part, float* dw, float* db, hipStream_t s) {
   float* dbpart = db ? part + (int64_t)splits * M * N : nullptr;
-  const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128) * splits;
-  k_gemm_tn<<<xcd_grid(tiles), 256, 0, s>>>(A, lda, a_rows, B, ldb, b_rows, T, M, N, chunk, splits, part, dbpart);
+  const int64_t tiles = (int64_t)((M + tn::BM - 1) / tn::BM) * ((N + tn::BN - 1) / tn::BN) * splits;
+  k_gemm_tn<<<xcd_grid(tiles), tn::NT, 0, s>>>(A, lda, B, ldb, T, M, N, chunk, splits, part, dbpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n = (int64_t)M * N;
-  k_reduce_splits<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, splits, n, n, dw);
+  k_reduce_splits_t<<<dim3((unsigned)((M + 31) / 32), (unsigned)((N + 31) / 32)), 256, 0, s>>>(part, splits, M, N,
+                                                                                               dw);
   e = hipGetLastError();
   if (e != hipSuccess || !db) return e;
   k_reduce_splits<<<(unsigned)((M + 255) / 256), 256, 0, s>>>(dbpart, splits, M, M, db);

@@ -331,18 +331,19 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
   p->saved_lse = align256(nt * (size_t)p->nh * 4);
   p->saved_total = p->saved_qkv + p->saved_o + p->saved_lse;
   if (desc->dtype == SWIN_BF16) {
-    // split-K for the weight gradients: enough output-tile x split workgroups to fill the chip
+    // split-K for the weight gradients: 256 x 256 output tiles, one workgroup per CU at a
+    // time, and at most two full rounds of workgroups (no partial third round)
     auto splits = [&](int64_t M, int64_t N) {
-      const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-      int64_t s = std::max<int64_t>(1, (1024 + tiles - 1) / tiles);
-      s = std::min<int64_t>(s, std::max<int64_t>(1, p->n_tok / 256));
+      const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+      int64_t s = std::max<int64_t>(1, 512 / tiles);
+      s = std::min<int64_t>(s, std::max<int64_t>(1, p->n_tok / 512));
       return (int)s;
     };
     p->wgrad_splits_qkv = splits(3 * C, C);
     p->wgrad_splits_proj = splits(C, C);
     auto chunk = [&](int s) {
       int64_t c = (p->n_tok + s - 1) / s;
-      return (c + 31) / 32 * 32;
+      return (c + 63) / 64 * 64;
     };
     p->wgrad_chunk_qkv = chunk(p->wgrad_splits_qkv);
     p->wgrad_chunk_proj = chunk(p->wgrad_splits_proj);
