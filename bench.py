@@ -4,7 +4,8 @@ One step = the whole hot path on the 540x1080-token, C=512, 16-head, 12x12-windo
 workload (a 2160x4320 field after 4x4 patch embedding): W-MSA forward, SW-MSA
 (shift 6,6) forward, SW-MSA backward, W-MSA backward, each module being gather +
 QKV GEMM + window attention + proj GEMM + scatter and their backward. Inputs are
-seeded synthetic data resident in HBM before the timed region.
+seeded synthetic data resident in HBM before the timed region. After the timed steps the
+window gather and scatter are also timed stand-alone against a device-to-device copy.
 
 Prints one JSON line on stdout:
   value = token-blocks per second (tokens x modules per step / step time),
@@ -85,9 +86,9 @@ def stage_flops_bytes(cfg, pairs):
     b = {"qkv_gemm": 2 * N * C + 2 * N * 3 * C,                     # x in, q/k/v out
          "attn_fwd": tok_head * (3 * 64 + 64 + 4),                  # q, k, v in; o, lse out
          "proj_gemm": 2 * N * C * 2,                                # o in, y out
-         "dproj_gemm": 2 * N * C * 2,                               # dy in, dO out
+         "dproj_gemm": 2 * N * C * 3 + tok_head * 4,                # dy, o in; dO, D = rowsum(dO o) out
          "wgrad_proj": 2 * N * C * 2,                               # dy, o in
-         "attn_bwd": tok_head * (5 * 64 + 4 + 3 * 64),              # q k v o dO lse in; dq dk dv out
+         "attn_bwd": tok_head * (4 * 64 + 2 * 4 + 3 * 64),          # q k v dO lse D in; dq dk dv out
          "dgrad_qkv": 2 * N * 3 * C + 2 * N * C,                    # dqkv in, dx out
          "wgrad_qkv": 2 * N * 3 * C + 2 * N * C,                    # dqkv, x in
          "w_transpose": 2 * 2 * 4 * C * C, "dbias_reduce": 0}
@@ -176,6 +177,36 @@ def _device_inputs(cfg):
     x = torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16)
     dy = torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16)
     return types.SimpleNamespace(modules=mods, x_t=x, dy_t=dy)
+
+
+def time_window_moves(hip, N, plan, x, stream, cfg, reps=20):
+    """Stand-alone window gather (shift + partition) and scatter (reverse + un-shift) of the
+    SW-MSA module, outside the timed step, against a device-to-device copy of the same bytes.
+    The gather is also the known-size copy that calibrates the HBM byte counters."""
+    import torch
+    xw = torch.empty_like(x)
+    y = torch.empty_like(x)
+    ev = hip.events(2 * reps + 2)
+    N.swin_window_gather(plan, x, xw, stream=stream)
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn in (("gather", lambda: N.swin_window_gather(plan, x, xw, stream=stream)),
+                     ("scatter", lambda: N.swin_window_scatter(plan, xw, y, stream=stream)),
+                     ("device_copy", lambda: y.copy_(xw))):
+        for i in range(reps):
+            assert hip.l.hipEventRecord(ev[2 * i], stream.cuda_stream) == 0
+            fn()
+            assert hip.l.hipEventRecord(ev[2 * i + 1], stream.cuda_stream) == 0
+        torch.cuda.synchronize()
+        ms = sorted(hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(reps))[reps // 2]
+        moved = 2 * x.numel() * x.element_size()   # read + write of the activation
+        res[name] = {"median_ms": round(ms, 4), "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    hip.destroy(ev)
+    for name in ("gather", "scatter"):
+        res[name]["frac_of_device_copy"] = round(res[name]["gbs"] / res["device_copy"]["gbs"], 3)
+    res["bytes_moved"] = 2 * x.numel() * x.element_size()
+    return res
 
 
 def main():
@@ -321,6 +352,8 @@ def main():
     roof["algorithmic_per_launch"] = per_launch_ref
     roof["traffic"] = traffic_for(dom, per_launch_ref)
 
+    moves = time_window_moves(hip, N, mods[1].plan.handle, x, stream, cfg)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: oracle CPU baseline (~%.0f s)" % args.cpu_seconds)
@@ -338,7 +371,7 @@ def main():
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "algorithmic_gflop_per_step": round(flops_step / 1e9, 2),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "roofline": roof, "kernels": kernels, "cpu_baseline": cpu,
+        "roofline": roof, "kernels": kernels, "window_moves": moves, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

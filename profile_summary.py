@@ -1,0 +1,180 @@
+"""Short text summaries of rocprofv3 runs of bench.py, for profiles/.
+
+  python profile_summary.py trace DIR OUT.md --cmd "<rocprofv3 command>"
+      per-kernel table from the --kernel-trace --stats CSV (kernel_stats.csv) under DIR
+  python profile_summary.py traffic FETCH_DIR WRITE_DIR --cmd-fetch "..." --cmd-write "..."
+      HBM bytes per dispatch from two --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per
+      dispatch), each scaled by what the same counter reads for the window gather, a copy of
+      known size (n_tok x C bf16 rows plus the int32 permutation in, the rows out). Writes
+      profiles/traffic.json (read by bench.py for its roofline "traffic" field) and
+      profiles/traffic_540x1080_c512.md.
+
+Kernels launched more than once per step with different shapes (the two GEMM kernels) are
+told apart by their position in the step's fixed launch order.
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# launch order of the two GEMM kernels within one bench step (W fwd, SW fwd, SW bwd, W bwd)
+NT_ROLES = ["qkv_gemm", "proj_gemm", "qkv_gemm", "proj_gemm", "dproj_gemm", "dgrad_qkv", "dproj_gemm", "dgrad_qkv"]
+TN_ROLES = ["wgrad_proj", "wgrad_qkv", "wgrad_proj", "wgrad_qkv"]
+SINGLE = {"k_attn_fwd": "attn_fwd", "k_attn_bwd": "attn_bwd"}
+SOURCES = {"k_gemm_nt": "gemm.hip", "k_gemm_tn": "gemm.hip", "k_attn_fwd": "attn_fwd.hip",
+           "k_attn_bwd": "attn_bwd.hip"}
+COPY = "k_window_move<true>"
+
+
+def short(name):
+    n = name.split("(")[0].replace("void ", "").replace("swin::", "")
+    return n.strip()
+
+
+def base(name):
+    return short(name).split("<")[0]
+
+
+def find(dirname, suffix):
+    hits = sorted(glob.glob(os.path.join(dirname, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit("no *%s under %s" % (suffix, dirname))
+    return hits[0]
+
+
+def source_sha(fname):
+    with open(os.path.join(ROOT, "shifted_window_attention_amd", "csrc", fname), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def cmd_trace(a):
+    path = find(a.dir, "kernel_stats.csv")
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# Kernel time: %s" % a.title, "", "Command (from the repository root on the GPU host):", "",
+             "    " + a.cmd, "", "rocprofv3 kernel_stats, all dispatches of the run (warmup, timed steps and the",
+             "stand-alone gather/scatter timing):", "",
+             "| kernel | calls | avg us | min us | max us | total ms | % |", "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| %s | %s | %.1f | %.1f | %.1f | %.2f | %.1f |" % (
+            short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    if a.bench_json and os.path.exists(a.bench_json):
+        txt = open(a.bench_json).read().strip().splitlines()
+        if txt:
+            b = json.loads(txt[-1])
+            lines += ["", "bench.py line of the same run: %.3f ms/step, %.1f TFLOP/s (%.1f%% of bf16 MFMA peak)" % (
+                b["ms_per_step"], b["tflops"], 100 * b["mfma_peak_frac"]), "",
+                "| stage | avg ms per launch (HIP events) |", "|---|---|"]
+            for k, v in b["kernels"].items():
+                lines.append("| %s | %.4f |" % (k, v["avg_ms"]))
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("wrote", a.out)
+
+
+def per_dispatch(path, counter):
+    """{(kernel short name, role): [values]} in dispatch order."""
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    out = defaultdict(list)
+    seq = defaultdict(int)
+    for r in rows:
+        name = short(r["Kernel_Name"])
+        b = base(r["Kernel_Name"])
+        v = float(r["Counter_Value"])
+        if b == "k_gemm_nt":
+            role = NT_ROLES[seq[b] % len(NT_ROLES)]
+        elif b == "k_gemm_tn":
+            role = TN_ROLES[seq[b] % len(TN_ROLES)]
+        elif b in SINGLE:
+            role = SINGLE[b]
+        elif name == COPY:
+            role = "copy"
+        else:
+            role = None
+        seq[b] += 1
+        if role:
+            out[(name, role)].append(v)
+    return out
+
+
+def cmd_traffic(a):
+    from bench import stage_flops_bytes
+    from workloads import get_config
+    cfg = get_config("highres")
+    n, C = cfg.n_tokens, cfg.channels
+    fetch = per_dispatch(find(a.fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    write = per_dispatch(find(a.write_dir, "counter_collection.csv"), "WRITE_SIZE")
+    mean = lambda v: sum(v) / len(v)
+    cf = [v for (k, r), v in fetch.items() if r == "copy"]
+    cw = [v for (k, r), v in write.items() if r == "copy"]
+    if not cf or not cw:
+        raise SystemExit("no %s dispatches in the counter runs" % COPY)
+    copy_read, copy_write = n * C * 2 + n * 4, n * C * 2
+    f_read = mean(cf[0]) * 1024 / copy_read
+    f_write = mean(cw[0]) * 1024 / copy_write
+    # algorithmic bytes of the SW-MSA module (both modules move the same bytes)
+    _, alg = stage_flops_bytes(cfg, 0)
+    out = {"_calibration": {"copy_kernel": COPY, "copy_read_bytes": copy_read, "copy_write_bytes": copy_write,
+                            "fetch_kib": round(mean(cf[0]), 1), "write_kib": round(mean(cw[0]), 1),
+                            "fetch_factor": round(f_read, 4), "write_factor": round(f_write, 4)},
+           "_commands": {"fetch": a.cmd_fetch, "write": a.cmd_write}}
+    lines = ["# HBM traffic per dispatch: 540x1080 tokens, C=512, 16 heads, 12x12 windows", "",
+             "Counter runs (from the repository root on the GPU host):", "", "    " + a.cmd_fetch,
+             "    " + a.cmd_write, "",
+             "Calibration: the window gather (%s) moves a known %d bytes in (rows + int32 permutation) and %d out." %
+             (COPY, copy_read, copy_write),
+             "FETCH_SIZE reads %.1f KiB for it (factor %.4f), WRITE_SIZE %.1f KiB (factor %.4f); each kernel's counter" %
+             (mean(cf[0]), f_read, mean(cw[0]), f_write),
+             "is divided by its factor.", "",
+             "| stage | kernel | dispatches | FETCH KiB | WRITE KiB | HBM bytes (calibrated) | algorithmic bytes | ratio |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (kname, role), fv in sorted(fetch.items(), key=lambda t: t[0][1]):
+        if role == "copy":
+            continue
+        wv = write.get((kname, role))
+        if not wv:
+            continue
+        fb = mean(fv) * 1024 / f_read
+        wb = mean(wv) * 1024 / f_write
+        total = fb + wb
+        ab = alg.get(role, 0)
+        out[role] = {"kernel": kname, "source_sha": source_sha(SOURCES[base(kname)]), "dispatches": len(fv),
+                     "fetch_kib": round(mean(fv), 1), "write_kib": round(mean(wv), 1),
+                     "read_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(total),
+                     "algorithmic_bytes_per_launch": ab}
+        lines.append("| %s | %s | %d | %.0f | %.0f | %.3e | %.3e | %.2f |" % (
+            role, kname, len(fv), mean(fv), mean(wv), total, ab, total / ab if ab else float("nan")))
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    json.dump(out, open(os.path.join(ROOT, "profiles", "traffic.json"), "w"), indent=1)
+    open(os.path.join(ROOT, "profiles", "traffic_540x1080_c512.md"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    t.add_argument("out")
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--title", default="bench.py, 540x1080 tokens, C=512, W-MSA -> SW-MSA fwd+bwd")
+    t.add_argument("--bench-json", default=None)
+    f = sub.add_parser("traffic")
+    f.add_argument("fetch_dir")
+    f.add_argument("write_dir")
+    f.add_argument("--cmd-fetch", required=True)
+    f.add_argument("--cmd-write", required=True)
+    a = ap.parse_args()
+    (cmd_trace if a.what == "trace" else cmd_traffic)(a)
+
+
+if __name__ == "__main__":
+    main()
