@@ -64,7 +64,10 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
   constexpr int NKC = (NKT + 1) / 2;
   constexpr int NT = 64 * NKT;
   constexpr int ROWS = BwdBuf<NKT>::ROWS;
-  constexpr int SP = ROWS + 4;                        // dS row pitch (bf16)
+  // dS is kept transposed, dSt[key][query], so a lane's 4 consecutive queries of one key
+  // are one 8-byte store; the pitch (an odd multiple of 8 bytes past a 16-byte multiple)
+  // puts the 16 keys x 2 query groups of a half-wave store on distinct banks
+  constexpr int SPT = 16 * NKT + 8;
   constexpr int SLAB = ((int)sizeof(BwdBuf<NKT>) / (NKT * 16 * 4)) / 16 * 16;  // rows per pass in bufA
   static_assert(SLAB >= 16, "LDS too small for the bias-gradient slab");
   static_assert(BwdBuf<NKT>::FROWS % 64 == 0 && BwdBuf<NKT>::FROWS >= ROWS, "float rows are whole copies");
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
   // the per-bin partial sums.
   __shared__ __attribute__((aligned(1024))) BwdBuf<NKT> bufA;
   __shared__ __attribute__((aligned(1024))) BwdBuf<NKT> bufB;
-  __shared__ __attribute__((aligned(16))) bf16 dSs[16 * NKT * SP];
+  __shared__ __attribute__((aligned(16))) bf16 dSt[ROWS * SPT];
   __shared__ int offs[kMaxChunk];
   __shared__ int codes[16 * NKT];  // per-token local-offset codes and wrap labels
   extern __shared__ float dyn_lds[];   // [2 nbins]: bias-gradient bins, then the scaled table
@@ -112,10 +115,9 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
     stage_floats(make_rsrc(Dh + off, (uint32_t)n * 4), b.dd, BwdBuf<NKT>::FROWS, kt, NKT, lane);
     stage_floats(make_rsrc(a.perm + off, (uint32_t)n * 4), (float*)b.grow, BwdBuf<NKT>::FROWS, kt, NKT, lane);
   };
-  // key columns of dS that no wave owns (odd tile count) are read by dQ: keep them zero
+  // key rows of dS that no wave owns (odd tile count) are read by dQ: keep them zero
   if constexpr (ROWS > 16 * NKT) {
-    constexpr int EXTRA = ROWS - 16 * NKT;
-    for (int c = tid; c < 16 * NKT * EXTRA; c += NT) dSs[(c / EXTRA) * SP + 16 * NKT + c % EXTRA] = to_bf16(0.f);
+    for (int c = tid; c < (ROWS - 16 * NKT) * SPT; c += NT) dSt[16 * NKT * SPT + c] = to_bf16(0.f);
   }
   for (int i = tid; i < a.nbins; i += NT) {
     bins_lds[i] = 0.f;
@@ -194,8 +196,8 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
             dbacc[qt][i] += ds;
             pb[4 * u + i] = to_bf16(p);
             sb[4 * u + i] = to_bf16(ds);
-            dSs[(16 * qt + 4 * g + i) * SP + key] = sb[4 * u + i];
           }
+          *(bf16x4*)(dSt + key * SPT + 16 * qt + 4 * g) = bf16x4{sb[4 * u], sb[4 * u + 1], sb[4 * u + 2], sb[4 * u + 3]};
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -221,16 +223,18 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
         *(bf16x4*)(row + 2 * C + 16 * dt + 4 * g) = v4;
       }
     }
-    // dQ^T for query tile kt: K^T (transposed read of K) times dS^T (rows of dS)
+    // dQ^T for query tile kt: K^T (transposed read of K) times dS^T, whose columns (8 keys
+    // at one query) come from dSt through the transposing LDS read
     {
-      const int q = 16 * kt + li;
+      // lane j of each 16-lane group addresses key row 4g + j/4, queries 16 kt + 4 (j%4) ..
+      const bf16* dq_src = dSt + (4 * g + (li >> 2)) * SPT + 16 * kt + 4 * (li & 3);
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         f32x4 dq = f32x4{};
 #pragma unroll
         for (int c = 0; c < NKC; ++c) {
-          const bf16x4 lo = *(const bf16x4*)(dSs + q * SP + 32 * c + 4 * g);
-          const bf16x4 hi = *(const bf16x4*)(dSs + q * SP + 32 * c + 16 + 4 * g);
+          const bf16x4 lo = lds_read_tr(dq_src + 32 * c * SPT);
+          const bf16x4 hi = lds_read_tr(dq_src + (32 * c + 16) * SPT);
           const bf16x8 sq = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           dq = mfma16(tile_frag_tr(cur.k, 32 * c, 16 * dt, g, li), sq, dq);
         }

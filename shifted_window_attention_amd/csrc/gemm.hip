@@ -2,16 +2,17 @@
 //
 //   k_gemm_nt:   C[m, n] = sum_k A[m, k] * B[n, k]   (both operands K-contiguous)
 //                A rows may be gathered through a row map (the cyclic shift + window
-//                partition fused into the operand load), and the epilogue either
-//                writes head-split q/k/v planes or scatters rows back to the grid
-//                (window reverse + un-shift fused into the store).
+//                partition fused into the operand load), and the epilogue writes
+//                head-split q/k/v planes or plain rows (optionally through a row map)
+//                and can also form per-head row dot products with a second matrix.
 //   k_gemm_tn:   P[s, m, n] = sum_{t in chunk s} A[t, m] * B[t, n]   (contraction over
 //                tokens for the weight gradients; deterministic split-K partials)
-//   k_reduce_splits: fixed-order sum of the split-K partials.
+//   k_reduce_splits: fixed-order sum of the split-K partials (weights and biases).
 //
-// Tiling for gfx950: 256 threads (4 waves of 64), v_mfma_f32_32x32x16_bf16, 64-deep
-// K steps staged through LDS with 16-byte rows padded by 16 bytes so that both the
-// row-wise 16-byte stores and the MFMA fragment reads are bank-conflict free.
+// Both GEMMs run on v_mfma_f32_32x32x16_bf16. k_gemm_nt: 256 threads (4 waves of 64),
+// 64-deep K steps staged through LDS via registers, rows padded by 16 bytes so that both
+// the row-wise 16-byte stores and the MFMA fragment reads are bank-conflict free.
+// k_gemm_tn: operand tiles copied straight into swizzled LDS tiles, double-buffered.
 #include "device_common.h"
 #include "swin_internal.h"
 
@@ -353,7 +354,8 @@ __global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ 
     }
   }
 
-  // partial tile, transposed: P[s][n][m]; lane holds 4 consecutive m per 32x32 tile row group
+  // partial tile as P[s][m/4][n][m%4]: a lane's 4 consecutive rows m of one column n are one
+  // 16-byte store, and the split reduction reads them back as one 16-byte load (M % 4 == 0)
   float* P = part + (int64_t)s * M * N;
   const int fr = lane & 31;
 #pragma unroll
@@ -364,12 +366,9 @@ __global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ 
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int m = m0 + wm * tn::WTM + 32 * i + 8 * q + 4 * (lane >> 5);
-        if (n < N && m + 3 < M) {
+        if (n < N && m < M) {
           const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          *(f32x4*)(P + (int64_t)n * M + m) = v;
-        } else if (n < N) {
-          for (int e = 0; e < 4; ++e)
-            if (m + e < M) P[(int64_t)n * M + m + e] = acc[i][j][4 * q + e];
+          *(f32x4*)(P + ((int64_t)(m >> 2) * N + n) * 4) = v;
         }
       }
     }
@@ -385,34 +384,36 @@ __global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ 
   }
 }
 
-// out[i] = sum_{s < S} part[s * stride + i], in order of s.
-__global__ void k_reduce_splits(const float* __restrict__ part, int S, int64_t stride, int64_t n,
-                                float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  float acc = 0.f;
-  for (int s = 0; s < S; ++s) acc += part[(int64_t)s * stride + i];
-  out[i] = acc;
-}
-
-// out[m][n] = sum_{s < S} part[s][n][m] (transposed split partials), in order of s; a 32 x 32
-// tile per block through LDS so reads and writes are both row-contiguous.
-__global__ __launch_bounds__(256) void k_reduce_splits_t(const float* __restrict__ part, int S, int M, int N,
-                                                         float* __restrict__ out) {
-  __shared__ float tile[32][33];
-  const int m0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int k = ty; k < 32; k += 8) {
-    const int n = n0 + k, m = m0 + tx;
-    float acc = 0.f;
-    if (n < N && m < M)
-      for (int s = 0; s < S; ++s) acc += part[((int64_t)s * N + n) * M + m];
-    tile[k][tx] = acc;
-  }
-  __syncthreads();
-  for (int k = ty; k < 32; k += 8) {
-    const int m = m0 + k, n = n0 + tx;
-    if (m < M && n < N) out[(int64_t)m * N + n] = tile[tx][k];
+// Split-K reduction of the weight gradients, in order of s:
+//   dw[m][n] = sum_s P[s][m/4][n][m%4]   (threads 0 .. M N / 4 - 1: 4 rows of one column)
+//   db[m]    = sum_s dbpart[s][m]        (the next M / 4 threads: 4 consecutive entries)
+__global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__ part, int S, int M, int N,
+                                                       float* __restrict__ dw, const float* __restrict__ dbpart,
+                                                       float* __restrict__ db) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n_w = (int64_t)M * N / 4;
+  if (t < n_w) {
+    const int64_t mq = t / N;
+    const int n = (int)(t - mq * N);
+    const f32x4* src = (const f32x4*)part + t;
+    const int64_t stride = n_w;  // one split, in f32x4
+    f32x4 acc = src[0];
+    for (int k = 1; k < S; ++k) acc += src[k * stride];
+    float* o = dw + (4 * mq) * N + n;
+    o[0] = acc[0];
+    o[N] = acc[1];
+    o[2 * N] = acc[2];
+    o[3 * N] = acc[3];
+  } else if (db && t < n_w + M / 4) {
+    const int64_t i = t - n_w;
+    const f32x4* src = (const f32x4*)dbpart + i;
+    f32x4 acc = src[0];
+    for (int k = 1; k < S; ++k) acc += src[k * (M / 4)];
+    float* o = db + 4 * i;  // the caller's pointer: no alignment beyond 4 bytes assumed
+    o[0] = acc[0];
+    o[1] = acc[1];
+    o[2] = acc[2];
+    o[3] = acc[3];
   }
 }
 
@@ -505,11 +506,8 @@ hipError_t launch_wgrad_bf16(const bf16* A, int64_t lda, const bf16* B, int64_t 
   k_gemm_tn<<<xcd_grid(tiles), tn::NT, 0, s>>>(A, lda, B, ldb, T, M, N, chunk, splits, part, dbpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_reduce_splits_t<<<dim3((unsigned)((M + 31) / 32), (unsigned)((N + 31) / 32)), 256, 0, s>>>(part, splits, M, N,
-                                                                                               dw);
-  e = hipGetLastError();
-  if (e != hipSuccess || !db) return e;
-  k_reduce_splits<<<(unsigned)((M + 255) / 256), 256, 0, s>>>(dbpart, splits, M, M, db);
+  const int64_t threads = (int64_t)M * N / 4 + (db ? M / 4 : 0);
+  k_reduce_splits<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(part, splits, M, N, dw, dbpart, db);
   return hipGetLastError();
 }
 
