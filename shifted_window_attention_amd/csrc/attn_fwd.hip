@@ -10,9 +10,10 @@
 // per 16-query tile. Every window of a class has the same extent and label split, so a
 // lane's bias + mask values (its query against every key) are computed once per
 // workgroup and then serve as the initial accumulator of the Q K^T MFMA for every window
-// of the chunk. A window's Q, K and V (n x 32 bf16 each) are staged in LDS by direct
-// global->LDS copies into one of two buffers, so the copies for window w+1 run while
-// window w is computed (one barrier per window).
+// of the chunk. A window's Q, K and V (n x 32 bf16 each) and grid rows are staged in LDS
+// by direct global->LDS copies into one of two or three buffers (as many as LDS allows with
+// two workgroups per CU), one or two windows ahead of the one being computed, with one
+// barrier per window.
 //
 // The logits are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16), so a lane
 // holds one query and 4 consecutive keys of every 16-key tile. The row max is an
@@ -44,25 +45,38 @@ struct AttnArgs {
 
 template <int NKT>
 struct FwdBuf {
-  static constexpr int ROWS = (NKT + 1) / 2 * 32;      // staged rows per tile (32-key chunks)
-  static constexpr int FROWS = (ROWS + 63) / 64 * 64;  // word rows: whole 64-lane copies
-  unsigned char q[ROWS * 64], k[ROWS * 64], v[ROWS * 64];
-  int grow[FROWS];  // grid row of each token of the window
+  static constexpr int ROWS = (NKT + 1) / 2 * 32;  // key/value rows (32-key chunks of the PV product)
+  unsigned char k[ROWS * 64], v[ROWS * 64];
+  unsigned char q[16 * NKT * 64];                  // wave qt's 16 query rows at 1024 qt
+  int grow[NKT * 64];                              // wave qt's query grid rows at 64 qt
+};
+
+// All of the kernel's LDS is one object: the compiler then leaves the ordering of the
+// direct-to-LDS copies against LDS reads to the explicit waits below.
+template <int NKT>
+struct FwdSmem {
+  static constexpr int B = sizeof(FwdBuf<NKT>), T = 4 * (kMaxBins + kMaxChunk + 16 * NKT);
+  // two workgroups per CU when the register budget allows it (up to 10 query tiles), with as
+  // many buffers as then fit; otherwise three buffers if one workgroup fits them
+  static constexpr int MIN_BLOCKS = NKT <= 10 ? 2 : 1;
+  static constexpr int LDS_CAP = 160 * 1024 / MIN_BLOCKS;
+  static constexpr int NBUF = 3 * B + T <= LDS_CAP ? 3 : (2 * B + T <= LDS_CAP ? 2 : (3 * B + T <= 160 * 1024 ? 3 : 2));
+  FwdBuf<NKT> buf[NBUF];
+  float tab[kMaxBins];  // the head's bias table times log2(e)
+  int offs[kMaxChunk];
+  int codes[16 * NKT];  // per-token local-offset codes and wrap labels
 };
 
 template <int NKT>
-__global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
+__global__ __launch_bounds__(64 * NKT, FwdSmem<NKT>::MIN_BLOCKS) void k_attn_fwd(AttnArgs a) {
   constexpr int NKC = (NKT + 1) / 2;   // 32-key chunks of the PV product
   constexpr int ROWS = FwdBuf<NKT>::ROWS;
-  // Two buffers, filled by direct global->LDS copies: window w is computed from one while
-  // window w+1 is copied into the other. They are separate objects (and the window loop is
-  // unrolled by two) so the compiler can tell the copies never touch the buffer being read
-  // and leaves them in flight until the end-of-window barrier.
-  __shared__ __attribute__((aligned(1024))) FwdBuf<NKT> bufA;
-  __shared__ __attribute__((aligned(1024))) FwdBuf<NKT> bufB;
-  __shared__ int offs[kMaxChunk];
-  __shared__ int codes[16 * NKT];     // per-token local-offset codes and wrap labels
-  extern __shared__ float tab_lds[];  // [nbins]: the head's bias table times log2(e)
+  constexpr int NBUF = FwdSmem<NKT>::NBUF;
+  // NBUF buffers, filled by direct global->LDS copies NBUF-1 windows ahead of the one being
+  // computed. A wave waits only for its own copies into the buffer it is about to read (an
+  // explicit vector-memory count), then meets the other waves at a barrier that leaves that
+  // count alone.
+  __shared__ __attribute__((aligned(1024))) FwdSmem<NKT> sm;
 
   const int lane = threadIdx.x & 63;
   const int qt = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -74,67 +88,102 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
   const int q = qt * 16 + li;
   const bool qv = q < n;
   const float* tab = a.table + (int64_t)h * a.nbins;
-  for (int i = threadIdx.x; i < a.nbins; i += 64 * NKT) tab_lds[i] = tab[i] * kLog2e;
-  if (threadIdx.x < wk.count) offs[threadIdx.x] = a.win_off[a.class_win[wk.first + threadIdx.x]];
-  if (threadIdx.x < 16 * NKT) codes[threadIdx.x] = threadIdx.x < n ? token_code(threadIdx.x, ci.ext, ci.split, a.win) : 0;
-  const int64_t off0 = a.win_off[a.class_win[wk.first]];
+  for (int i = threadIdx.x; i < a.nbins; i += 64 * NKT) sm.tab[i] = tab[i] * kLog2e;
+  if (threadIdx.x < wk.count) sm.offs[threadIdx.x] = a.win_off[a.class_win[wk.first + threadIdx.x]];
+  if (threadIdx.x < 16 * NKT)
+    sm.codes[threadIdx.x] = threadIdx.x < n ? token_code(threadIdx.x, ci.ext, ci.split, a.win) : 0;
+  // V rows past the copied 16 NKT (odd tile count) feed the last PV chunk: keep them zero
+  if constexpr (ROWS > 16 * NKT) {
+    constexpr int TAIL = (ROWS - 16 * NKT) * 64 / 4;
+    for (int i = threadIdx.x; i < TAIL * NBUF; i += 64 * NKT)
+      ((int*)(sm.buf[i / TAIL].v + 16 * NKT * 64))[i % TAIL] = 0;
+  }
+  __syncthreads();  // table, offsets, codes and zero rows in LDS
 
   const bf16* Qh = a.qkv + ((int64_t)(0 * a.nh + h) * a.n_tok) * 32;
   const bf16* Kh = a.qkv + ((int64_t)(1 * a.nh + h) * a.n_tok) * 32;
   const bf16* Vh = a.qkv + ((int64_t)(2 * a.nh + h) * a.n_tok) * 32;
-  // rows past n arrive as zeros (buffer range = the window's n rows)
-  auto stage = [&](int64_t off, FwdBuf<NKT>& b) {
-    const uint32_t bytes = (uint32_t)n * 64;
-    stage_rows(make_rsrc(Qh + off * 32, bytes), b.q, ROWS, qt, NKT, lane);
-    stage_rows(make_rsrc(Kh + off * 32, bytes), b.k, ROWS, qt, NKT, lane);
-    stage_rows(make_rsrc(Vh + off * 32, bytes), b.v, ROWS, qt, NKT, lane);
-    stage_floats(make_rsrc(a.perm + off, (uint32_t)n * 4), (float*)b.grow, FwdBuf<NKT>::FROWS, qt, NKT, lane);
+  // Copies of rows past n read row n-1 instead: those keys are masked (-inf logits, zero
+  // probabilities) and those queries' outputs are dropped, so any finite values will do.
+  // Each wave issues exactly four copies per window: the 16-row slabs qt of K, V and Q and
+  // the grid rows of its 16 queries (lanes 16..63 repeat them).
+  constexpr int COPIES = 4;
+  const int crow = 16 * qt + (lane >> 2);
+  const int cchunk = (lane & 3) ^ swz(crow);
+  const int crow_src = crow < n ? crow : n - 1;
+  const int grow_src = 16 * qt + li < n ? 16 * qt + li : n - 1;
+  auto stage = [&](int w) {
+    FwdBuf<NKT>& b = sm.buf[w % NBUF];
+    const int64_t off = sm.offs[w];
+    const int64_t src = (off + crow_src) * 32 + 8 * cchunk;
+    lds_copy16(Kh + src, b.k + 1024 * qt);
+    lds_copy16(Vh + src, b.v + 1024 * qt);
+    lds_copy16(Qh + src, b.q + 1024 * qt);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.perm + off + grow_src),
+                                     (__attribute__((address_space(3))) void*)(b.grow + 64 * qt), 4, 0, 0);
   };
-  stage(off0, bufA);
-  __syncthreads();  // table and offsets in LDS
+  for (int w = 0; w < NBUF - 1 && w < wk.count; ++w) stage(w);
 
   // bias + mask of this lane's query against every key; keys past n are masked, and
-  // queries past n (whose outputs are dropped) get finite zeros
+  // queries past n (whose outputs are dropped) get finite zeros. Held as fp16 (|error| <=
+  // 2^-11 |bias|, -inf exact) to leave registers for a second workgroup per CU.
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
   const int code0 = code0_of(a.win);
-  const int cq = codes[q];
-  f32x4 bias[NKT];
+  const int cq = sm.codes[q];
+  h4 bias[NKT];
 #pragma unroll
   for (int kt = 0; kt < NKT; ++kt) {
-    const int4 ck = *(const int4*)(codes + 16 * kt + 4 * g);
+    const int4 ck = *(const int4*)(sm.codes + 16 * kt + 4 * g);
     const int kk[4] = {ck.x, ck.y, ck.z, ck.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = 16 * kt + 4 * g + i;
-      bias[kt][i] = !qv ? 0.f : (k >= n ? -INFINITY : pair_bias_codes(cq, kk[i], code0, tab_lds));
+      bias[kt][i] = (_Float16)(!qv ? 0.f : (k >= n ? -INFINITY : pair_bias_codes(cq, kk[i], code0, sm.tab)));
     }
   }
-  __syncthreads();
 
-  // a window's results are stored at the start of the next iteration, after the next
-  // copies are issued, so the end-of-window barrier does not wait for them
+  // a window's results are stored in the next window, before that window's copies are issued
   bf16x4 ov[2] = {};
   float lse_v = 0.f;
   int64_t prev_off = -1;
   int prev_row = 0;  // grid row of this lane's query in the previous window
-  auto flush = [&]() {
+  // fragment offsets inside a tile: row 16 t + li of slab t, and the transposed V^T reads
+  // (rows 32 c + 4 g + li/4 and +16, columns 4 (li % 4) and +16) are these lane offsets plus
+  // constants, because rows that differ by a multiple of 16 have the same swizzle
+  const int kq_off = li * 64 + 16 * (g ^ swz(li));
+  const int vr = 4 * g + (li >> 2);
+  const int vt_off0 = swz_off(vr, 4 * (li & 3)), vt_off1 = swz_off(vr, 16 + 4 * (li & 3));
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = to_bf16(1.f);
+  for (int w = 0; w < wk.count; ++w) {
+    const FwdBuf<NKT>& cur = sm.buf[w % NBUF];
+    // Issue order: the first NBUF-1 windows' copies, then per window w: the stores of window
+    // w-1, then the copies of window w+NBUF-1. Operations complete in issue order, so the
+    // copies of window w are done once at most the copies issued after them (those of
+    // windows w+1 .. w+NBUF-2) are outstanding.
+    if (NBUF == 3 && w + 1 < wk.count)
+      vm_wait(COPIES);
+    else
+      vm_wait(0);
+    // every wave's copies into `cur` have landed, and every wave is done with window w-1
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (prev_off >= 0 && qv) {
       bf16* orow = a.o + (int64_t)prev_row * a.C + h * 32;
       *(bf16x4*)(orow + 4 * g) = ov[0];
       *(bf16x4*)(orow + 16 + 4 * g) = ov[1];
       if (g == 0) a.lse[(int64_t)h * a.n_tok + prev_off + q] = lse_v;
     }
-  };
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = to_bf16(1.f);
-  auto window = [&](int w, const FwdBuf<NKT>& cur, FwdBuf<NKT>& nxt) {
-    const int64_t off = offs[w];
-    if (w + 1 < wk.count) stage(offs[w + 1], nxt);  // overlaps with this window's compute
-    flush();
-    const bf16x8 bq = tile_frag(cur.q, q, g);
+    if (w + NBUF - 1 < wk.count) stage(w + NBUF - 1);  // into the buffer window w-1 used
+    const bf16x8 bq = *(const bf16x8*)(cur.q + kq_off + 1024 * qt);
     f32x4 s[NKT];
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) s[kt] = mfma16(tile_frag(cur.k, 16 * kt + li, g), bq, bias[kt]);
+    for (int kt = 0; kt < NKT; ++kt) asm volatile("" : "+v"(bias[kt]));  // expand per window, not hoisted
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      const f32x4 b4 = {(float)bias[kt][0], (float)bias[kt][1], (float)bias[kt][2], (float)bias[kt][3]};
+      s[kt] = mfma16(*(const bf16x8*)(cur.k + kq_off + 1024 * kt), bq, b4);
+    }
     float m = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
@@ -158,31 +207,33 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_fwd(AttnArgs a) {
         pb[i] = to_bf16(s[2 * c][i]);
         pb[4 + i] = (2 * c + 1 < NKT) ? to_bf16(s[2 * c + 1][i]) : to_bf16(0.f);
       }
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) oacc[dt] = mfma16(tile_frag_tr(cur.v, 32 * c, 16 * dt, g, li), pb, oacc[dt]);
+      bf16x8 v0, v1;
+      tile_frag_tr2_at(cur.v + 2048 * c, vt_off0, vt_off1, v0, v1);
+      oacc[0] = mfma16(v0, pb, oacc[0]);
+      oacc[1] = mfma16(v1, pb, oacc[1]);
       lacc = mfma16(ones, pb, lacc);
     }
     const float l = lacc[0];
-    const float inv = 1.f / l;
+    const float inv = __builtin_amdgcn_rcpf(l);
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) ov[dt][i] = to_bf16(oacc[dt][i] * inv);
     lse_v = m + fast_log2(l);
-    prev_off = off;
-    prev_row = cur.grow[q];
-    __syncthreads();  // window w+1 staged; this buffer is free
-  };
-  for (int w = 0; w < wk.count; w += 2) {
-    window(w, bufA, bufB);
-    if (w + 1 < wk.count) window(w + 1, bufB, bufA);
+    prev_off = sm.offs[w];
+    prev_row = cur.grow[64 * qt + li];
   }
-  flush();
+  if (prev_off >= 0 && qv) {
+    bf16* orow = a.o + (int64_t)prev_row * a.C + h * 32;
+    *(bf16x4*)(orow + 4 * g) = ov[0];
+    *(bf16x4*)(orow + 16 + 4 * g) = ov[1];
+    if (g == 0) a.lse[(int64_t)h * a.n_tok + prev_off + q] = lse_v;
+  }
 }
 
 template <int NKT>
 static void launch_one(const AttnArgs& a, int n_items, int nh, hipStream_t s) {
-  k_attn_fwd<NKT><<<dim3((unsigned)n_items, (unsigned)nh), 64 * NKT, (size_t)a.nbins * sizeof(float), s>>>(a);
+  k_attn_fwd<NKT><<<dim3((unsigned)n_items, (unsigned)nh), 64 * NKT, 0, s>>>(a);
 }
 
 typedef void (*fwd_launcher)(const AttnArgs&, int, int, hipStream_t);

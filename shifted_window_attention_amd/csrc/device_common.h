@@ -102,6 +102,38 @@ __device__ __forceinline__ bf16x8 tile_frag_tr(const unsigned char* tile, int ro
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// LDS byte address of a pointer into a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// The two V^T-style MFMA operands of a swizzled tile (see tile_frag_tr) for columns
+// col0 + li and col0 + 16 + li, from the lane offsets off0 = swz_off(r, col) and
+// off1 = swz_off(r, col + 16) of its row r = row0 + 4 g + li/4 (rows r and r + 16 share a
+// swizzle, so the second read of each pair is 1 KB further). The four transposing reads are
+// inline assembly ended by their own LDS wait, so the compiler adds no vector-memory wait in
+// front of them: kernels that keep direct-to-LDS copies to other buffers in flight across
+// these reads order those copies themselves.
+__device__ __forceinline__ void tile_frag_tr2_at(const unsigned char* tile, int off0, int off1, bf16x8& f0,
+                                                 bf16x8& f1) {
+  const uint32_t base = lds_addr(tile);
+  const uint32_t a0 = base + off0, a2 = base + off1;
+  u32x2 v0, v1, v2, v3;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %2, %5\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+      : "v"(a0), "v"(a2)
+      : "memory");
+  const bf16x4 lo0 = __builtin_bit_cast(bf16x4, v0), hi0 = __builtin_bit_cast(bf16x4, v1);
+  const bf16x4 lo1 = __builtin_bit_cast(bf16x4, v2), hi1 = __builtin_bit_cast(bf16x4, v3);
+  f0 = bf16x8{lo0[0], lo0[1], lo0[2], lo0[3], hi0[0], hi0[1], hi0[2], hi0[3]};
+  f1 = bf16x8{lo1[0], lo1[1], lo1[2], lo1[3], hi1[0], hi1[1], hi1[2], hi1[3]};
+}
+
 // Buffer resource over `bytes` bytes at `base` (raw buffer, 32-bit elements format as the
 // CDNA buffer descriptor expects). Loads past `bytes` return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -129,6 +161,36 @@ __device__ __forceinline__ void stage_floats(__amdgpu_buffer_rsrc_t src, float* 
   for (int j = w; j < rows / 64; j += nw)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(dst + 64 * j), 4,
                                              4 * (64 * j + lane), 0, 0, 0);
+}
+
+// Asynchronous 16-byte-per-lane copy from global memory (a 64-bit address per lane) into
+// LDS: lane l writes bytes [16 l, 16 l + 16) of the 1 KB at lds_base (wave-uniform).
+__device__ __forceinline__ void lds_copy16(const void* src, unsigned char* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n <= 15: wait until at most n vector-memory
+// operations of this wave are outstanding (they complete in issue order).
+__device__ __forceinline__ void vm_wait(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+    case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+  }
 }
 
 }  // namespace swin

@@ -72,6 +72,8 @@ static swin_status check_kernel_support(const swin_attn_desc* d, int64_t max_tok
   const int hd = d->channels / d->heads;
   if (max_tokens > 16 * kMaxFwdTiles)
     return fail(SWIN_ERR_UNSUPPORTED, "windows of more than 256 tokens are not supported");
+  const int64_t nbins = int64_t(2 * d->window[0] - 1) * (2 * d->window[1] - 1) * (2 * d->window[2] - 1);
+  if (nbins > kMaxBins) return fail(SWIN_ERR_UNSUPPORTED, "relative-position table larger than 2048 bins per head");
   if (d->dtype == SWIN_BF16) {
     if (hd != 32) return fail(SWIN_ERR_UNSUPPORTED, "bf16 kernels need head_dim == 32");
     if (d->channels % 64 != 0) return fail(SWIN_ERR_UNSUPPORTED, "bf16 kernels need channels % 64 == 0");
