@@ -170,50 +170,75 @@ __global__ __launch_bounds__(256, 2) void k_gemm_nt(const bf16* __restrict__ A, 
       }
   }
   __syncthreads();
+  // copy-out: a thread keeps one 8-column chunk and walks rows, so the column part of its
+  // destination (plane, head and offset, or column) is computed once
   constexpr int CH_PER_ROW = BN / 8;
-  static_assert((BM * CH_PER_ROW) % Cfg::NT == 0, "uniform copy-out loop");
+  constexpr int ROW_STEP = Cfg::NT / CH_PER_ROW;
+  constexpr int ITERS = BM / ROW_STEP;
+  static_assert(Cfg::NT % CH_PER_ROW == 0 && BM % ROW_STEP == 0, "uniform copy-out loop");
+  const int cc = (tid % CH_PER_ROW) * 8;
+  const int n = n0 + cc;
+  const int row0 = tid / CH_PER_ROW;
+  int64_t col_off, row_pitch;
+  if (ep.mode == 1) {
+    const int plane = n / ep.C;
+    const int rem = n - plane * ep.C;
+    const int head = rem / ep.hd;
+    col_off = ((int64_t)plane * ep.nh + head) * ep.n_tok * ep.hd + (rem - head * ep.hd);
+    row_pitch = ep.hd;
+  } else {
+    col_off = n;
+    row_pitch = ep.ldc;
+  }
+  if (!ep.dot_o) {
 #pragma unroll 4
-  for (int c = tid; c < BM * CH_PER_ROW; c += Cfg::NT) {
-    const int row = c / CH_PER_ROW;
-    const int cc = (c % CH_PER_ROW) * 8;
-    const int64_t m = m0 + row;
-    const int n = n0 + cc;
-    const bool valid = m < M && n < N;
-    const bf16x8 v = *(const bf16x8*)(Cs + row * Cfg::CPITCH + cc);
-    float dot = 0.f;
-    if (valid) {
-      bf16* dst;
-      if (ep.mode == 1) {
-        const int plane = n / ep.C;
-        const int rem = n - plane * ep.C;
-        const int head = rem / ep.hd;
-        const int d = rem - head * ep.hd;
-        dst = ep.out + (((int64_t)plane * ep.nh + head) * ep.n_tok + m) * ep.hd + d;
-      } else {
-        const int64_t orow = ep.out_rows ? (int64_t)ep.out_rows[m] : m;
-        dst = ep.out + orow * ep.ldc + n;
-      }
-      *(bf16x8*)dst = v;
-      if (ep.dot_o) {
-        const int64_t orow = ep.dot_rows ? (int64_t)ep.dot_rows[m] : m;
-        const bf16x8 ov = *(const bf16x8*)(ep.dot_o + orow * ep.C + n);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dot += to_f32(v[e]) * to_f32(ov[e]);
+    for (int it = 0; it < ITERS; ++it) {
+      const int row = row0 + ROW_STEP * it;
+      const int64_t m = m0 + row;
+      if (m < M && n < N) {
+        const int64_t orow = (ep.mode == 0 && ep.out_rows) ? (int64_t)ep.out_rows[m] : m;
+        *(bf16x8*)(ep.out + col_off + orow * row_pitch) = *(const bf16x8*)(Cs + row * Cfg::CPITCH + cc);
       }
     }
-    if (ep.dot_o) {
+  } else {
+    // Row dot products with dot_o: every row's chunk of dot_o is loaded up front (the
+    // accumulators are free by now), so the latency of those gathered loads is paid once.
+    bf16x8 ov[ITERS];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int64_t m = m0 + row0 + ROW_STEP * it;
+      ov[it] = bf16x8{};
+      if (m < M && n < N) {
+        const int64_t drow = ep.dot_rows ? (int64_t)ep.dot_rows[m] : m;
+        ov[it] = *(const bf16x8*)(ep.dot_o + drow * ep.C + n);
+      }
+    }
+    const int64_t dot_head = (int64_t)(n / ep.hd) * ep.n_tok;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int row = row0 + ROW_STEP * it;
+      const int64_t m = m0 + row;
+      const bool valid = m < M && n < N;
+      const bf16x8 v = *(const bf16x8*)(Cs + row * Cfg::CPITCH + cc);
+      float dot = 0.f;
+      if (valid) {
+        const int64_t orow = (ep.mode == 0 && ep.out_rows) ? (int64_t)ep.out_rows[m] : m;
+        *(bf16x8*)(ep.out + col_off + orow * row_pitch) = v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot += to_f32(v[e]) * to_f32(ov[it][e]);
+      }
       // the 4 chunks of one (row, head) sit in 4 consecutive lanes (head_dim 32)
       dot += __shfl_xor(dot, 1);
       dot += __shfl_xor(dot, 2);
-      if (valid && (c & 3) == 0) ep.dot_out[(int64_t)(n / ep.hd) * ep.n_tok + m] = dot;
+      if (valid && (tid & 3) == 0) ep.dot_out[dot_head + m] = dot;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Weight-gradient GEMM: P[s] = sum over the tokens t of chunk s of A[t, m0:m0+256]^T B[t, n0:n0+256]
-// (both operands token-major: a contraction over tokens), stored transposed per split as
-// P[s][n][m] so that each lane's four consecutive MFMA rows are one 16-byte store.
+// (both operands token-major: a contraction over tokens), stored per split as
+// P[s][m/4][n][m%4] so that each lane's four consecutive MFMA rows are one 16-byte store.
 //
 // 256 x 256 output tile, 8 waves of 128 x 64 (v_mfma_f32_32x32x16_bf16, 128 accumulators
 // per lane), 64-token steps. Both 64 x 256 operand tiles are copied straight into LDS
