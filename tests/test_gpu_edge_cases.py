@@ -1,0 +1,119 @@
+"""Edge cases of the HIP path against the fp64 oracle (through the C ABI).
+
+Degenerate and boundary shapes of the method: a window covering the whole grid (global
+attention), one-token windows, the largest windows each pass supports (256 tokens forward,
+160 backward), axes that are all or none periodic, ragged 3-D windows, and the smallest
+channel count. Same bars as the other parity tests: max-abs 2e-2 (bf16) / 1e-5 (fp32) on
+per-token outputs, 2e-2 * max(1, |ref|_inf) on reduced gradients."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from tests.gpu_util import log, run_chain, to_dev, ModuleOnDevice
+from tests.oracle_runner import chain_full
+from workloads import make_inputs
+from workloads.configs import SwinConfig
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+TOL_F32 = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from shifted_window_attention_amd import native  # noqa: F401  (raises if the library is missing)
+
+
+def _cfg(name, grid, window, shifts, channels=64, heads=2, batch=1, periodic=0x4, dtype="bf16", backward=True):
+    return SwinConfig(name=name, batch=batch, grid=grid, channels=channels, heads=heads, window=window,
+                      shifts=shifts, dtype=dtype, backward=backward, periodic=periodic, description=name)
+
+
+def _maxabs(a, b):
+    return float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
+
+
+def _check(cfg, with_bwd=True):
+    inp = make_inputs(cfg)
+    got = run_chain(cfg, inp, with_bwd=with_bwd)
+    ref = chain_full(cfg, inp, with_bwd=with_bwd)
+    tol = TOL_BF16 if cfg.dtype == "bf16" else TOL_F32
+    ey = _maxabs(got["y"], ref["y"])
+    log("  %s y max-abs %.3e" % (cfg.name, ey))
+    assert ey <= tol
+    if not with_bwd:
+        return
+    edx = _maxabs(got["dx"], ref["dx"])
+    log("  %s dx max-abs %.3e" % (cfg.name, edx))
+    assert edx <= tol
+    for i, (gm, rm) in enumerate(zip(got["grads"], ref["grads"])):
+        for k in ("w_qkv", "b_qkv", "w_proj", "b_proj", "table"):
+            r, g = rm[k].reshape(-1), gm[k].reshape(-1)
+            bound = tol * max(1.0, float(np.abs(r).max()))
+            err = _maxabs(g, r)
+            assert err <= bound, (cfg.name, i, k, err, bound)
+
+
+BF16_CASES = [
+    # the window is the whole grid: global attention over 128 tokens, two batch items
+    _cfg("global_8x16", (1, 8, 16), (1, 8, 16), ((0, 0, 0),), batch=2),
+    # one-token windows: every token attends only to itself (o = v)
+    _cfg("window_1x1", (1, 6, 10), (1, 1, 1), ((0, 0, 0),)),
+    # 160-token windows, the largest the backward pass supports, W-MSA then SW-MSA
+    _cfg("window_10x16", (1, 20, 48), (1, 10, 16), ((0, 0, 0), (0, 5, 8)), channels=128, heads=4),
+    # no periodic axis: both axes masked, ragged edges
+    _cfg("periodic_none", (1, 21, 29), (1, 6, 8), ((0, 3, 4),), periodic=0x0),
+    # both spatial axes periodic: shifted windows wrap without masks
+    _cfg("periodic_lat_lon", (1, 21, 29), (1, 6, 8), ((0, 3, 4),), periodic=0x6),
+    # 3-D with a ragged level axis (3 levels, 2-level windows) shifted on every axis
+    _cfg("levels_ragged", (3, 13, 26), (2, 6, 12), ((1, 3, 6),), channels=64, heads=2),
+]
+
+
+@pytest.mark.parametrize("cfg", BF16_CASES, ids=lambda c: c.name)
+def test_bf16_edge_case_vs_oracle(cfg):
+    log("bf16 edge case", cfg.name, cfg.grid, cfg.window, cfg.shifts)
+    _check(cfg)
+
+
+def test_bf16_256_token_windows_forward_and_backward_refusal():
+    import torch
+    from shifted_window_attention_amd import native as N
+    cfg = _cfg("window_16x16", (1, 32, 40), (1, 16, 16), ((0, 8, 8),), backward=False)
+    log("bf16 256-token windows", cfg.grid, cfg.window)
+    _check(cfg, with_bwd=False)
+    # the backward pass supports windows of at most 160 tokens and says so before launching
+    inp = make_inputs(cfg)
+    m = ModuleOnDevice(cfg, 0, inp.modules[0])
+    x = to_dev(inp.x_dev, "bf16")
+    y = m.fwd(x)
+    L = N.lib
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    C = cfg.channels
+    dx = torch.empty_like(x)
+    dwq = torch.empty(3 * C, C, dtype=torch.float32, device="cuda")
+    dwp = torch.empty(C, C, dtype=torch.float32, device="cuda")
+    dtab = torch.empty_like(m.table)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    st = L.swin_attn_bwd(m.plan.handle, p(y), p(x), p(m.w_qkv), p(m.w_proj), p(m.table), p(m.saved), p(dx),
+                         p(dwq), None, p(dwp), None, p(dtab), p(ws), ws.numel(), None)
+    assert st == 2  # SWIN_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+
+
+F32_CASES = [
+    _cfg("f32_ragged", (1, 21, 29), (1, 6, 8), ((0, 3, 4),), dtype="f32", backward=False),
+    _cfg("f32_window_1x1", (1, 6, 10), (1, 1, 1), ((0, 0, 0),), dtype="f32", backward=False),
+    _cfg("f32_global", (1, 8, 16), (1, 8, 16), ((0, 0, 0),), dtype="f32", backward=False, batch=2),
+]
+
+
+@pytest.mark.parametrize("cfg", F32_CASES, ids=lambda c: c.name)
+def test_f32_edge_case_forward_vs_oracle(cfg):
+    log("fp32 edge case", cfg.name, cfg.grid, cfg.window, cfg.shifts)
+    _check(cfg, with_bwd=False)
