@@ -68,10 +68,17 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
   // are one 8-byte store; the pitch (an odd multiple of 8 bytes past a 16-byte multiple)
   // puts the 16 keys x 2 query groups of a half-wave store on distinct banks
   constexpr int SPT = 16 * NKT + 8;
-  constexpr int SLAB = ((int)sizeof(BwdBuf<NKT>) / (NKT * 16 * 4)) / 16 * 16;  // rows per pass in bufA
-  static_assert(SLAB >= 16, "LDS too small for the bias-gradient slab");
+  // Binning slab: rows of 16 NKT fp32 pair sums, laid over the two staging buffers and the dS
+  // tile once the window loop is done (rows [0, RA) in bufA, [RA, 2 RA) in bufB, the rest in
+  // dSt); usually all 16 NKT query rows fit, so one pass bins the whole chunk.
+  // slab row pitch: 16 NKT + 4 floats, so the 4 query groups of a store land on distinct banks
+  constexpr int KCOLS = 16 * NKT + 4;
+  constexpr int KROW = KCOLS * 4;                                       // bytes per slab row
+  constexpr int RA = (int)sizeof(BwdBuf<NKT>) / KROW;
+  constexpr int RS = (int)(ROWS * (16 * NKT + 8) * sizeof(bf16)) / KROW;
+  constexpr int SLAB = 2 * RA + RS;
+  static_assert(RA >= 1 && SLAB >= 16, "LDS too small for the bias-gradient slab");
   static_assert(BwdBuf<NKT>::FROWS % 64 == 0 && BwdBuf<NKT>::FROWS >= ROWS, "float rows are whole copies");
-  static_assert(SLAB * NKT * 16 * 4 <= (int)sizeof(BwdBuf<NKT>), "binning slab fits in one buffer");
   // Two staging buffers (separate objects, loop unrolled by two, see the forward kernel)
   // filled by direct global->LDS copies while the other one is computed, dS for dQ, and
   // the per-bin partial sums.
@@ -253,15 +260,18 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
   flush();
 
   // bin the chunk's per-position dS sums into the relative-position table, slab by slab
-  float* acc = (float*)&bufA;  // [SLAB][16 NKT] fp32 inside the first staging buffer
-  const int kcols = 16 * NKT;
+  auto slab_row = [&](int lr) -> float* {
+    if (lr < RA) return (float*)&bufA + lr * KCOLS;
+    if (lr < 2 * RA) return (float*)&bufB + (lr - RA) * KCOLS;
+    return (float*)dSt + (lr - 2 * RA) * KCOLS;
+  };
   for (int q0 = 0; q0 < 16 * NKT; q0 += SLAB) {
 #pragma unroll
     for (int qt = 0; qt < NKT; ++qt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = 16 * qt + 4 * g + i;
-        if (q >= q0 && q < q0 + SLAB) acc[(q - q0) * kcols + key] = dbacc[qt][i];
+        if (q >= q0 && q < q0 + SLAB) slab_row(q - q0)[key] = dbacc[qt][i];
       }
     __syncthreads();
     for (int b = tid; b < a.nbins; b += NT) {
@@ -280,7 +290,7 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
           const int w0 = rw > 0 ? rw : 0, w1 = ci.ext[2] + (rw < 0 ? rw : 0);
           for (int qw = w0; qw < w1; ++qw) {
             const int q = row + qw;
-            if (q >= q0 && q < q1) sum += acc[(q - q0) * kcols + (q - dk)];
+            if (q >= q0 && q < q1) sum += slab_row(q - q0)[q - dk];
           }
         }
       bins_lds[b] = sum;

@@ -323,7 +323,8 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
     }
   }
   build_work(p->classes, p->nh, 4096, 16, p->fwd_work, p->fwd_ranges);
-  build_work(p->classes, p->nh, 2048, kMaxChunk, p->bwd_work, p->bwd_ranges);
+  // the backward bins its bias gradient once per work item: fewer, longer items (1 WG per CU)
+  build_work(p->classes, p->nh, 1024, kMaxChunk, p->bwd_work, p->bwd_ranges);
 
   // saved state and workspace layout
   const size_t es = desc->dtype == SWIN_BF16 ? 2 : 4;

@@ -40,7 +40,7 @@ struct WorkRange {
 
 constexpr int kMaxFwdTiles = 16;  // forward: windows of up to 256 tokens
 constexpr int kMaxBwdTiles = 10;  // backward: windows of up to 160 tokens (LDS budget)
-constexpr int kMaxChunk = 32;     // windows per attention work item
+constexpr int kMaxChunk = 64;     // windows per attention work item
 constexpr int kMaxBins = 2048;    // bias-table bins per head (windows of <= 256 tokens have < 2048)
 
 struct DevTables {
