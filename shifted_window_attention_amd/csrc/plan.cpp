@@ -322,7 +322,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
       p->class_win[p->classes[c].first + fill[c]++] = (int32_t)w;
     }
   }
-  build_work(p->classes, p->nh, 4096, 16, p->fwd_work, p->fwd_ranges);
+  build_work(p->classes, p->nh, 1024, 64, p->fwd_work, p->fwd_ranges);
   // the backward bins its bias gradient once per work item: fewer, longer items (1 WG per CU)
   build_work(p->classes, p->nh, 1024, kMaxChunk, p->bwd_work, p->bwd_ranges);
 
