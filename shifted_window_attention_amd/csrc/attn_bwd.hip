@@ -6,7 +6,8 @@
 // (q' = tau log2(e) q is the stored query). The inverse routes carry these gradients
 // back to their sources (TERRA section IV-D).
 //
-// D = rowsum(dO * O) comes from the epilogue of the GEMM that produces dO.
+// D = rowsum(dO * O) comes (negated) from the epilogue of the GEMM that produces dO; the
+// logit and dP products start from bias - lse and -D, which saves two subtractions per pair.
 //
 // Work decomposition: one workgroup per (chunk of windows of one class, head), one wave
 // per 16-key tile. Each window's Q', dO, K, V, lse and D are staged in LDS by direct
@@ -34,7 +35,7 @@ struct BwdArgs {
   const bf16* o;            // saved [n_tok][C], grid order
   const float* lse;         // saved [nh][n_tok] (log2 units)
   const bf16* dO;           // [nh][n_tok][32]
-  const float* dd;          // [nh][n_tok]: D = rowsum(dO * O)
+  const float* dd;          // [nh][n_tok]: -D = -rowsum(dO * O)
   const float* table;       // [nh][nbins]
   bf16* dqkv;               // [n_tok][3C], grid order (row perm[slot])
   const int32_t* perm;      // window-major slot -> grid row
@@ -191,15 +192,18 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
       for (int u = 0; u < 2; ++u) {
         const int qt = 2 * c + u;
         if (qt < NKT) {
-          const f32x4 b4 = {(float)bias[qt][0], (float)bias[qt][1], (float)bias[qt][2], (float)bias[qt][3]};
-          const f32x4 s = mfma16(tile_frag(cur.q, 16 * qt + li, g), kb, b4);
-          const f32x4 dp = mfma16(tile_frag(cur.dO, 16 * qt + li, g), vb, f32x4{});
+          // the products start from bias - lse and from -D, so they end as log2(P) and dP - D
           const f32x4 l4 = *(const f32x4*)(cur.lse + 16 * qt + 4 * g);
-          const f32x4 d4 = *(const f32x4*)(cur.dd + 16 * qt + 4 * g);
+          const f32x4 nd4 = *(const f32x4*)(cur.dd + 16 * qt + 4 * g);
+          const u32x2 bp = __builtin_bit_cast(u32x2, bias[qt]);
+          const f32x4 b4 = {half_lo_minus(bp[0], l4[0]), half_hi_minus(bp[0], l4[1]), half_lo_minus(bp[1], l4[2]),
+                            half_hi_minus(bp[1], l4[3])};
+          const f32x4 s = mfma16(tile_frag(cur.q, 16 * qt + li, g), kb, b4);
+          const f32x4 dp = mfma16(tile_frag(cur.dO, 16 * qt + li, g), vb, nd4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p = fast_exp2(s[i] - l4[i]);
-            const float ds = p * (dp[i] - d4[i]);
+            const float p = fast_exp2(s[i]);
+            const float ds = p * dp[i];
             dbacc[qt][i] += ds;
             pb[4 * u + i] = to_bf16(p);
             sb[4 * u + i] = to_bf16(ds);

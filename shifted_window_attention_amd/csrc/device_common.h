@@ -102,6 +102,19 @@ __device__ __forceinline__ bf16x8 tile_frag_tr(const unsigned char* tile, int ro
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// (float)h - x for the low or high fp16 half h of a packed pair, in one mixed-precision FMA
+// (the compiler emits a conversion and a subtraction for the plain expression).
+__device__ __forceinline__ float half_lo_minus(uint32_t pair, float x) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(x));
+  return r;
+}
+__device__ __forceinline__ float half_hi_minus(uint32_t pair, float x) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(x));
+  return r;
+}
+
 // LDS byte address of a pointer into a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;

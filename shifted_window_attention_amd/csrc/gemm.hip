@@ -27,9 +27,10 @@ struct EpiParams {
   float qscale;              // mode 1: factor for columns < C (the q block)
   int C, nh, hd;
   int64_t n_tok;
-  const bf16* dot_o;         // mode 1, one plane: if set, also write dot_out[head][m] =
-  float* dot_out;            //   sum over the head's columns of C[m, :] * dot_o[row(m), :]
+  const bf16* dot_o;         // mode 1, one plane: if set, also write dot_out[head][m] = dot_scale *
+  float* dot_out;            //   (sum over the head's columns of C[m, :] * dot_o[row(m), :])
   const int32_t* dot_rows;   //   with row(m) = dot_rows[m] (NULL: m)
+  float dot_scale;
 };
 
 template <int BM, int BN>
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_nt(const bf16* __restrict__ A, 
       // the 4 chunks of one (row, head) sit in 4 consecutive lanes (head_dim 32)
       dot += __shfl_xor(dot, 1);
       dot += __shfl_xor(dot, 2);
-      if (valid && (tid & 3) == 0) ep.dot_out[dot_head + m] = dot;
+      if (valid && (tid & 3) == 0) ep.dot_out[dot_head + m] = dot * ep.dot_scale;
     }
   }
 }
@@ -499,11 +500,12 @@ hipError_t launch_proj_fwd_bf16(const swin_attn_plan* p, const void* o, const vo
 hipError_t launch_dproj_bf16(const swin_attn_plan* p, const void* dy, const void* wprojT, void* dO, const void* o,
                              float* dd, hipStream_t s) {
   EpiParams ep{};
-  ep.mode = 1;  // head-split, one plane, plus D = rowsum(dO * O) per head
+  ep.mode = 1;  // head-split, one plane, plus -D = -rowsum(dO * O) per head
   ep.out = (bf16*)dO;
   ep.dot_o = (const bf16*)o;
   ep.dot_rows = p->dev.perm;  // o is in grid order
   ep.dot_out = dd;
+  ep.dot_scale = -1.f;        // the attention backward starts its dP products from -D
   ep.qscale = 1.f;
   ep.C = p->C;
   ep.nh = p->nh;
