@@ -5,7 +5,8 @@ workload (a 2160x4320 field after 4x4 patch embedding): W-MSA forward, SW-MSA
 (shift 6,6) forward, SW-MSA backward, W-MSA backward, each module being gather +
 QKV GEMM + window attention + proj GEMM + scatter and their backward. Inputs are
 seeded synthetic data resident in HBM before the timed region. After the timed steps the
-window gather and scatter are also timed stand-alone against a device-to-device copy.
+window gather and scatter are also timed stand-alone against a device-to-device copy, and the
+chain is timed on one GPU's share of an 8-way latitude split (72x1080 tokens).
 
 Prints one JSON line on stdout:
   value = token-blocks per second (tokens x modules per step / step time),
@@ -209,6 +210,65 @@ def time_window_moves(hip, N, plan, x, stream, cfg, reps=20):
     return res
 
 
+def time_shard_share(hip, N, stream, base_cfg, steps, warmup):
+    """The same W-MSA -> SW-MSA chain on one GPU's share of an 8-way latitude split of the grid:
+    72 of the 540 latitude rows (6 window rows, 540 windows per module). A sharded run would fill
+    6 halo rows from the neighbour for the shifted module; here the stripe edges are masked like
+    the grid's own latitude edges, so the per-GPU compute shape is the same."""
+    import numpy as np
+    import torch
+    from tests.gpu_util import ModuleOnDevice
+    from workloads.configs import small_variant
+    cfg = small_variant(base_cfg, grid=(1, 72, base_cfg.grid[2]))
+    inp = _device_inputs(cfg)
+    x, dy = inp.x_t, inp.dy_t
+    mods = [ModuleOnDevice(cfg, i, p) for i, p in enumerate(inp.modules)]
+    C = cfg.channels
+    y1, y2, dx2, dx1 = (torch.empty_like(x) for _ in range(4))
+    grads = [{"w_qkv": torch.empty(3 * C, C, dtype=torch.float32, device="cuda"),
+              "b_qkv": torch.empty(3 * C, dtype=torch.float32, device="cuda"),
+              "w_proj": torch.empty(C, C, dtype=torch.float32, device="cuda"),
+              "b_proj": torch.empty(C, dtype=torch.float32, device="cuda"),
+              "table": torch.empty_like(m.table)} for m in mods]
+
+    def step():
+        m1, m2 = mods
+        N.swin_attn_fwd(m1.plan.handle, x, m1.w_qkv, m1.b_qkv, m1.w_proj, m1.b_proj, m1.table, y1, m1.saved,
+                        stream=stream)
+        N.swin_attn_fwd(m2.plan.handle, y1, m2.w_qkv, m2.b_qkv, m2.w_proj, m2.b_proj, m2.table, y2, m2.saved,
+                        stream=stream)
+        g = grads[1]
+        N.swin_attn_bwd(m2.plan.handle, dy, y1, m2.w_qkv, m2.w_proj, m2.table, m2.saved, dx2, g["w_qkv"],
+                        g["b_qkv"], g["w_proj"], g["b_proj"], g["table"], m2.ws, stream=stream)
+        g = grads[0]
+        N.swin_attn_bwd(m1.plan.handle, dx2, x, m1.w_qkv, m1.w_proj, m1.table, m1.saved, dx1, g["w_qkv"],
+                        g["b_qkv"], g["w_proj"], g["b_proj"], g["table"], m1.ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = hip.events(2)
+    assert hip.l.hipEventRecord(t0, stream.cuda_stream) == 0
+    for _ in range(steps):
+        step()
+    assert hip.l.hipEventRecord(t1, stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(t0, t1) / steps
+    hip.destroy([t0, t1])
+    flops = 0
+    for m in mods:
+        f, _ = stage_flops_bytes(cfg, m.plan.stats["allowed_pairs"])
+        flops += sum(f.values())
+    res = {"grid": list(cfg.grid[1:]), "windows_per_module": int(mods[0].plan.stats["n_windows"]),
+           "tokens": cfg.n_tokens, "steps": steps, "ms_per_step": round(ms, 4),
+           "tokens_per_s": round(cfg.n_tokens * cfg.modules / (ms * 1e-3), 1),
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "mfma_peak_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    for m in mods:
+        m.plan.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,6 +413,7 @@ def main():
     roof["traffic"] = traffic_for(dom, per_launch_ref)
 
     moves = time_window_moves(hip, N, mods[1].plan.handle, x, stream, cfg)
+    shard = time_shard_share(hip, N, stream, cfg, max(1, args.steps // 2), max(1, args.warmup // 2))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -371,7 +432,7 @@ def main():
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "algorithmic_gflop_per_step": round(flops_step / 1e9, 2),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "roofline": roof, "kernels": kernels, "window_moves": moves, "cpu_baseline": cpu,
+        "roofline": roof, "kernels": kernels, "window_moves": moves, "shard_share_8way": shard, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
