@@ -110,3 +110,47 @@ def make_inputs(cfg: SwinConfig, seed: int = 0, bias_scale: float = 0.1,
         x = None
         dy = None
     return Inputs(cfg=cfg, x=x, dy=dy, modules=mods, x_dev=x_dev, dy_dev=dy_dev)
+
+
+@dataclass
+class BlockExtras:
+    """The parts of one Swin block around its attention module: two layer normalisations and
+    the MLP, as float64 values rounded to the run dtype, plus their device storage (``dev``)."""
+    ln1_g: np.ndarray
+    ln1_b: np.ndarray
+    ln2_g: np.ndarray
+    ln2_b: np.ndarray
+    w1: np.ndarray   # [hidden, C]
+    b1: np.ndarray   # [hidden]
+    w2: np.ndarray   # [C, hidden]
+    b2: np.ndarray   # [C]
+    dev: dict = None
+
+
+def make_block_extras(cfg: SwinConfig, hidden: Optional[int] = None, seed: int = 0,
+                      bias_scale: float = 0.1, norm_scale: float = 0.1) -> List[BlockExtras]:
+    """Per chained block, drawn from numpy default_rng([seed, 1]) (a stream separate from
+    make_inputs, whose draws stay unchanged) in float64, in the order ln1 scale, ln1 shift,
+    ln2 scale, ln2 shift, W1, b1, W2, b2. Scales are 1 + norm_scale N(0,1) and shifts
+    norm_scale N(0,1) (0 and 1 exactly when norm_scale = 0); W1, W2 Xavier-normal; biases
+    bias_scale N(0,1). Hidden width 4C unless given."""
+    rng = np.random.default_rng([seed, 1])
+    C = cfg.channels
+    H = 4 * C if hidden is None else hidden
+    out = []
+    for _ in range(cfg.modules):
+        draws = {
+            "ln1_g": 1.0 + norm_scale * rng.standard_normal(C),
+            "ln1_b": norm_scale * rng.standard_normal(C),
+            "ln2_g": 1.0 + norm_scale * rng.standard_normal(C),
+            "ln2_b": norm_scale * rng.standard_normal(C),
+            "w1": rng.standard_normal((H, C)) * np.sqrt(2.0 / (C + H)),
+            "b1": bias_scale * rng.standard_normal(H),
+            "w2": rng.standard_normal((C, H)) * np.sqrt(2.0 / (C + H)),
+            "b2": bias_scale * rng.standard_normal(C),
+        }
+        vals, dev = {}, {}
+        for k, v in draws.items():
+            vals[k], dev[k] = _to_dtype(v, cfg.dtype)
+        out.append(BlockExtras(dev=dev, **vals))
+    return out
