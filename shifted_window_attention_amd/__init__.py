@@ -2,7 +2,7 @@
 
 A thin ctypes binding over libswinattn.so: every function here only marshals
 arguments (tensor data pointers, sizes, the current HIP stream) to the C ABI
-declared in include/swin_attn.h, under the same names. All computation runs in
+declared in include/swin_attn.h and include/swin_block.h, under the same names. All computation runs in
 the library's HIP kernels; there is no fallback. If the library has not been
 built, importing the binding raises.
 """
@@ -14,4 +14,6 @@ from .native import (  # noqa: F401
     SwinAttnStats, SwinError, lib, make_desc, swin_attn_bwd, swin_attn_fwd, swin_attn_host_index_map,
     swin_attn_host_stats, swin_attn_plan_create, swin_attn_plan_destroy, swin_attn_plan_stats, swin_attn_sizes,
     swin_status_string, swin_window_gather, swin_window_scatter, swin_attn_trace_events, swin_attn_trace_cursor, Plan,
+    SwinBlockDesc, SwinBlockParams, SwinBlockGrads, make_block_desc, swin_block_plan_create, swin_block_plan_destroy,
+    swin_block_sizes, swin_block_fwd, swin_block_bwd, BlockPlan,
 )

@@ -330,9 +330,6 @@ hipError_t launch_dproj_bf16(const swin_attn_plan* p, const void* dy, const void
                              float* dd, hipStream_t s);
 hipError_t launch_dgrad_qkv_bf16(const swin_attn_plan* p, const void* dqkv, const void* wqkvT, void* dx,
                                  hipStream_t s);
-hipError_t launch_wgrad_bf16(const bf16* A, int64_t lda, const bf16* B, int64_t ldb, int64_t T, int M, int N,
-                             int splits, int64_t chunk, float* part, float* dw, float* db, hipStream_t s);
-hipError_t launch_transpose_bf16(const void* in, void* out, int R, int Cn, hipStream_t s);
 
 hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* x, const void* w_qkv,
                            const void* w_proj, const float* table, const void* saved, void* dx, float* dw_qkv,

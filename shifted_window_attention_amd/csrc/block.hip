@@ -1,0 +1,188 @@
+// Swin Transformer block around the attention module (TERRA section IV-A, Fig. 4: block 0
+// is W-MSA followed by an MLP, block 1 SW-MSA followed by an MLP, with layer
+// normalisation), read as the pre-normalisation block
+//     h = x + A(LN1(x)),        y = h + W2 GELU(W1 LN2(h) + b1) + b2.
+//
+// Layer normalisation has kernels of its own (one wave per token row, fp32 statistics);
+// the residual adds, the MLP bias + GELU and the GELU derivative are fused into the
+// epilogues of the row GEMMs, and the MLP weight gradients use the split-K token
+// contraction of the attention module.
+#include "device_common.h"
+#include "swin_internal.h"
+
+namespace swin {
+
+__device__ __forceinline__ float wave_sum64(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// y = (x - mean) rstd g + b per row of C channels (biased variance, fp32 statistics);
+// mean and rstd are saved for the backward. One wave per row, lane l holds the 8-channel
+// chunks l, l + 64, ... (CH of them).
+template <int CH>
+__global__ __launch_bounds__(256) void k_layernorm_fwd(const bf16* __restrict__ x, const bf16* __restrict__ g,
+                                                       const bf16* __restrict__ b, bf16* __restrict__ y,
+                                                       float* __restrict__ mean_out, float* __restrict__ rstd_out,
+                                                       int64_t rows, int C, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int nch = C / 8;
+  float v[CH][8];
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ch = lane + 64 * c;
+    const bf16x8 t = ch < nch ? *(const bf16x8*)(x + row * C + 8 * ch) : bf16x8{};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[c][e] = to_f32(t[e]);
+      sum += v[c][e];
+    }
+  }
+  const float mean = wave_sum64(sum) / C;
+  float sq = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+    if (lane + 64 * c < nch)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq += (v[c][e] - mean) * (v[c][e] - mean);
+  const float rstd = rsqrtf(wave_sum64(sq) / C + eps);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nch) {
+      const bf16x8 gg = *(const bf16x8*)(g + 8 * ch), bb = *(const bf16x8*)(b + 8 * ch);
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = to_bf16((v[c][e] - mean) * rstd * to_f32(gg[e]) + to_f32(bb[e]));
+      *(bf16x8*)(y + row * C + 8 * ch) = o;
+    }
+  }
+  if (lane == 0) {
+    mean_out[row] = mean;
+    rstd_out[row] = rstd;
+  }
+}
+
+// Backward of k_layernorm_fwd plus a residual gradient:
+//   dx = dres + rstd (dxhat - mean(dxhat) - xhat mean(dxhat xhat)),  dxhat = dy g,
+// and, per group of LN_GROUP_ROWS rows, partial sums of dg = sum dy xhat and db = sum dy
+// (part[group][0][:] and part[group][1][:]), combined over the 4 waves in a fixed order.
+constexpr int kLnGroupRows = 256;
+
+template <int CH>
+__global__ __launch_bounds__(256) void k_layernorm_bwd(const bf16* __restrict__ dy, const bf16* __restrict__ x,
+                                                       const float* __restrict__ mean, const float* __restrict__ rstd,
+                                                       const bf16* __restrict__ g, const bf16* __restrict__ dres,
+                                                       bf16* __restrict__ dx, float* __restrict__ part, int64_t rows,
+                                                       int C) {
+  __shared__ float red[4][2][64 * 8 * CH];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nch = C / 8;
+  const int64_t r0 = (int64_t)blockIdx.x * kLnGroupRows;
+  const int64_t r1 = r0 + kLnGroupRows < rows ? r0 + kLnGroupRows : rows;
+  float gv[CH][8], dg[CH][8], db[CH][8];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ch = lane + 64 * c;
+    const bf16x8 t = ch < nch ? *(const bf16x8*)(g + 8 * ch) : bf16x8{};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      gv[c][e] = to_f32(t[e]);
+      dg[c][e] = 0.f;
+      db[c][e] = 0.f;
+    }
+  }
+  for (int64_t row = r0 + w; row < r1; row += 4) {
+    const float mu = mean[row], rs = rstd[row];
+    float xh[CH][8], dxh[CH][8];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ch = lane + 64 * c;
+      const bf16x8 tx = ch < nch ? *(const bf16x8*)(x + row * C + 8 * ch) : bf16x8{};
+      const bf16x8 ty = ch < nch ? *(const bf16x8*)(dy + row * C + 8 * ch) : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = to_f32(ty[e]);
+        xh[c][e] = ch < nch ? (to_f32(tx[e]) - mu) * rs : 0.f;
+        dxh[c][e] = d * gv[c][e];
+        s1 += dxh[c][e];
+        s2 += dxh[c][e] * xh[c][e];
+        dg[c][e] += d * xh[c][e];
+        db[c][e] += d;
+      }
+    }
+    s1 = wave_sum64(s1) / C;
+    s2 = wave_sum64(s2) / C;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch) {
+        const bf16x8 tr = *(const bf16x8*)(dres + row * C + 8 * ch);
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = to_bf16(rs * (dxh[c][e] - s1 - xh[c][e] * s2) + to_f32(tr[e]));
+        *(bf16x8*)(dx + row * C + 8 * ch) = o;
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      red[w][0][8 * (lane + 64 * c) + e] = dg[c][e];
+      red[w][1][8 * (lane + 64 * c) + e] = db[c][e];
+    }
+  __syncthreads();
+  float* out = part + (int64_t)blockIdx.x * 2 * C;
+  for (int i = threadIdx.x; i < 2 * C; i += 256) {
+    const int k = i / C, c = i - k * C;
+    out[i] = ((red[0][k][c] + red[1][k][c]) + red[2][k][c]) + red[3][k][c];
+  }
+}
+
+// out[i] = sum over groups (in order) of part[g][i], i < n; the first half to dg, the second to db.
+__global__ __launch_bounds__(256) void k_reduce_groups(const float* __restrict__ part, int groups, int n,
+                                                       float* __restrict__ dg, float* __restrict__ db) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float acc = 0.f;
+  for (int k = 0; k < groups; ++k) acc += part[(int64_t)k * n + i];
+  const int C = n / 2;
+  if (i < C)
+    dg[i] = acc;
+  else
+    db[i - C] = acc;
+}
+
+hipError_t launch_layernorm_fwd(const bf16* x, const bf16* g, const bf16* b, bf16* y, float* mean, float* rstd,
+                                int64_t rows, int C, float eps, hipStream_t s) {
+  const unsigned blocks = (unsigned)((rows + 3) / 4);
+  if (C <= 512)
+    k_layernorm_fwd<1><<<blocks, 256, 0, s>>>(x, g, b, y, mean, rstd, rows, C, eps);
+  else
+    k_layernorm_fwd<2><<<blocks, 256, 0, s>>>(x, g, b, y, mean, rstd, rows, C, eps);
+  return hipGetLastError();
+}
+
+int layernorm_groups(int64_t rows) { return (int)((rows + kLnGroupRows - 1) / kLnGroupRows); }
+
+hipError_t launch_layernorm_bwd(const bf16* dy, const bf16* x, const float* mean, const float* rstd, const bf16* g,
+                                const bf16* dres, bf16* dx, float* part, float* dg, float* db, int64_t rows, int C,
+                                hipStream_t s) {
+  const int groups = layernorm_groups(rows);
+  if (C <= 512)
+    k_layernorm_bwd<1><<<groups, 256, 0, s>>>(dy, x, mean, rstd, g, dres, dx, part, rows, C);
+  else
+    k_layernorm_bwd<2><<<groups, 256, 0, s>>>(dy, x, mean, rstd, g, dres, dx, part, rows, C);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_reduce_groups<<<(unsigned)((2 * C + 255) / 256), 256, 0, s>>>(part, groups, 2 * C, dg, db);
+  return hipGetLastError();
+}
+
+}  // namespace swin

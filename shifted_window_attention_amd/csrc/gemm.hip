@@ -19,8 +19,13 @@
 namespace swin {
 
 struct EpiParams {
-  int mode;                  // 0: rows (optionally scattered), 1: head-split planes [P][nh][n_tok][hd]
+  int mode;                  // 0: rows (optionally scattered), 1: head-split planes [P][nh][n_tok][hd],
+                             // 2: rows of GELU(C + bias), with C + bias also written to out2,
+                             // 3: rows of C * GELU'(aux) (aux [M][N] bf16, no bias)
   bf16* out;
+  bf16* out2;                // mode 2: pre-activation rows [M][N]
+  const bf16* aux;           // mode 3: the pre-activation the GELU derivative is taken at
+  const bf16* res;           // mode 0: if set, residual rows added before rounding (same layout as out)
   const int32_t* out_rows;   // mode 0: destination row of each C row (NULL: identity)
   int64_t ldc;               // mode 0: row pitch of out (elements)
   const bf16* bias;          // [N] or NULL
@@ -64,6 +69,76 @@ __device__ __forceinline__ bool xcd_tile(int64_t n_tiles, int nt, int64_t& mt_ou
 }
 
 static inline unsigned xcd_grid(int64_t n_tiles) { return (unsigned)((n_tiles + 7) / 8 * 8); }
+
+// Exact GELU and its derivative (erf from the device math library).
+__device__ __forceinline__ float gelu_f(float a) { return 0.5f * a * (1.f + erff(a * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_grad_f(float a) {
+  return 0.5f * (1.f + erff(a * 0.70710678118654752f)) + a * 0.39894228040143268f * __expf(-0.5f * a * a);
+}
+
+// Epilogue of the element-wise modes (2, 3, and 0 with a residual): the accumulator tile
+// plus bias goes through LDS as fp32 in two halves of BM/2 rows, so the residual add or the
+// activation is applied before the single rounding to bf16; 16-byte row stores.
+template <int BM, int BN>
+__device__ __forceinline__ void epilogue_f32(const f32x16 (&acc)[NtCfg<BM, BN>::TM][NtCfg<BM, BN>::TN], bf16* smem,
+                                             int tid, int lane, int wm, int wn, int64_t m0, int n0, int64_t M, int N,
+                                             const EpiParams& ep) {
+  using Cfg = NtCfg<BM, BN>;
+  constexpr int HALF = BM / 2, FP = BN + 4;  // fp32 pitch
+  static_assert(Cfg::WAVES_M == 2 && HALF == Cfg::WTM, "one wave row per half");
+  static_assert(HALF * FP * 4 <= Cfg::LDS_ELEMS * 2, "an fp32 half tile fits the LDS of the main loop");
+  float* Cs = (float*)smem;
+  const int fr = lane & 31;
+  constexpr int CH_PER_ROW = BN / 8;
+  constexpr int ROW_STEP = Cfg::NT / CH_PER_ROW;
+  const int cc = (tid % CH_PER_ROW) * 8;
+  const int n = n0 + cc;
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+#pragma unroll
+      for (int j = 0; j < Cfg::TN; ++j) {
+        const int col = wn * Cfg::WTN + 32 * j + fr;
+        const float bv = (ep.bias && n0 + col < N) ? to_f32(ep.bias[n0 + col]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            Cs[row * FP + col] = acc[i][j][r] + bv;
+          }
+      }
+    }
+    __syncthreads();
+#pragma unroll 2
+    for (int row = tid / CH_PER_ROW; row < HALF; row += ROW_STEP) {
+      const int64_t m = m0 + HALF * half + row;
+      if (m >= M || n >= N) continue;
+      const f32x4 lo = *(const f32x4*)(Cs + row * FP + cc), hi = *(const f32x4*)(Cs + row * FP + cc + 4);
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const int64_t orow = (ep.mode == 0 && ep.out_rows) ? (int64_t)ep.out_rows[m] : m;
+      bf16x8 o;
+      if (ep.mode == 2) {
+        bf16x8 pre;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pre[e] = to_bf16(v[e]);
+          o[e] = to_bf16(gelu_f(v[e]));
+        }
+        *(bf16x8*)(ep.out2 + m * ep.ldc + n) = pre;
+      } else if (ep.mode == 3) {
+        const bf16x8 a = *(const bf16x8*)(ep.aux + m * ep.ldc + n);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = to_bf16(v[e] * gelu_grad_f(to_f32(a[e])));
+      } else {
+        const bf16x8 r = *(const bf16x8*)(ep.res + orow * ep.ldc + n);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = to_bf16(v[e] + to_f32(r[e]));
+      }
+      *(bf16x8*)(ep.out + orow * ep.ldc + n) = o;
+    }
+    __syncthreads();
+  }
+}
 
 template <int BM, int BN>
 __global__ __launch_bounds__(256, 2) void k_gemm_nt(const bf16* __restrict__ A, int64_t lda,
@@ -154,6 +229,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_nt(const bf16* __restrict__ A, 
     }
   }
 
+  if (ep.mode >= 2 || ep.res) {
+    epilogue_f32<BM, BN>(acc, smem, tid, lane, wm, wn, m0, n0, M, N, ep);
+    return;
+  }
   // epilogue: scale/bias in registers, bf16 tile through LDS, 16-byte row stores
   bf16* Cs = smem;
 #pragma unroll
@@ -524,6 +603,39 @@ hipError_t launch_dgrad_qkv_bf16(const swin_attn_plan* p, const void* dqkv, cons
   ep.C = p->C;
   return gemm_nt((const bf16*)dqkv, 3 * p->C, nullptr, (const bf16*)wqkvT, 3 * p->C, p->n_tok, p->C, 3 * p->C, ep,
                  s);
+}
+
+// Output projection whose epilogue also adds a residual (the block's h = x + proj(o)).
+hipError_t launch_proj_fwd_res_bf16(const swin_attn_plan* p, const void* o, const void* w, const void* b,
+                                    const void* res, void* y, hipStream_t s) {
+  EpiParams ep{};
+  ep.mode = 0;
+  ep.out = (bf16*)y;
+  ep.res = (const bf16*)res;
+  ep.ldc = p->C;
+  ep.bias = (const bf16*)b;
+  ep.qscale = 1.f;
+  ep.C = p->C;
+  return gemm_nt((const bf16*)o, p->C, nullptr, (const bf16*)w, p->C, p->n_tok, p->C, p->C, ep, s);
+}
+
+// out[M][N] = epilogue(A[M][K] B[N][K]^T): mode 0 (+ bias, + optional residual rows),
+// 2 (GELU of the biased product, the biased product itself to out2) or 3 (product times
+// GELU'(aux)). All row-major with pitch N.
+hipError_t launch_rows_gemm_bf16(const bf16* A, int64_t lda, const bf16* B, int64_t ldb, int64_t M, int N, int K,
+                                 const bf16* bias, int mode, bf16* out, bf16* out2, const bf16* aux, const bf16* res,
+                                 hipStream_t s) {
+  EpiParams ep{};
+  ep.mode = mode;
+  ep.out = out;
+  ep.out2 = out2;
+  ep.aux = aux;
+  ep.res = res;
+  ep.ldc = N;
+  ep.bias = bias;
+  ep.qscale = 1.f;
+  ep.C = N;
+  return gemm_nt(A, lda, nullptr, B, ldb, M, N, K, ep, s);
 }
 
 hipError_t launch_wgrad_bf16(const bf16* A, int64_t lda, const bf16* B, int64_t ldb, int64_t T, int M, int N,

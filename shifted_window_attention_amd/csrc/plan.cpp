@@ -68,6 +68,18 @@ static swin_status validate(const swin_attn_desc* d) {
   return SWIN_OK;
 }
 
+// Split-K for a weight gradient (a contraction over n_tok tokens with an M x N output):
+// 256 x 256 output tiles, one workgroup per CU at a time, and at most two full rounds of
+// workgroups (no partial third round); chunks are whole 64-token steps.
+void wgrad_split(int64_t n_tok, int64_t M, int64_t N, int* splits, int64_t* chunk) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  int64_t s = std::max<int64_t>(1, 512 / tiles);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, n_tok / 512));
+  *splits = (int)s;
+  const int64_t c = (n_tok + s - 1) / s;
+  *chunk = (c + 63) / 64 * 64;
+}
+
 static swin_status check_kernel_support(const swin_attn_desc* d, int64_t max_tokens) {
   const int hd = d->channels / d->heads;
   if (max_tokens > 16 * kMaxFwdTiles)
@@ -334,22 +346,8 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
   p->saved_lse = align256(nt * (size_t)p->nh * 4);
   p->saved_total = p->saved_qkv + p->saved_o + p->saved_lse;
   if (desc->dtype == SWIN_BF16) {
-    // split-K for the weight gradients: 256 x 256 output tiles, one workgroup per CU at a
-    // time, and at most two full rounds of workgroups (no partial third round)
-    auto splits = [&](int64_t M, int64_t N) {
-      const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-      int64_t s = std::max<int64_t>(1, 512 / tiles);
-      s = std::min<int64_t>(s, std::max<int64_t>(1, p->n_tok / 512));
-      return (int)s;
-    };
-    p->wgrad_splits_qkv = splits(3 * C, C);
-    p->wgrad_splits_proj = splits(C, C);
-    auto chunk = [&](int s) {
-      int64_t c = (p->n_tok + s - 1) / s;
-      return (c + 63) / 64 * 64;
-    };
-    p->wgrad_chunk_qkv = chunk(p->wgrad_splits_qkv);
-    p->wgrad_chunk_proj = chunk(p->wgrad_splits_proj);
+    wgrad_split(p->n_tok, 3 * C, C, &p->wgrad_splits_qkv, &p->wgrad_chunk_qkv);
+    wgrad_split(p->n_tok, C, C, &p->wgrad_splits_proj, &p->wgrad_chunk_proj);
     p->bwd_do = align256(nt * C * 2);
     p->bwd_dqkv = align256(nt * 3 * C * 2);
     p->bwd_wt = align256((C * C + 3 * C * C) * 2);

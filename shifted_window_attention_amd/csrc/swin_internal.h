@@ -96,6 +96,25 @@ hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* 
                            float* db_qkv, float* dw_proj, float* db_proj, float* dtable, void* ws,
                            hipStream_t s);
 
+// Swin block pieces
+typedef __bf16 bf16_t;
+hipError_t launch_proj_fwd_res_bf16(const swin_attn_plan* p, const void* o, const void* w, const void* b,
+                                    const void* res, void* y, hipStream_t s);
+hipError_t launch_rows_gemm_bf16(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb, int64_t M, int N, int K,
+                                 const bf16_t* bias, int mode, bf16_t* out, bf16_t* out2, const bf16_t* aux,
+                                 const bf16_t* res, hipStream_t s);
+hipError_t launch_wgrad_bf16(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb, int64_t T, int M, int N,
+                             int splits, int64_t chunk, float* part, float* dw, float* db, hipStream_t s);
+hipError_t launch_transpose_bf16(const void* in, void* out, int R, int Cn, hipStream_t s);
+hipError_t launch_layernorm_fwd(const bf16_t* x, const bf16_t* g, const bf16_t* b, bf16_t* y, float* mean, float* rstd,
+                                int64_t rows, int C, float eps, hipStream_t s);
+hipError_t launch_layernorm_bwd(const bf16_t* dy, const bf16_t* x, const float* mean, const float* rstd,
+                                const bf16_t* g, const bf16_t* dres, bf16_t* dx, float* part, float* dg, float* db,
+                                int64_t rows, int C, hipStream_t s);
+int layernorm_groups(int64_t rows);
+// split-K count and chunk for a token contraction with an M x N output (plan helper)
+void wgrad_split(int64_t n_tok, int64_t M, int64_t N, int* splits, int64_t* chunk);
+
 // fp32 path (forward only)
 hipError_t launch_fwd_f32(const swin_attn_plan* p, const void* x, const void* w_qkv, const void* b_qkv,
                           const void* w_proj, const void* b_proj, const float* table, void* y, void* saved,

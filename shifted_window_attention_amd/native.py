@@ -1,4 +1,5 @@
-"""ctypes declarations of the C ABI (include/swin_attn.h) and argument marshalling.
+"""ctypes declarations of the C ABI (include/swin_attn.h, include/swin_block.h) and argument
+marshalling.
 
 Functions take torch tensors (device memory, already allocated by the caller)
 and pass their data pointers and the current HIP stream to the library.
@@ -42,6 +43,22 @@ class SwinAttnStats(ctypes.Structure):
         return {f: int(getattr(self, f)) for f, _ in self._fields_}
 
 
+class SwinBlockDesc(ctypes.Structure):
+    _fields_ = [("attn", SwinAttnDesc), ("hidden", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+
+
+_BLOCK_PARAM_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_proj", "b_proj", "bias_table", "ln2_g", "ln2_b", "w1",
+                       "b1", "w2", "b2")
+
+
+class SwinBlockParams(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in _BLOCK_PARAM_FIELDS]
+
+
+class SwinBlockGrads(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in _BLOCK_PARAM_FIELDS]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libswinattn.so is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
@@ -62,6 +79,11 @@ def _load():
         "swin_window_scatter": (st, [vp, vp, vp, vp]),
         "swin_attn_trace_events": (st, [P(vp), st]),
         "swin_attn_trace_cursor": (st, []),
+        "swin_block_plan_create": (st, [P(SwinBlockDesc), P(vp)]),
+        "swin_block_plan_destroy": (None, [vp]),
+        "swin_block_sizes": (st, [vp, P(sz), P(sz), P(sz)]),
+        "swin_block_fwd": (st, [vp, vp, P(SwinBlockParams), vp, vp, vp, sz, vp]),
+        "swin_block_bwd": (st, [vp, vp, vp, P(SwinBlockParams), vp, vp, P(SwinBlockGrads), vp, sz, vp]),
         "swin_status_string": (ctypes.c_char_p, [st]),
         "swin_attn_last_error": (ctypes.c_char_p, []),
     }
@@ -189,6 +211,88 @@ def swin_window_gather(plan, x, xw, stream=None):
 
 def swin_window_scatter(plan, yw, y, stream=None):
     _check(lib.swin_window_scatter(plan, _ptr(yw), _ptr(y), _stream(stream)), "swin_window_scatter")
+
+
+def make_block_desc(attn_desc, hidden=0, ln_eps=0.0):
+    d = SwinBlockDesc()
+    d.attn = attn_desc
+    d.hidden = int(hidden)
+    d.ln_eps = float(ln_eps)
+    return d
+
+
+def _struct_of(cls, tensors):
+    """tensors: a mapping from field name to a tensor or None (NULL)."""
+    unknown = set(tensors) - set(_BLOCK_PARAM_FIELDS)
+    if unknown:
+        raise KeyError("unknown block fields: %s" % sorted(unknown))
+    s = cls()
+    for f in _BLOCK_PARAM_FIELDS:
+        t = tensors.get(f)
+        setattr(s, f, None if t is None else t.data_ptr())
+    return s
+
+
+def swin_block_plan_create(desc):
+    h = ctypes.c_void_p()
+    _check(lib.swin_block_plan_create(ctypes.byref(desc), ctypes.byref(h)), "swin_block_plan_create")
+    return h
+
+
+def swin_block_plan_destroy(plan):
+    lib.swin_block_plan_destroy(plan)
+
+
+def swin_block_sizes(plan):
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.swin_block_sizes(plan, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "swin_block_sizes")
+    return a.value, b.value, c.value
+
+
+def swin_block_fwd(plan, x, params, y, saved, ws=None, stream=None):
+    """params: mapping from field name (ln1_g, ..., b2) to a device tensor or None."""
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    prm = _struct_of(SwinBlockParams, params)
+    _check(lib.swin_block_fwd(plan, _ptr(x), ctypes.byref(prm), _ptr(y), _ptr(saved), _ptr(ws), ws_bytes,
+                              _stream(stream)), "swin_block_fwd")
+
+
+def swin_block_bwd(plan, dy, x, params, saved, dx, grads, ws, stream=None):
+    """params as for swin_block_fwd; grads: the same names mapped to fp32 device tensors (None: NULL)."""
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    prm = _struct_of(SwinBlockParams, params)
+    grd = _struct_of(SwinBlockGrads, grads)
+    _check(lib.swin_block_bwd(plan, _ptr(dy), _ptr(x), ctypes.byref(prm), _ptr(saved), _ptr(dx), ctypes.byref(grd),
+                              _ptr(ws), ws_bytes, _stream(stream)), "swin_block_bwd")
+
+
+class BlockPlan:
+    """Owns a block plan handle; allocates its saved state and backward workspace with torch on request."""
+
+    def __init__(self, desc, device="cuda"):
+        import torch
+        self.desc = desc
+        self.handle = swin_block_plan_create(desc)
+        self.fwd_ws, self.bwd_ws, self.saved_bytes = swin_block_sizes(self.handle)
+        self.device = device
+        self._torch = torch
+
+    def alloc_saved(self):
+        return self._torch.empty(max(self.saved_bytes, 1), dtype=self._torch.uint8, device=self.device)
+
+    def alloc_bwd_ws(self):
+        return self._torch.empty(max(self.bwd_ws, 1), dtype=self._torch.uint8, device=self.device)
+
+    def close(self):
+        if self.handle is not None:
+            swin_block_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class Plan:

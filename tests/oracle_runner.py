@@ -158,3 +158,32 @@ def chain_masked_dy(cfg, inp, last_windows, dy_masked):
                        "table": g1.table}
     res["dx_tokens"], res["dx"] = _tokens_of_windows(l1, S1f), g1.dxw[slots1f]
     return res
+
+
+def block_params_of(m, e):
+    """Oracle parameters of one Swin block: attention module m, extras e (layer norms, MLP)."""
+    from oracle import block_oracle as BO
+    return BO.BlockParams(ln1_g=e.ln1_g, ln1_b=e.ln1_b, attn=params_of(m), ln2_g=e.ln2_g, ln2_b=e.ln2_b,
+                          w1=e.w1, b1=e.b1, w2=e.w2, b2=e.b2)
+
+
+def block_chain_full(cfg, inp, extras, with_bwd=True):
+    """The chained Swin blocks (one per shift of cfg) forward, then backward in reverse."""
+    from oracle import block_oracle as BO
+    lays = layouts(cfg)
+    ps = [block_params_of(m, e) for m, e in zip(inp.modules, extras)]
+    xs = [inp.x]
+    for p, lay in zip(ps, lays):
+        y, _ = BO.block_fwd(xs[-1], p, lay, cfg.heads)
+        xs.append(y)
+    out = {"y": xs[-1], "xs": xs}
+    if with_bwd:
+        d = inp.dy
+        grads = [None] * len(ps)
+        for i in reversed(range(len(ps))):
+            g = BO.block_bwd(d, xs[i], ps[i], lays[i], cfg.heads)
+            d = g.pop("dx")
+            grads[i] = g
+        out["dx"] = d
+        out["grads"] = grads
+    return out

@@ -12,7 +12,8 @@ from workloads import get_config
 from workloads.configs import ORDER
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "swin_attn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -22,16 +23,39 @@ def native():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(swin_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(swin_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_entry_points():
     names = declared_functions()
     for must in ("swin_attn_fwd", "swin_attn_bwd", "swin_window_gather", "swin_window_scatter",
-                 "swin_attn_plan_create", "swin_attn_plan_destroy", "swin_attn_sizes", "swin_status_string"):
+                 "swin_attn_plan_create", "swin_attn_plan_destroy", "swin_attn_sizes", "swin_status_string",
+                 "swin_block_plan_create", "swin_block_plan_destroy", "swin_block_sizes", "swin_block_fwd",
+                 "swin_block_bwd"):
         assert must in names
+
+
+def test_block_plan_rejects_unsupported_descriptors(native):
+    """Block descriptor checks that run before any device work: fp32, a hidden width that is not a
+    multiple of 64, more than 1024 channels and a negative epsilon are refused with a status."""
+    cfg = get_config(ORDER[0])
+    base = _desc(native, cfg, dtype="bf16")
+    bad = [(native.make_block_desc(_desc(native, cfg, dtype="f32")), 2),
+           (native.make_block_desc(base, hidden=96), 2),
+           (native.make_block_desc(base, ln_eps=-1.0), 1)]
+    wide = _desc(native, cfg, dtype="bf16")
+    wide.channels = 1088
+    wide.heads = 17
+    bad.append((native.make_block_desc(wide), 2))
+    for d, want in bad:
+        h = ctypes.c_void_p()
+        st = native.lib.swin_block_plan_create(ctypes.byref(d), ctypes.byref(h))
+        assert st == want, (st, native.lib.swin_attn_last_error())
+        assert not h.value
 
 
 def test_library_exports_every_declared_symbol(native):
