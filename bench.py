@@ -269,6 +269,70 @@ def time_shard_share(hip, N, stream, base_cfg, steps, warmup):
     return res
 
 
+def time_block_chain(hip, N, stream, cfg, steps, warmup, hidden_mult=4):
+    """Two Swin blocks (W-MSA block, then SW-MSA block: layer norms, attention module, GELU MLP of
+    hidden width 4C, residuals) forward and backward on the full grid, inputs and weights drawn on
+    the device. FLOPs: the attention module's products plus the two MLP products (4 T C H per
+    block forward, twice that backward); layer norms, GELU and residual adds are not counted."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    C = cfg.channels
+    H = hidden_mult * C
+    T = cfg.n_tokens
+
+    def rnd(*shape, scale=1.0, dtype=torch.bfloat16):
+        return (torch.randn(*shape, device="cuda", generator=g) * scale).to(dtype)
+    blocks = []
+    for i, shift in enumerate(cfg.shifts):
+        desc = N.make_desc(cfg.batch, cfg.grid, C, cfg.heads, cfg.window, shift, cfg.periodic, N.SWIN_BF16)
+        plan = N.BlockPlan(N.make_block_desc(desc, hidden=H))
+        prm = {"ln1_g": 1 + rnd(C, scale=0.1), "ln1_b": rnd(C, scale=0.1),
+               "w_qkv": rnd(3 * C, C, scale=(2.0 / (4 * C)) ** 0.5), "b_qkv": rnd(3 * C, scale=0.1),
+               "w_proj": rnd(C, C, scale=(1.0 / C) ** 0.5), "b_proj": rnd(C, scale=0.1),
+               "bias_table": rnd(*cfg.bias_table_shape(), scale=0.02, dtype=torch.float32),
+               "ln2_g": 1 + rnd(C, scale=0.1), "ln2_b": rnd(C, scale=0.1),
+               "w1": rnd(H, C, scale=(2.0 / (C + H)) ** 0.5), "b1": rnd(H, scale=0.1),
+               "w2": rnd(C, H, scale=(2.0 / (C + H)) ** 0.5), "b2": rnd(C, scale=0.1)}
+        grads = {k: torch.empty(v.shape, dtype=torch.float32, device="cuda") for k, v in prm.items()}
+        blocks.append((plan, prm, grads, plan.alloc_saved(), plan.alloc_bwd_ws()))
+    shape = (cfg.batch,) + tuple(cfg.grid) + (C,)
+    x = rnd(*shape)
+    dy = rnd(*shape)
+    y1, y2, dx2, dx1 = (torch.empty_like(x) for _ in range(4))
+
+    def step():
+        (p1, w1, g1, s1, ws1), (p2, w2, g2, s2, ws2) = blocks
+        N.swin_block_fwd(p1.handle, x, w1, y1, s1, stream=stream)
+        N.swin_block_fwd(p2.handle, y1, w2, y2, s2, stream=stream)
+        N.swin_block_bwd(p2.handle, dy, y1, w2, s2, dx2, g2, ws2, stream=stream)
+        N.swin_block_bwd(p1.handle, dx2, x, w1, s1, dx1, g1, ws1, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = hip.events(2)
+    assert hip.l.hipEventRecord(t0, stream.cuda_stream) == 0
+    for _ in range(steps):
+        step()
+    assert hip.l.hipEventRecord(t1, stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(t0, t1) / steps
+    hip.destroy([t0, t1])
+    flops = 0
+    for plan, *_ in blocks:
+        st = N.swin_attn_host_stats(plan.desc.attn)
+        f, _ = stage_flops_bytes(cfg, st["allowed_pairs"])
+        flops += sum(f.values()) + 3 * 4 * T * C * H
+    res = {"hidden": H, "steps": steps, "ms_per_step": round(ms, 4),
+           "tokens_per_s": round(T * len(blocks) / (ms * 1e-3), 1), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "mfma_peak_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "algorithmic_gflop_per_step": round(flops / 1e9, 2)}
+    for plan, *_ in blocks:
+        plan.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -414,6 +478,10 @@ def main():
 
     moves = time_window_moves(hip, N, mods[1].plan.handle, x, stream, cfg)
     shard = time_shard_share(hip, N, stream, cfg, max(1, args.steps // 2), max(1, args.warmup // 2))
+    # the activations of the attention chain are no longer needed: free them before the blocks
+    del mods, grads, y1, y2, dx2, dx1
+    torch.cuda.empty_cache()
+    block = time_block_chain(hip, N, stream, cfg, max(1, args.steps // 5), max(1, args.warmup // 5))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -432,7 +500,8 @@ def main():
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "algorithmic_gflop_per_step": round(flops_step / 1e9, 2),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "roofline": roof, "kernels": kernels, "window_moves": moves, "shard_share_8way": shard, "cpu_baseline": cpu,
+        "roofline": roof, "kernels": kernels, "window_moves": moves, "shard_share_8way": shard,
+        "swin_block_chain": block, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

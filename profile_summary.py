@@ -10,7 +10,9 @@
       profiles/traffic_540x1080_c512.md.
 
 Kernels launched more than once per step with different shapes (the two GEMM kernels) are
-told apart by their position in the step's fixed launch order.
+told apart by their position in the step's fixed launch order: within the attention chain
+(every dispatch before the first stand-alone window move, which bench.py times after the chain) and
+within the Swin-block chain (from the first layer-norm dispatch on).
 """
 import argparse
 import csv
@@ -28,6 +30,11 @@ sys.path.insert(0, ROOT)
 NT_ROLES = ["qkv_gemm", "proj_gemm", "qkv_gemm", "proj_gemm", "dproj_gemm", "dgrad_qkv", "dproj_gemm", "dgrad_qkv"]
 TN_ROLES = ["wgrad_proj", "wgrad_qkv", "wgrad_proj", "wgrad_qkv"]
 SINGLE = {"k_attn_fwd": "attn_fwd", "k_attn_bwd": "attn_bwd"}
+# the same for one step of the two-block chain (block 0 fwd, block 1 fwd, block 1 bwd, block 0 bwd)
+NT_BLOCK_ROLES = (["qkv_gemm", "proj_res_gemm", "mlp_w1_gelu", "mlp_w2_res"] * 2 +
+                  ["mlp_dgelu", "mlp_dxn", "dproj_gemm", "dgrad_qkv"] * 2)
+TN_BLOCK_ROLES = ["wgrad_w2", "wgrad_w1", "wgrad_proj", "wgrad_qkv"] * 2
+BLOCK_START = "k_layernorm_fwd"
 SOURCES = {"k_gemm_nt": "gemm.hip", "k_gemm_tn": "gemm.hip", "k_attn_fwd": "attn_fwd.hip",
            "k_attn_bwd": "attn_bwd.hip"}
 COPY = "k_window_move<true>"
@@ -66,17 +73,69 @@ def cmd_trace(a):
         lines.append("| %s | %s | %.1f | %.1f | %.1f | %.2f | %.1f |" % (
             short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    bj = None
     if a.bench_json and os.path.exists(a.bench_json):
         txt = open(a.bench_json).read().strip().splitlines()
-        if txt:
-            b = json.loads(txt[-1])
-            lines += ["", "bench.py line of the same run: %.3f ms/step, %.1f TFLOP/s (%.1f%% of bf16 MFMA peak)" % (
-                b["ms_per_step"], b["tflops"], 100 * b["mfma_peak_frac"]), "",
-                "| stage | avg ms per launch (HIP events) |", "|---|---|"]
-            for k, v in b["kernels"].items():
-                lines.append("| %s | %.4f |" % (k, v["avg_ms"]))
+        bj = json.loads(txt[-1]) if txt else None
+    roles = trace_roles(find(a.dir, "kernel_trace.csv"))
+    chain_avg = {}
+    for phase, title in (("chain", "attention chain (W-MSA -> SW-MSA modules), every dispatch incl. warmup"),
+                         ("block", "Swin-block chain (W-MSA block -> SW-MSA block, MLP 4C), incl. warmup")):
+        keys = [k for k in roles if k[0] == phase]
+        if not keys:
+            continue
+        lines += ["", "Per stage, %s (kernel_trace.csv, labelled by launch order):" % title, "",
+                  "| stage | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for k in sorted(keys, key=lambda k: -sum(roles[k])):
+            v = roles[k]
+            if phase == "chain":
+                chain_avg[k[1]] = sum(v) / len(v) / 1e6
+            lines.append("| %s | %d | %.1f | %.1f | %.1f |" % (k[1], len(v), sum(v) / len(v) / 1e3, min(v) / 1e3,
+                                                               max(v) / 1e3))
+    if bj:
+        b = bj
+        lines += ["", "bench.py line of the same run: %.3f ms/step, %.1f TFLOP/s (%.1f%% of bf16 MFMA peak)" % (
+            b["ms_per_step"], b["tflops"], 100 * b["mfma_peak_frac"]), "",
+            "| stage | avg ms per launch (HIP events, timed steps) | avg ms per dispatch (trace, all chain steps) |",
+            "|---|---|---|"]
+        for k, v in b["kernels"].items():
+            t = chain_avg.get(k)
+            lines.append("| %s | %.4f | %s |" % (k, v["avg_ms"], "%.4f" % t if t is not None else "-"))
+        if b.get("swin_block_chain"):
+            bc = b["swin_block_chain"]
+            lines += ["", "Swin-block chain: %.3f ms/step, %.1f TFLOP/s (%.1f%% of bf16 MFMA peak)" % (
+                bc["ms_per_step"], bc["tflops"], 100 * bc["mfma_peak_frac"])]
     open(a.out, "w").write("\n".join(lines) + "\n")
     print("wrote", a.out)
+
+
+def trace_roles(path):
+    """Per-dispatch durations from kernel_trace.csv, labelled by phase and role:
+    {("chain" | "block", role): [ns, ...]} in dispatch order."""
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    out = defaultdict(list)
+    phase, seq = "chain", defaultdict(int)
+    for r in rows:
+        b = base(r["Kernel_Name"])
+        if phase == "chain" and b == "k_window_move":
+            phase = "moves"
+        if phase != "block" and b == BLOCK_START:
+            phase, seq = "block", defaultdict(int)
+        if phase == "moves":
+            continue
+        ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if b == "k_gemm_nt":
+            roles = NT_ROLES if phase == "chain" else NT_BLOCK_ROLES
+            role = roles[seq[b] % len(roles)]
+        elif b == "k_gemm_tn":
+            roles = TN_ROLES if phase == "chain" else TN_BLOCK_ROLES
+            role = roles[seq[b] % len(roles)]
+        else:
+            role = SINGLE.get(b, short(r["Kernel_Name"]))
+        seq[b] += 1
+        out[(phase, role)].append(ns)
+    return out
 
 
 def per_dispatch(path, counter):

@@ -69,21 +69,28 @@ __global__ __launch_bounds__(256) void k_layernorm_fwd(const bf16* __restrict__ 
 
 // Backward of k_layernorm_fwd plus a residual gradient:
 //   dx = dres + rstd (dxhat - mean(dxhat) - xhat mean(dxhat xhat)),  dxhat = dy g,
-// and, per group of LN_GROUP_ROWS rows, partial sums of dg = sum dy xhat and db = sum dy
-// (part[group][0][:] and part[group][1][:]), combined over the 4 waves in a fixed order.
-constexpr int kLnGroupRows = 256;
+// and, per workgroup (a contiguous range of `per` rows), partial sums of dg = sum dy xhat
+// and db = sum dy (part[group][0][:] and part[group][1][:]), combined over the 4 waves in a
+// fixed order. At most kLnMaxGroups workgroups, so that the final reduction stays short.
+constexpr int kLnMaxGroups = 1024;
+
+static int64_t ln_rows_per_group(int64_t rows) {
+  int64_t per = (rows + kLnMaxGroups - 1) / kLnMaxGroups;
+  per = per < 64 ? 64 : per;
+  return (per + 3) / 4 * 4;
+}
 
 template <int CH>
 __global__ __launch_bounds__(256) void k_layernorm_bwd(const bf16* __restrict__ dy, const bf16* __restrict__ x,
                                                        const float* __restrict__ mean, const float* __restrict__ rstd,
                                                        const bf16* __restrict__ g, const bf16* __restrict__ dres,
                                                        bf16* __restrict__ dx, float* __restrict__ part, int64_t rows,
-                                                       int C) {
+                                                       int64_t per, int C) {
   __shared__ float red[4][2][64 * 8 * CH];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nch = C / 8;
-  const int64_t r0 = (int64_t)blockIdx.x * kLnGroupRows;
-  const int64_t r1 = r0 + kLnGroupRows < rows ? r0 + kLnGroupRows : rows;
+  const int64_t r0 = (int64_t)blockIdx.x * per;
+  const int64_t r1 = r0 + per < rows ? r0 + per : rows;
   float gv[CH][8], dg[CH][8], db[CH][8];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
@@ -145,18 +152,29 @@ __global__ __launch_bounds__(256) void k_layernorm_bwd(const bf16* __restrict__ 
   }
 }
 
-// out[i] = sum over groups (in order) of part[g][i], i < n; the first half to dg, the second to db.
+// out[i] = sum over groups of part[g][i], i < n, in a fixed order: each of 4 waves sums the
+// groups congruent to its index mod 4 (ascending), then the 4 sums are added in wave order.
+// The first half of the n outputs goes to dg, the second to db. One workgroup per 64 outputs.
 __global__ __launch_bounds__(256) void k_reduce_groups(const float* __restrict__ part, int groups, int n,
                                                        float* __restrict__ dg, float* __restrict__ db) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + lane;
   float acc = 0.f;
-  for (int k = 0; k < groups; ++k) acc += part[(int64_t)k * n + i];
-  const int C = n / 2;
-  if (i < C)
-    dg[i] = acc;
-  else
-    db[i - C] = acc;
+  if (i < n) {
+#pragma unroll 8
+    for (int k = q; k < groups; k += 4) acc += part[(int64_t)k * n + i];
+  }
+  red[q][lane] = acc;
+  __syncthreads();
+  if (q == 0 && i < n) {
+    const float v = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    const int C = n / 2;
+    if (i < C)
+      dg[i] = v;
+    else
+      db[i - C] = v;
+  }
 }
 
 hipError_t launch_layernorm_fwd(const bf16* x, const bf16* g, const bf16* b, bf16* y, float* mean, float* rstd,
@@ -169,19 +187,23 @@ hipError_t launch_layernorm_fwd(const bf16* x, const bf16* g, const bf16* b, bf1
   return hipGetLastError();
 }
 
-int layernorm_groups(int64_t rows) { return (int)((rows + kLnGroupRows - 1) / kLnGroupRows); }
+int layernorm_groups(int64_t rows) {
+  const int64_t per = ln_rows_per_group(rows);
+  return (int)((rows + per - 1) / per);
+}
 
 hipError_t launch_layernorm_bwd(const bf16* dy, const bf16* x, const float* mean, const float* rstd, const bf16* g,
                                 const bf16* dres, bf16* dx, float* part, float* dg, float* db, int64_t rows, int C,
                                 hipStream_t s) {
   const int groups = layernorm_groups(rows);
+  const int64_t per = ln_rows_per_group(rows);
   if (C <= 512)
-    k_layernorm_bwd<1><<<groups, 256, 0, s>>>(dy, x, mean, rstd, g, dres, dx, part, rows, C);
+    k_layernorm_bwd<1><<<groups, 256, 0, s>>>(dy, x, mean, rstd, g, dres, dx, part, rows, per, C);
   else
-    k_layernorm_bwd<2><<<groups, 256, 0, s>>>(dy, x, mean, rstd, g, dres, dx, part, rows, C);
+    k_layernorm_bwd<2><<<groups, 256, 0, s>>>(dy, x, mean, rstd, g, dres, dx, part, rows, per, C);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_reduce_groups<<<(unsigned)((2 * C + 255) / 256), 256, 0, s>>>(part, groups, 2 * C, dg, db);
+  k_reduce_groups<<<(unsigned)((2 * C + 63) / 64), 256, 0, s>>>(part, groups, 2 * C, dg, db);
   return hipGetLastError();
 }
 

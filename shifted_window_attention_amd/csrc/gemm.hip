@@ -70,15 +70,35 @@ __device__ __forceinline__ bool xcd_tile(int64_t n_tiles, int nt, int64_t& mt_ou
 
 static inline unsigned xcd_grid(int64_t n_tiles) { return (unsigned)((n_tiles + 7) / 8 * 8); }
 
-// Exact GELU and its derivative (erf from the device math library).
-__device__ __forceinline__ float gelu_f(float a) { return 0.5f * a * (1.f + erff(a * 0.70710678118654752f)); }
+// Exact GELU, a Phi(a), and its derivative Phi(a) + a phi(a). erf is evaluated with
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7
+// for x >= 0, odd extension for x < 0), far below the bf16 rounding of the results; the
+// factor exp(-x^2) of that formula at x = |a|/sqrt(2) is exp(-a^2/2), which also gives phi.
+__device__ __forceinline__ void gelu_parts(float a, float& cdf, float& g) {
+  const float z = fabsf(a) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.f));
+  const float poly =
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f), -0.284496736f), 0.254829592f);
+  g = __expf(-z * z);
+  const float erf_abs = fmaf(-poly, g, 1.f);
+  cdf = 0.5f + 0.5f * (a < 0.f ? -erf_abs : erf_abs);
+}
+__device__ __forceinline__ float gelu_f(float a) {
+  float cdf, g;
+  gelu_parts(a, cdf, g);
+  return a * cdf;
+}
 __device__ __forceinline__ float gelu_grad_f(float a) {
-  return 0.5f * (1.f + erff(a * 0.70710678118654752f)) + a * 0.39894228040143268f * __expf(-0.5f * a * a);
+  float cdf, g;
+  gelu_parts(a, cdf, g);
+  return fmaf(a * 0.39894228040143268f, g, cdf);
 }
 
 // Epilogue of the element-wise modes (2, 3, and 0 with a residual): the accumulator tile
 // plus bias goes through LDS as fp32 in two halves of BM/2 rows, so the residual add or the
-// activation is applied before the single rounding to bf16; 16-byte row stores.
+// activation is applied before the single rounding to bf16; 16-byte row stores. The rows a
+// thread reads (GELU pre-activation or residual) are loaded for the whole half before the
+// LDS phase, so their latency overlaps it.
 template <int BM, int BN>
 __device__ __forceinline__ void epilogue_f32(const f32x16 (&acc)[NtCfg<BM, BN>::TM][NtCfg<BM, BN>::TN], bf16* smem,
                                              int tid, int lane, int wm, int wn, int64_t m0, int n0, int64_t M, int N,
@@ -91,9 +111,24 @@ __device__ __forceinline__ void epilogue_f32(const f32x16 (&acc)[NtCfg<BM, BN>::
   const int fr = lane & 31;
   constexpr int CH_PER_ROW = BN / 8;
   constexpr int ROW_STEP = Cfg::NT / CH_PER_ROW;
+  constexpr int ITERS = HALF / ROW_STEP;
+  static_assert(HALF % ROW_STEP == 0, "uniform copy-out loop");
   const int cc = (tid % CH_PER_ROW) * 8;
   const int n = n0 + cc;
+  const int row0 = tid / CH_PER_ROW;
+  const bf16* src = ep.mode == 3 ? ep.aux : (ep.mode == 0 ? ep.res : nullptr);
   for (int half = 0; half < 2; ++half) {
+    bf16x8 pre[ITERS];
+    if (src) {
+#pragma unroll
+      for (int it = 0; it < ITERS; ++it) {
+        const int64_t m = m0 + HALF * half + row0 + it * ROW_STEP;
+        if (m < M && n < N) {
+          const int64_t orow = (ep.mode == 0 && ep.out_rows) ? (int64_t)ep.out_rows[m] : m;
+          pre[it] = *(const bf16x8*)(src + orow * ep.ldc + n);
+        }
+      }
+    }
     if (wm == half) {
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j) {
@@ -109,8 +144,9 @@ __device__ __forceinline__ void epilogue_f32(const f32x16 (&acc)[NtCfg<BM, BN>::
       }
     }
     __syncthreads();
-#pragma unroll 2
-    for (int row = tid / CH_PER_ROW; row < HALF; row += ROW_STEP) {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int row = row0 + it * ROW_STEP;
       const int64_t m = m0 + HALF * half + row;
       if (m >= M || n >= N) continue;
       const f32x4 lo = *(const f32x4*)(Cs + row * FP + cc), hi = *(const f32x4*)(Cs + row * FP + cc + 4);
@@ -118,21 +154,19 @@ __device__ __forceinline__ void epilogue_f32(const f32x16 (&acc)[NtCfg<BM, BN>::
       const int64_t orow = (ep.mode == 0 && ep.out_rows) ? (int64_t)ep.out_rows[m] : m;
       bf16x8 o;
       if (ep.mode == 2) {
-        bf16x8 pre;
+        bf16x8 pa;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pre[e] = to_bf16(v[e]);
+          pa[e] = to_bf16(v[e]);
           o[e] = to_bf16(gelu_f(v[e]));
         }
-        *(bf16x8*)(ep.out2 + m * ep.ldc + n) = pre;
+        *(bf16x8*)(ep.out2 + m * ep.ldc + n) = pa;
       } else if (ep.mode == 3) {
-        const bf16x8 a = *(const bf16x8*)(ep.aux + m * ep.ldc + n);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = to_bf16(v[e] * gelu_grad_f(to_f32(a[e])));
+        for (int e = 0; e < 8; ++e) o[e] = to_bf16(v[e] * gelu_grad_f(to_f32(pre[it][e])));
       } else {
-        const bf16x8 r = *(const bf16x8*)(ep.res + orow * ep.ldc + n);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = to_bf16(v[e] + to_f32(r[e]));
+        for (int e = 0; e < 8; ++e) o[e] = to_bf16(v[e] + to_f32(pre[it][e]));
       }
       *(bf16x8*)(ep.out + orow * ep.ldc + n) = o;
     }
