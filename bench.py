@@ -269,6 +269,62 @@ def time_shard_share(hip, N, stream, base_cfg, steps, warmup):
     return res
 
 
+def time_offload(hip, N, stream, mods, x, dy, outs, grads, steps):
+    """The W-MSA module's saved state (q/k/v, o, LSE) sent to pinned host memory and back by the
+    offload engine: each direction alone (GB/s), and the chain step with the store issued right
+    after the W-MSA forward (overlapping the SW-MSA forward and backward) and the load issued
+    before the W-MSA backward."""
+    import torch
+    m1, m2 = mods
+    y1, y2, dx2, dx1 = outs
+    nbytes = m1.plan.saved_bytes
+    host = N.PinnedBuffer(nbytes)
+    eng = N.swin_offload_create(0)
+    ev = hip.events(2)
+    res = {"saved_bytes": nbytes}
+    for name, issue in (("store", lambda: N.swin_offload_store(eng, m1.saved, host, nbytes, after=stream)),
+                        ("load", lambda: N.swin_offload_load(eng, host, m1.saved, nbytes, after=stream))):
+        torch.cuda.synchronize()
+        assert hip.l.hipEventRecord(ev[0], stream.cuda_stream) == 0
+        t = issue()
+        N.swin_offload_wait(eng, t, stream)
+        assert hip.l.hipEventRecord(ev[1], stream.cuda_stream) == 0
+        torch.cuda.synchronize()
+        ms = hip.elapsed_ms(ev[0], ev[1])
+        res[name + "_ms"] = round(ms, 3)
+        res[name + "_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 2)
+
+    def step():
+        N.swin_attn_fwd(m1.plan.handle, x, m1.w_qkv, m1.b_qkv, m1.w_proj, m1.b_proj, m1.table, y1, m1.saved,
+                        stream=stream)
+        ts = N.swin_offload_store(eng, m1.saved, host, nbytes, after=stream)
+        N.swin_attn_fwd(m2.plan.handle, y1, m2.w_qkv, m2.b_qkv, m2.w_proj, m2.b_proj, m2.table, y2, m2.saved,
+                        stream=stream)
+        g = grads[1]
+        N.swin_attn_bwd(m2.plan.handle, dy, y1, m2.w_qkv, m2.w_proj, m2.table, m2.saved, dx2, g["w_qkv"],
+                        g["b_qkv"], g["w_proj"], g["b_proj"], g["table"], m2.ws, stream=stream)
+        N.swin_offload_wait(eng, ts, stream)
+        tl = N.swin_offload_load(eng, host, m1.saved, nbytes, after=stream)
+        N.swin_offload_wait(eng, tl, stream)
+        g = grads[0]
+        N.swin_attn_bwd(m1.plan.handle, dx2, x, m1.w_qkv, m1.w_proj, m1.table, m1.saved, dx1, g["w_qkv"],
+                        g["b_qkv"], g["w_proj"], g["b_proj"], g["table"], m1.ws, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    assert hip.l.hipEventRecord(ev[0], stream.cuda_stream) == 0
+    for _ in range(steps):
+        step()
+    assert hip.l.hipEventRecord(ev[1], stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    res["steps"] = steps
+    res["chain_ms_per_step_with_offload"] = round(hip.elapsed_ms(ev[0], ev[1]) / steps, 3)
+    hip.destroy(ev)
+    N.swin_offload_destroy(eng)
+    host.free()
+    return res
+
+
 def time_block_chain(hip, N, stream, cfg, steps, warmup, hidden_mult=4):
     """Two Swin blocks (W-MSA block, then SW-MSA block: layer norms, attention module, GELU MLP of
     hidden width 4C, residuals) forward and backward on the full grid, inputs and weights drawn on
@@ -478,6 +534,8 @@ def main():
 
     moves = time_window_moves(hip, N, mods[1].plan.handle, x, stream, cfg)
     shard = time_shard_share(hip, N, stream, cfg, max(1, args.steps // 2), max(1, args.warmup // 2))
+    offload = time_offload(hip, N, stream, mods, x, dy, (y1, y2, dx2, dx1), grads, 3)
+    offload["chain_ms_per_step"] = round(ms_step, 4)
     # the activations of the attention chain are no longer needed: free them before the blocks
     del mods, grads, y1, y2, dx2, dx1
     torch.cuda.empty_cache()
@@ -501,7 +559,7 @@ def main():
         "algorithmic_gflop_per_step": round(flops_step / 1e9, 2),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "roofline": roof, "kernels": kernels, "window_moves": moves, "shard_share_8way": shard,
-        "swin_block_chain": block, "cpu_baseline": cpu,
+        "swin_block_chain": block, "saved_offload": offload, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

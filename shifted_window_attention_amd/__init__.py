@@ -2,7 +2,8 @@
 
 A thin ctypes binding over libswinattn.so: every function here only marshals
 arguments (tensor data pointers, sizes, the current HIP stream) to the C ABI
-declared in include/swin_attn.h and include/swin_block.h, under the same names. All computation runs in
+declared in include/swin_attn.h, include/swin_block.h and include/swin_offload.h, under the
+same names. All computation runs in
 the library's HIP kernels; there is no fallback. If the library has not been
 built, importing the binding raises.
 """
@@ -16,4 +17,6 @@ from .native import (  # noqa: F401
     swin_status_string, swin_window_gather, swin_window_scatter, swin_attn_trace_events, swin_attn_trace_cursor, Plan,
     SwinBlockDesc, SwinBlockParams, SwinBlockGrads, make_block_desc, swin_block_plan_create, swin_block_plan_destroy,
     swin_block_sizes, swin_block_fwd, swin_block_bwd, BlockPlan,
+    PinnedBuffer, swin_offload_create, swin_offload_destroy, swin_offload_store, swin_offload_load, swin_offload_wait,
+    swin_offload_query, swin_offload_sync, swin_offload_bytes,
 )

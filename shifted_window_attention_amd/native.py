@@ -1,5 +1,5 @@
-"""ctypes declarations of the C ABI (include/swin_attn.h, include/swin_block.h) and argument
-marshalling.
+"""ctypes declarations of the C ABI (include/swin_attn.h, include/swin_block.h,
+include/swin_offload.h) and argument marshalling.
 
 Functions take torch tensors (device memory, already allocated by the caller)
 and pass their data pointers and the current HIP stream to the library.
@@ -84,6 +84,16 @@ def _load():
         "swin_block_sizes": (st, [vp, P(sz), P(sz), P(sz)]),
         "swin_block_fwd": (st, [vp, vp, P(SwinBlockParams), vp, vp, vp, sz, vp]),
         "swin_block_bwd": (st, [vp, vp, vp, P(SwinBlockParams), vp, vp, P(SwinBlockGrads), vp, sz, vp]),
+        "swin_offload_create": (st, [ctypes.c_int32, P(vp)]),
+        "swin_offload_destroy": (None, [vp]),
+        "swin_pinned_alloc": (st, [sz, P(vp)]),
+        "swin_pinned_free": (st, [vp]),
+        "swin_offload_store": (st, [vp, vp, vp, sz, vp, P(ctypes.c_uint64)]),
+        "swin_offload_load": (st, [vp, vp, vp, sz, vp, P(ctypes.c_uint64)]),
+        "swin_offload_wait": (st, [vp, ctypes.c_uint64, vp]),
+        "swin_offload_query": (st, [vp, ctypes.c_uint64, P(ctypes.c_int32)]),
+        "swin_offload_sync": (st, [vp]),
+        "swin_offload_bytes": (st, [vp, P(ctypes.c_uint64), P(ctypes.c_uint64)]),
         "swin_status_string": (ctypes.c_char_p, [st]),
         "swin_attn_last_error": (ctypes.c_char_p, []),
     }
@@ -293,6 +303,84 @@ class BlockPlan:
             self.close()
         except Exception:
             pass
+
+
+def _addr(p):
+    """A device tensor, a pinned-host buffer (PinnedBuffer) or a raw address -> c_void_p."""
+    if p is None:
+        return None
+    if hasattr(p, "data_ptr"):
+        return ctypes.c_void_p(p.data_ptr())
+    if isinstance(p, PinnedBuffer):
+        return ctypes.c_void_p(p.ptr)
+    return ctypes.c_void_p(int(p))
+
+
+class PinnedBuffer:
+    """Pinned host memory from swin_pinned_alloc; .array is a uint8 numpy view of it."""
+
+    def __init__(self, nbytes):
+        h = ctypes.c_void_p()
+        _check(lib.swin_pinned_alloc(nbytes, ctypes.byref(h)), "swin_pinned_alloc")
+        self.ptr = h.value
+        self.nbytes = nbytes
+        self.array = np.ctypeslib.as_array((ctypes.c_uint8 * nbytes).from_address(self.ptr))
+
+    def free(self):
+        if self.ptr:
+            self.array = None
+            _check(lib.swin_pinned_free(ctypes.c_void_p(self.ptr)), "swin_pinned_free")
+            self.ptr = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def swin_offload_create(ring=0):
+    h = ctypes.c_void_p()
+    _check(lib.swin_offload_create(int(ring), ctypes.byref(h)), "swin_offload_create")
+    return h
+
+
+def swin_offload_destroy(engine):
+    lib.swin_offload_destroy(engine)
+
+
+def swin_offload_store(engine, dev, host, nbytes, after=None):
+    t = ctypes.c_uint64()
+    _check(lib.swin_offload_store(engine, _addr(dev), _addr(host), nbytes, _stream(after), ctypes.byref(t)),
+           "swin_offload_store")
+    return t.value
+
+
+def swin_offload_load(engine, host, dev, nbytes, after=None):
+    t = ctypes.c_uint64()
+    _check(lib.swin_offload_load(engine, _addr(host), _addr(dev), nbytes, _stream(after), ctypes.byref(t)),
+           "swin_offload_load")
+    return t.value
+
+
+def swin_offload_wait(engine, ticket, stream=None):
+    _check(lib.swin_offload_wait(engine, ticket, _stream(stream)), "swin_offload_wait")
+
+
+def swin_offload_query(engine, ticket):
+    d = ctypes.c_int32()
+    _check(lib.swin_offload_query(engine, ticket, ctypes.byref(d)), "swin_offload_query")
+    return bool(d.value)
+
+
+def swin_offload_sync(engine):
+    _check(lib.swin_offload_sync(engine), "swin_offload_sync")
+
+
+def swin_offload_bytes(engine):
+    a, b = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(lib.swin_offload_bytes(engine, ctypes.byref(a), ctypes.byref(b)), "swin_offload_bytes")
+    return a.value, b.value
 
 
 class Plan:
