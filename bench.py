@@ -325,6 +325,56 @@ def time_offload(hip, N, stream, mods, x, dy, outs, grads, steps):
     return res
 
 
+def time_routes(hip, N, stream, cfg, ranks=8, reps=10):
+    """TERRA's DMP route (8 latitude stripes -> 8 Eq. 4 window ranks) and shift route (unshifted
+    -> shifted window ranks) on the full grid, all ranks on this GPU: per-rank pack, the
+    loopback exchange of every segment, per-rank restore. Algorithmic bytes: each phase reads
+    and writes every token row once (2 N C 2 B); the tokens that change rank are what a
+    multi-GPU run would send over xGMI."""
+    import numpy as np
+    import torch
+    C = cfg.channels
+    gdesc = N.make_desc(cfg.batch, cfg.grid, C, 1, cfg.window, (0, 0, 0), cfg.periodic, N.SWIN_BF16)
+    shift = cfg.shifts[-1]
+    routes = {"dmp_route": (N.make_rank_layout(0, ranks), N.make_rank_layout(1, ranks)),
+              "shift_route": (N.make_rank_layout(1, ranks), N.make_rank_layout(1, ranks, shift))}
+    res = {"ranks": ranks}
+    row = C * 2
+    for name, (src, dst) in routes.items():
+        plan = N.RoutePlan(gdesc, src, dst)
+        locs = [torch.randn(int(n), C, device="cuda").to(torch.bfloat16) for n in plan.src_sizes]
+        sends = [torch.empty_like(t) for t in locs]
+        recvs = [torch.empty(int(n), C, dtype=torch.bfloat16, device="cuda") for n in plan.dst_sizes]
+        outs = [torch.empty_like(t) for t in recvs]
+        phases = {"pack": lambda: [N.swin_route_pack(plan, p, locs[p], sends[p], stream) for p in range(plan.P)],
+                  "exchange": lambda: N.swin_route_loopback(plan, sends, recvs, stream),
+                  "unpack": lambda: [N.swin_route_unpack(plan, r, recvs[r], outs[r], stream) for r in range(plan.R)]}
+        rec = {}
+        n_tok = int(plan.src_sizes.sum())
+        for ph, fn in phases.items():
+            fn()
+            torch.cuda.synchronize()
+            ev = hip.events(2)
+            assert hip.l.hipEventRecord(ev[0], stream.cuda_stream) == 0
+            for _ in range(reps):
+                fn()
+            assert hip.l.hipEventRecord(ev[1], stream.cuda_stream) == 0
+            torch.cuda.synchronize()
+            ms = hip.elapsed_ms(ev[0], ev[1]) / reps
+            hip.destroy(ev)
+            gbs = 2 * n_tok * row / (ms * 1e-3) / 1e9
+            rec[ph] = {"ms": round(ms, 4), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        moved = int(plan.counts.sum() - np.trace(plan.counts))
+        rec["tokens_between_ranks"] = moved
+        rec["mb_between_ranks"] = round(moved * row / 1e6, 1)
+        rec["max_mb_per_rank_pair"] = round(
+            float(max(plan.counts[p, r] for p in range(plan.P) for r in range(plan.R) if p != r)) * row / 1e6, 2)
+        res[name] = rec
+        plan.close()
+        del locs, sends, recvs, outs
+    return res
+
+
 def time_block_chain(hip, N, stream, cfg, steps, warmup, hidden_mult=4):
     """Two Swin blocks (W-MSA block, then SW-MSA block: layer norms, attention module, GELU MLP of
     hidden width 4C, residuals) forward and backward on the full grid, inputs and weights drawn on
@@ -540,6 +590,7 @@ def main():
     del mods, grads, y1, y2, dx2, dx1
     torch.cuda.empty_cache()
     block = time_block_chain(hip, N, stream, cfg, max(1, args.steps // 5), max(1, args.warmup // 5))
+    routes = time_routes(hip, N, stream, cfg)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -559,7 +610,8 @@ def main():
         "algorithmic_gflop_per_step": round(flops_step / 1e9, 2),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "roofline": roof, "kernels": kernels, "window_moves": moves, "shard_share_8way": shard,
-        "swin_block_chain": block, "saved_offload": offload, "cpu_baseline": cpu,
+        "swin_block_chain": block, "saved_offload": offload,
+        "token_routes_8_ranks": routes, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

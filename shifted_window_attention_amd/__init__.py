@@ -2,8 +2,8 @@
 
 A thin ctypes binding over libswinattn.so: every function here only marshals
 arguments (tensor data pointers, sizes, the current HIP stream) to the C ABI
-declared in include/swin_attn.h, include/swin_block.h and include/swin_offload.h, under the
-same names. All computation runs in
+declared in include/swin_attn.h, include/swin_block.h, include/swin_offload.h and
+include/swin_route.h, under the same names. All computation runs in
 the library's HIP kernels; there is no fallback. If the library has not been
 built, importing the binding raises.
 """
@@ -19,4 +19,6 @@ from .native import (  # noqa: F401
     swin_block_sizes, swin_block_fwd, swin_block_bwd, BlockPlan,
     PinnedBuffer, swin_offload_create, swin_offload_destroy, swin_offload_store, swin_offload_load, swin_offload_wait,
     swin_offload_query, swin_offload_sync, swin_offload_bytes,
+    SWIN_LAYOUT_STRIPES, SWIN_LAYOUT_WINDOWS, SwinRankLayout, make_rank_layout, swin_route_host_tables, RoutePlan,
+    swin_route_pack, swin_route_unpack, swin_route_loopback,
 )

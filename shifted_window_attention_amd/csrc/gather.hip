@@ -45,27 +45,31 @@ __global__ __launch_bounds__(256) void k_window_move_u16(const uint16_t* __restr
   }
 }
 
-hipError_t launch_gather(const swin_attn_plan* p, const void* x, void* xw, bool scatter, hipStream_t s) {
-  const size_t es = p->d.dtype == SWIN_BF16 ? 2 : 4;
-  const size_t row_bytes = (size_t)p->C * es;
-  if (p->n_tok == 0) return hipSuccess;
-  if (row_bytes % 16 == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)xw % 16) == 0) {
+// Rows of row_bytes bytes: dst[i] = src[idx[i]] (gather) or dst[idx[i]] = src[i] (scatter),
+// i < n. 16-byte chunks when rows and pointers allow it, 2-byte words otherwise.
+hipError_t launch_rows_move(const void* src, void* dst, const int32_t* idx, int64_t n, size_t row_bytes, bool scatter,
+                            hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (row_bytes % 16 == 0 && ((uintptr_t)src % 16) == 0 && ((uintptr_t)dst % 16) == 0) {
     const int chunks = (int)(row_bytes / 16);
-    const unsigned blocks = (unsigned)((p->n_tok + 15) / 16);
+    const unsigned blocks = (unsigned)((n + 15) / 16);
     if (scatter)
-      k_window_move<true><<<blocks, 256, 0, s>>>((const uint4*)x, (uint4*)xw, p->dev.perm, p->n_tok, chunks);
+      k_window_move<true><<<blocks, 256, 0, s>>>((const uint4*)src, (uint4*)dst, idx, n, chunks);
     else
-      k_window_move<false><<<blocks, 256, 0, s>>>((const uint4*)x, (uint4*)xw, p->dev.perm, p->n_tok, chunks);
+      k_window_move<false><<<blocks, 256, 0, s>>>((const uint4*)src, (uint4*)dst, idx, n, chunks);
   } else {
     const int row = (int)(row_bytes / 2);
     if (scatter)
-      k_window_move_u16<true><<<(unsigned)p->n_tok, 64, 0, s>>>((const uint16_t*)x, (uint16_t*)xw, p->dev.perm,
-                                                                p->n_tok, row);
+      k_window_move_u16<true><<<(unsigned)n, 64, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, idx, n, row);
     else
-      k_window_move_u16<false><<<(unsigned)p->n_tok, 64, 0, s>>>((const uint16_t*)x, (uint16_t*)xw, p->dev.perm,
-                                                                 p->n_tok, row);
+      k_window_move_u16<false><<<(unsigned)n, 64, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, idx, n, row);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gather(const swin_attn_plan* p, const void* x, void* xw, bool scatter, hipStream_t s) {
+  const size_t es = p->d.dtype == SWIN_BF16 ? 2 : 4;
+  return launch_rows_move(x, xw, p->dev.perm, p->n_tok, (size_t)p->C * es, scatter, s);
 }
 
 }  // namespace swin

@@ -83,6 +83,8 @@ hipError_t trace_mark(hipStream_t s);
 
 // ---- kernel launchers (return hipSuccess or the launch error) ----
 hipError_t launch_gather(const swin_attn_plan* p, const void* x, void* xw, bool scatter, hipStream_t s);
+hipError_t launch_rows_move(const void* src, void* dst, const int32_t* idx, int64_t n, size_t row_bytes, bool scatter,
+                            hipStream_t s);
 
 // bf16 path
 hipError_t launch_qkv_fwd_bf16(const swin_attn_plan* p, const void* x, const void* w, const void* b,

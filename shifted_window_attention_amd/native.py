@@ -1,5 +1,5 @@
 """ctypes declarations of the C ABI (include/swin_attn.h, include/swin_block.h,
-include/swin_offload.h) and argument marshalling.
+include/swin_offload.h, include/swin_route.h) and argument marshalling.
 
 Functions take torch tensors (device memory, already allocated by the caller)
 and pass their data pointers and the current HIP stream to the library.
@@ -59,6 +59,26 @@ class SwinBlockGrads(ctypes.Structure):
     _fields_ = [(f, ctypes.c_void_p) for f in _BLOCK_PARAM_FIELDS]
 
 
+SWIN_LAYOUT_STRIPES = 0
+SWIN_LAYOUT_WINDOWS = 1
+
+
+class SwinRankLayout(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("ranks", ctypes.c_int32), ("shift", ctypes.c_int32 * 3)]
+
+
+def make_rank_layout(kind, ranks, shift=(0, 0, 0)):
+    lay = SwinRankLayout()
+    lay.kind = int(kind)
+    lay.ranks = int(ranks)
+    shift = tuple(int(v) for v in shift)
+    if len(shift) == 2:
+        shift = (0,) + shift
+    for a in range(3):
+        lay.shift[a] = shift[a]
+    return lay
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libswinattn.so is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
@@ -94,6 +114,14 @@ def _load():
         "swin_offload_query": (st, [vp, ctypes.c_uint64, P(ctypes.c_int32)]),
         "swin_offload_sync": (st, [vp]),
         "swin_offload_bytes": (st, [vp, P(ctypes.c_uint64), P(ctypes.c_uint64)]),
+        "swin_route_plan_create": (st, [P(SwinAttnDesc), P(SwinRankLayout), P(SwinRankLayout), P(vp)]),
+        "swin_route_plan_destroy": (None, [vp]),
+        "swin_route_counts": (st, [vp, P(ctypes.c_int64), P(ctypes.c_int64), P(ctypes.c_int64)]),
+        "swin_route_host_tables": (st, [P(SwinAttnDesc), P(SwinRankLayout), P(SwinRankLayout), P(ctypes.c_int64),
+                                        P(ctypes.c_int32), P(ctypes.c_int32)]),
+        "swin_route_pack": (st, [vp, ctypes.c_int32, vp, vp, vp]),
+        "swin_route_unpack": (st, [vp, ctypes.c_int32, vp, vp, vp]),
+        "swin_route_loopback": (st, [vp, P(vp), P(vp), vp]),
         "swin_status_string": (ctypes.c_char_p, [st]),
         "swin_attn_last_error": (ctypes.c_char_p, []),
     }
@@ -381,6 +409,70 @@ def swin_offload_bytes(engine):
     a, b = ctypes.c_uint64(), ctypes.c_uint64()
     _check(lib.swin_offload_bytes(engine, ctypes.byref(a), ctypes.byref(b)), "swin_offload_bytes")
     return a.value, b.value
+
+
+def _i64p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def _i32p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def swin_route_host_tables(grid_desc, src, dst):
+    """(counts [P, R], send_src [N_tok], recv_dst [N_tok]) of a route, computed on the host."""
+    st = SwinAttnStats()
+    d = SwinAttnDesc.from_buffer_copy(grid_desc)
+    d.shift[0] = d.shift[1] = d.shift[2] = 0
+    _check(lib.swin_attn_host_stats(ctypes.byref(d), ctypes.byref(st)), "swin_attn_host_stats")
+    n = st.n_tokens
+    counts = np.empty((src.ranks, dst.ranks), dtype=np.int64)
+    send = np.empty(n, dtype=np.int32)
+    recv = np.empty(n, dtype=np.int32)
+    _check(lib.swin_route_host_tables(ctypes.byref(grid_desc), ctypes.byref(src), ctypes.byref(dst), _i64p(counts),
+                                      _i32p(send), _i32p(recv)), "swin_route_host_tables")
+    return counts, send, recv
+
+
+class RoutePlan:
+    """Owns a route plan handle and its sizes."""
+
+    def __init__(self, grid_desc, src, dst):
+        h = ctypes.c_void_p()
+        _check(lib.swin_route_plan_create(ctypes.byref(grid_desc), ctypes.byref(src), ctypes.byref(dst),
+                                          ctypes.byref(h)), "swin_route_plan_create")
+        self.handle = h
+        self.P, self.R = src.ranks, dst.ranks
+        self.counts = np.empty((self.P, self.R), dtype=np.int64)
+        self.src_sizes = np.empty(self.P, dtype=np.int64)
+        self.dst_sizes = np.empty(self.R, dtype=np.int64)
+        _check(lib.swin_route_counts(h, _i64p(self.counts), _i64p(self.src_sizes), _i64p(self.dst_sizes)),
+               "swin_route_counts")
+
+    def close(self):
+        if self.handle is not None:
+            lib.swin_route_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def swin_route_pack(plan, p, local, send, stream=None):
+    _check(lib.swin_route_pack(plan.handle, int(p), _ptr(local), _ptr(send), _stream(stream)), "swin_route_pack")
+
+
+def swin_route_unpack(plan, r, recv, local, stream=None):
+    _check(lib.swin_route_unpack(plan.handle, int(r), _ptr(recv), _ptr(local), _stream(stream)), "swin_route_unpack")
+
+
+def swin_route_loopback(plan, sends, recvs, stream=None):
+    s_arr = (ctypes.c_void_p * len(sends))(*[None if t is None else t.data_ptr() for t in sends])
+    r_arr = (ctypes.c_void_p * len(recvs))(*[None if t is None else t.data_ptr() for t in recvs])
+    _check(lib.swin_route_loopback(plan.handle, s_arr, r_arr, _stream(stream)), "swin_route_loopback")
 
 
 class Plan:
