@@ -245,6 +245,7 @@ static const fwd_launcher kFwd[17] = {nullptr,          launch_one<1>,  launch_o
 
 hipError_t launch_attn_fwd_bf16(const swin_attn_plan* p, const void* qkv, const float* table, void* o, float* lse,
                                 hipStream_t s) {
+  if (p->tiled) return launch_tiled_fwd_bf16(p, qkv, table, o, lse, s);
   AttnArgs a{};
   a.qkv = (const bf16*)qkv;
   a.table = table;

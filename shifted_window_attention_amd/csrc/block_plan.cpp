@@ -160,6 +160,7 @@ swin_status swin_block_bwd(const swin_block_plan* plan, const void* dy, const vo
       !gr->w1 || !gr->w2)
     return fail(SWIN_ERR_ARG, "NULL gradient pointer");
   if (dx == dy || dx == x) return fail(SWIN_ERR_ARG, "dx must not alias dy or x");
+  if (plan->attn->tiled) return fail(SWIN_ERR_UNSUPPORTED, "tiled backward is not available yet");
   if (plan->attn->stats.max_tokens > 16 * swin::kMaxBwdTiles)
     return fail(SWIN_ERR_UNSUPPORTED, "backward supports windows of at most 160 tokens");
   if (!ws || ws_bytes < plan->w_total) return fail(SWIN_ERR_WORKSPACE, "backward workspace too small");

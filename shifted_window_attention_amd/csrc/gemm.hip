@@ -341,10 +341,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_nt(const bf16* __restrict__ A, 
 #pragma unroll
         for (int e = 0; e < 8; ++e) dot += to_f32(v[e]) * to_f32(ov[it][e]);
       }
-      // the 4 chunks of one (row, head) sit in 4 consecutive lanes (head_dim 32)
-      dot += __shfl_xor(dot, 1);
-      dot += __shfl_xor(dot, 2);
-      if (valid && (tid & 3) == 0) ep.dot_out[dot_head + m] = dot * ep.dot_scale;
+      // the hd/8 chunks of one (row, head) sit in hd/8 consecutive lanes (head_dim <= 128)
+      for (int sh = 1; sh < ep.hd / 8; sh <<= 1) dot += __shfl_xor(dot, sh);
+      if (valid && (tid & (ep.hd / 8 - 1)) == 0) ep.dot_out[dot_head + m] = dot * ep.dot_scale;
     }
   }
 }

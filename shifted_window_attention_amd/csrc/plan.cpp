@@ -80,16 +80,24 @@ void wgrad_split(int64_t n_tok, int64_t M, int64_t N, int* splits, int64_t* chun
   *chunk = (c + 63) / 64 * 64;
 }
 
-static swin_status check_kernel_support(const swin_attn_desc* d, int64_t max_tokens) {
+// Which kernels serve the descriptor: the one-tile bf16 path (head_dim 32, windows of up to
+// 256 tokens, tables of up to 2048 bins), the tiled bf16 path (head_dim 32, 64 or 128, any
+// window), or the fp32 forward path.
+static swin_status check_kernel_support(const swin_attn_desc* d, int64_t max_tokens, bool* tiled) {
   const int hd = d->channels / d->heads;
-  if (max_tokens > 16 * kMaxFwdTiles)
-    return fail(SWIN_ERR_UNSUPPORTED, "windows of more than 256 tokens are not supported");
   const int64_t nbins = int64_t(2 * d->window[0] - 1) * (2 * d->window[1] - 1) * (2 * d->window[2] - 1);
-  if (nbins > kMaxBins) return fail(SWIN_ERR_UNSUPPORTED, "relative-position table larger than 2048 bins per head");
+  *tiled = false;
   if (d->dtype == SWIN_BF16) {
-    if (hd != 32) return fail(SWIN_ERR_UNSUPPORTED, "bf16 kernels need head_dim == 32");
+    if (hd != 32 && hd != 64 && hd != 128)
+      return fail(SWIN_ERR_UNSUPPORTED, "bf16 kernels need head_dim 32, 64 or 128");
     if (d->channels % 64 != 0) return fail(SWIN_ERR_UNSUPPORTED, "bf16 kernels need channels % 64 == 0");
+    *tiled = hd != 32 || max_tokens > 16 * kMaxFwdTiles || nbins > kMaxBins;
+    if (*tiled && nbins >= (int64_t(1) << 24))
+      return fail(SWIN_ERR_UNSUPPORTED, "relative-position table of 2^24 bins or more per head");
   } else {
+    if (max_tokens > 16 * kMaxFwdTiles)
+      return fail(SWIN_ERR_UNSUPPORTED, "fp32 windows of more than 256 tokens are not supported");
+    if (nbins > kMaxBins) return fail(SWIN_ERR_UNSUPPORTED, "relative-position table larger than 2048 bins per head");
     if (hd > 64) return fail(SWIN_ERR_UNSUPPORTED, "fp32 kernels need head_dim <= 64");
     if (2 * max_tokens * hd * 4 > 160 * 1024)
       return fail(SWIN_ERR_UNSUPPORTED, "fp32 window K/V tiles exceed the 160 KB of LDS");
@@ -211,6 +219,7 @@ static void free_dev(swin_attn_plan* p) {
     hipFree(p->dev.classes);
     hipFree(p->dev.fwd_work);
     hipFree(p->dev.bwd_work);
+    hipFree(p->dev.tiled_work);
     if (cur >= 0) (void)hipSetDevice(cur);
   }
   p->dev = DevTables{};
@@ -303,12 +312,14 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
   if (st != SWIN_OK) return st;
   HostLayout L;
   build_layout(desc, L);
-  st = check_kernel_support(desc, L.stats.max_tokens);
+  bool tiled = false;
+  st = check_kernel_support(desc, L.stats.max_tokens, &tiled);
   if (st != SWIN_OK) return st;
 
   swin_attn_plan* p = new (std::nothrow) swin_attn_plan();
   if (!p) return fail(SWIN_ERR_ARG, "out of host memory");
   p->d = *desc;
+  p->tiled = tiled;
   p->n_tok = L.n_tok;
   p->n_win = L.n_win;
   p->C = desc->channels;
@@ -335,6 +346,13 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
     }
   }
   build_work(p->classes, p->nh, 1024, 64, p->fwd_work, p->fwd_ranges);
+  if (p->tiled) {
+    // one item per 64-token block of every window, windows in row-major order
+    for (int64_t w = 0; w < p->n_win; ++w) {
+      const int n = p->win_off[w + 1] - p->win_off[w];
+      for (int b = 0; b * 64 < n; ++b) p->tiled_work.push_back(WorkItem{L.win_cls[w], (int32_t)w, b, 0});
+    }
+  }
   // the backward bins its bias gradient once per work item: fewer, longer items (1 WG per CU)
   build_work(p->classes, p->nh, 1024, kMaxChunk, p->bwd_work, p->bwd_ranges);
 
@@ -354,7 +372,9 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
     const size_t part_qkv = (size_t)p->wgrad_splits_qkv * (3 * C * C + 3 * C);
     const size_t part_proj = (size_t)p->wgrad_splits_proj * (C * C + C);
     p->bwd_part = align256(std::max(part_qkv, part_proj) * 4);
-    p->bwd_dbias_part = align256(p->bwd_work.size() * (size_t)p->nh * (size_t)p->nbins * 4);
+    // dT: per-work-item partials (one-tile path) or one fixed-point accumulator (tiled path)
+    p->bwd_dbias_part = p->tiled ? align256((size_t)p->nh * (size_t)p->nbins * 8)
+                                 : align256(p->bwd_work.size() * (size_t)p->nh * (size_t)p->nbins * 4);
     p->bwd_dd = align256(nt * (size_t)p->nh * 4);
     p->bwd_total = p->bwd_do + p->bwd_dqkv + p->bwd_wt + p->bwd_part + p->bwd_dbias_part + p->bwd_dd;
   }
@@ -366,6 +386,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
   if (e == hipSuccess) e = upload(&p->dev.classes, p->classes);
   if (e == hipSuccess) e = upload(&p->dev.fwd_work, p->fwd_work);
   if (e == hipSuccess) e = upload(&p->dev.bwd_work, p->bwd_work);
+  if (e == hipSuccess && p->tiled) e = upload(&p->dev.tiled_work, p->tiled_work);
   if (e != hipSuccess) {
     set_error(std::string("plan upload failed: ") + hipGetErrorString(e));
     free_dev(p);
@@ -452,8 +473,11 @@ swin_status swin_attn_bwd(const swin_attn_plan* plan, const void* dy, const void
   if (!dy || !x || !w_qkv || !w_proj || !bias_table || !saved || !dx || !dw_qkv || !dw_proj || !dbias_table)
     return fail(SWIN_ERR_ARG, "NULL input or output pointer");
   if (dx == dy || dx == x) return fail(SWIN_ERR_ARG, "dx must not alias dy or x");
-  if (plan->stats.max_tokens > 16 * kMaxBwdTiles)
+  if (!plan->tiled && plan->stats.max_tokens > 16 * kMaxBwdTiles)
     return fail(SWIN_ERR_UNSUPPORTED, "backward supports windows of at most 160 tokens");
+  if (plan->tiled) return fail(SWIN_ERR_UNSUPPORTED, "tiled backward is not available yet");
+  if (plan->tiled && plan->nbins > kTiledMaxBwdBins)
+    return fail(SWIN_ERR_UNSUPPORTED, "tiled backward supports relative-position tables of at most 8192 bins");
   if (!ws || ws_bytes < plan->bwd_total) return fail(SWIN_ERR_WORKSPACE, "backward workspace too small");
   return hip_status(launch_bwd_bf16(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_qkv, dw_proj,
                                     db_proj, dbias_table, ws, (hipStream_t)stream),

@@ -42,6 +42,7 @@ constexpr int kMaxFwdTiles = 16;  // forward: windows of up to 256 tokens
 constexpr int kMaxBwdTiles = 10;  // backward: windows of up to 160 tokens (LDS budget)
 constexpr int kMaxChunk = 64;     // windows per attention work item
 constexpr int kMaxBins = 2048;    // bias-table bins per head (windows of <= 256 tokens have < 2048)
+constexpr int kTiledMaxBwdBins = 8192;  // tiled backward: bias-gradient bins per head held in LDS
 
 struct DevTables {
   int32_t* perm = nullptr;       // [n_tok] window-major slot -> grid row
@@ -50,6 +51,7 @@ struct DevTables {
   ClassInfo* classes = nullptr;  // [n_cls]
   WorkItem* fwd_work = nullptr;  // [n_fwd_work]
   WorkItem* bwd_work = nullptr;  // [n_bwd_work]
+  WorkItem* tiled_work = nullptr;  // [n_tiled_work] (class, window, 64-token block) of the tiled path
 };
 
 }  // namespace swin
@@ -66,6 +68,8 @@ struct swin_attn_plan {
   std::vector<swin::ClassInfo> classes;
   std::vector<swin::WorkItem> fwd_work, bwd_work;
   std::vector<swin::WorkRange> fwd_ranges, bwd_ranges;
+  bool tiled = false;                      // bf16 windows over 256 tokens, head_dim 64/128, large tables
+  std::vector<swin::WorkItem> tiled_work;
   swin::DevTables dev;
   // workspace / saved-state layout (bytes)
   size_t saved_qkv = 0, saved_o = 0, saved_lse = 0, saved_total = 0;
@@ -116,6 +120,10 @@ hipError_t launch_layernorm_bwd(const bf16_t* dy, const bf16_t* x, const float* 
 int layernorm_groups(int64_t rows);
 // split-K count and chunk for a token contraction with an M x N output (plan helper)
 void wgrad_split(int64_t n_tok, int64_t M, int64_t N, int* splits, int64_t* chunk);
+
+// tiled path (any window size, head_dim 32/64/128)
+hipError_t launch_tiled_fwd_bf16(const swin_attn_plan* p, const void* qkv, const float* table, void* o, float* lse,
+                                 hipStream_t s);
 
 // fp32 path (forward only)
 hipError_t launch_fwd_f32(const swin_attn_plan* p, const void* x, const void* w_qkv, const void* b_qkv,

@@ -137,10 +137,13 @@ def test_descriptor_errors(native):
 def test_plan_create_rejects_before_touching_the_device(native):
     UNSUP = 2
     h = ctypes.c_void_p()
-    d = native.make_desc(1, (1, 8, 8), 128, 2, (1, 4, 4), (0, 2, 2))   # head_dim 64 in bf16
+    d = native.make_desc(1, (1, 8, 8), 64, 4, (1, 4, 4), (0, 2, 2))   # head_dim 16 in bf16
     assert native.lib.swin_attn_plan_create(ctypes.byref(d), ctypes.byref(h)) == UNSUP
     assert h.value is None
-    d = native.make_desc(1, (1, 32, 32), 64, 2, (1, 17, 16), (0, 0, 0))   # 272-token windows
+    assert b"head_dim" in native.lib.swin_attn_last_error()
+    d = native.make_desc(1, (1, 8, 8), 96, 1, (1, 4, 4), (0, 2, 2))   # head_dim 96 in bf16
+    assert native.lib.swin_attn_plan_create(ctypes.byref(d), ctypes.byref(h)) == UNSUP
+    d = native.make_desc(1, (1, 32, 32), 64, 2, (1, 17, 16), (0, 0, 0), dtype=native.SWIN_F32)  # 272 tokens, fp32
     assert native.lib.swin_attn_plan_create(ctypes.byref(d), ctypes.byref(h)) == UNSUP
     assert b"256" in native.lib.swin_attn_last_error()
 
