@@ -361,40 +361,48 @@ hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* 
                           dw_proj, db_proj, s);
   if (e == hipSuccess) e = trace_mark(s);
   if (e != hipSuccess) return e;
-  // attention core backward
-  BwdArgs a{};
-  a.qkv = qkv;
-  a.o = o;
-  a.lse = lse;
-  a.dO = dO;
-  a.dd = dd;
-  a.table = table;
-  a.dqkv = dqkv;
-  a.perm = p->dev.perm;
-  a.dbias_part = dbias_part;
-  a.classes = p->dev.classes;
-  a.class_win = p->dev.class_win;
-  a.win_off = p->dev.win_off;
-  a.n_tok = p->n_tok;
-  a.nh = p->nh;
-  a.C = C;
-  a.nbins = p->nbins;
-  for (int i = 0; i < 3; ++i) a.win[i] = p->d.window[i];
-  a.tau = p->tau;
-  const size_t dyn = 2 * (size_t)p->nbins * sizeof(float);
-  for (const auto& r : p->bwd_ranges) {
-    a.work = p->dev.bwd_work + r.begin;
-    a.item_base = r.begin;
-    kBwd[r.nqt](a, r.count, p->nh, dyn, s);
+  if (p->tiled_bwd) {
+    // windows over 160 tokens, wider heads or large tables: the tiled kernels; dT goes through
+    // a fixed-point accumulator held where the one-tile path keeps its partials
+    e = launch_tiled_bwd_bf16(p, qkv, lse, dO, dd, table, dqkv, (unsigned long long*)dbias_part, dtable, s);
+    if (e == hipSuccess) e = trace_mark(s);
+    if (e == hipSuccess) e = trace_mark(s);
+  } else {
+    // attention core backward
+    BwdArgs a{};
+    a.qkv = qkv;
+    a.o = o;
+    a.lse = lse;
+    a.dO = dO;
+    a.dd = dd;
+    a.table = table;
+    a.dqkv = dqkv;
+    a.perm = p->dev.perm;
+    a.dbias_part = dbias_part;
+    a.classes = p->dev.classes;
+    a.class_win = p->dev.class_win;
+    a.win_off = p->dev.win_off;
+    a.n_tok = p->n_tok;
+    a.nh = p->nh;
+    a.C = C;
+    a.nbins = p->nbins;
+    for (int i = 0; i < 3; ++i) a.win[i] = p->d.window[i];
+    a.tau = p->tau;
+    const size_t dyn = 2 * (size_t)p->nbins * sizeof(float);
+    for (const auto& r : p->bwd_ranges) {
+      a.work = p->dev.bwd_work + r.begin;
+      a.item_base = r.begin;
+      kBwd[r.nqt](a, r.count, p->nh, dyn, s);
+    }
+    e = hipGetLastError();
+    if (e == hipSuccess) e = trace_mark(s);
+    if (e != hipSuccess) return e;
+    const int per_item = p->nh * p->nbins;
+    k_dbias_reduce<<<(unsigned)((per_item + 255) / 256), 256, 0, s>>>(dbias_part, (int)p->bwd_work.size(), per_item,
+                                                                       dtable);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = trace_mark(s);
   }
-  e = hipGetLastError();
-  if (e == hipSuccess) e = trace_mark(s);
-  if (e != hipSuccess) return e;
-  const int per_item = p->nh * p->nbins;
-  k_dbias_reduce<<<(unsigned)((per_item + 255) / 256), 256, 0, s>>>(dbias_part, (int)p->bwd_work.size(), per_item,
-                                                                     dtable);
-  e = hipGetLastError();
-  if (e == hipSuccess) e = trace_mark(s);
   if (e != hipSuccess) return e;
   // QKV backward: dx = scatter(dqkv W_qkv), dW_qkv = dqkv^T gather(x), db_qkv
   e = launch_dgrad_qkv_bf16(p, dqkv, wqkvT, dx, s);

@@ -13,6 +13,15 @@
 // V^T operand comes from the transposing LDS read); the row sums come from the matrix core
 // (an all-ones operand against the same bf16 P). Bias + mask come from the tokens' local
 // offset codes and the head's relative-position table in global memory.
+//
+// Backward (recomputing P from q, k and the saved LSE; dS = P (dP - D), D = rowsum(dO o)):
+//   k_tiled_bwd_dkv: one workgroup per (window, block of 64 keys, head), a wave per 16 keys;
+//     query blocks (q, dO, LSE, -D, codes) stream through LDS; dV^T += dO^T P and
+//     dK^T += q^T dS accumulate in registers; dT is binned per workgroup in LDS as 64-bit
+//     fixed point (2^-32 units), then added to a global fixed-point accumulator. Integer sums
+//     do not depend on the order of the additions, so dT is bitwise reproducible.
+//   k_tiled_bwd_dq: one workgroup per (window, block of 64 queries, head), the forward's
+//     layout: key blocks stream through LDS and dQ^T += K^T dS^T.
 #include "device_common.h"
 #include "swin_internal.h"
 
@@ -40,8 +49,9 @@ struct TiledArgs {
   float tau;
 };
 
-// Token codes of keys past the window's end: a wrap label no real token has, so every pair
-// with them is masked.
+// Token codes of tokens past the window's end: a wrap label no real token has, so every pair
+// of such a token with a real one is masked. Two padding tokens share the label, so the
+// kernels also mask on the query's or key's own validity where both can be padding.
 constexpr int kPadCode = 0x7f << 24;
 
 template <int HD>
@@ -160,7 +170,7 @@ __global__ __launch_bounds__(256, 2) void k_tiled_fwd(TiledArgs a) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) asm volatile("" : "+v"(s[kt]));
+    for (int kt = 0; kt < 4; ++kt) asm volatile("" : "+v"(s[kt]) : : "memory");
     if (kb + 1 < nkb) {
       TiledBuf<HD>& nx = sm.buf[(kb + 1) & 1];
       tiled_stage<HD>(Kh, Vh, off, n, kb + 1, wv, lane, ci, a.win, nx.k, nx.v, nx.codes);
@@ -224,6 +234,346 @@ __global__ __launch_bounds__(256, 2) void k_tiled_fwd(TiledArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------------------
+constexpr float kFix = 4294967296.f;  // 2^32: fixed-point scale of the dT accumulator
+
+template <int HD>
+struct TiledQBuf {
+  unsigned char q[HD / 32][kTB * 64];
+  unsigned char d[HD / 32][kTB * 64];  // dO
+  float lse[kTB];
+  float nd[kTB];                       // -D
+  int codes[kTB];
+};
+
+// All of the dK/dV kernel's LDS is one static object: with one object the compiler leaves the
+// ordering of the direct-to-LDS copies against LDS reads to the explicit waits.
+template <int HD>
+struct DkvSmem {
+  TiledQBuf<HD> buf[2];
+  unsigned long long bins[kTiledMaxBwdBins];
+};
+
+// dQ: the forward's structure with lse fixed; dP^T = V dO^T starts from -D.
+template <int HD>
+__global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
+  constexpr int NSUB = HD / 32;
+  __shared__ __attribute__((aligned(1024))) TiledFwdSmem<HD> sm;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, li = lane & 15;
+  const WorkItem wk = a.work[blockIdx.x];
+  const int h = blockIdx.y;
+  const ClassInfo ci = a.classes[wk.cls];
+  const int n = ci.n;
+  const int64_t off = a.win_off[wk.first];
+  const int q = wk.count * kTB + 16 * wv + li;
+  const bool qv = q < n;
+  const int qc = qv ? q : n - 1;
+  const size_t plane = (size_t)a.nh * a.n_tok * HD;
+  const bf16* Qh = a.qkv + (size_t)h * a.n_tok * HD;
+  const bf16* Kh = Qh + plane;
+  const bf16* Vh = Kh + plane;
+  const bf16* dOh = a.dO + (size_t)h * a.n_tok * HD;
+  const float* tab = a.table + (int64_t)h * a.nbins;
+  const int code0 = code0_of(a.win);
+  const int cq = token_code(qc, ci.ext, ci.split, a.win);
+  const int nkb = (n + kTB - 1) / kTB;
+
+  tiled_stage<HD>(Kh, Vh, off, n, 0, wv, lane, ci, a.win, sm.buf[0].k, sm.buf[0].v, sm.buf[0].codes);
+  bf16x8 bq[NSUB], bd[NSUB];
+#pragma unroll
+  for (int c = 0; c < NSUB; ++c) {
+    bq[c] = *(const bf16x8*)(Qh + (off + qc) * HD + 32 * c + 8 * g);
+    bd[c] = *(const bf16x8*)(dOh + (off + qc) * HD + 32 * c + 8 * g);
+  }
+  float lse_q = a.lse[(int64_t)h * a.n_tok + off + qc];
+  float nd_q = a.dd[(int64_t)h * a.n_tok + off + qc];
+  vm_wait(0);
+#pragma unroll
+  for (int c = 0; c < NSUB; ++c) asm volatile("" : "+v"(bq[c]), "+v"(bd[c]));
+  asm volatile("" : "+v"(lse_q), "+v"(nd_q));
+
+  const int kq_off = li * 64 + 16 * (g ^ swz(li));
+  const int vr = 4 * g + (li >> 2);
+  const int kt_off0 = swz_off(vr, 4 * (li & 3)), kt_off1 = swz_off(vr, 16 + 4 * (li & 3));
+  f32x4 dqacc[HD / 16];
+#pragma unroll
+  for (int d = 0; d < HD / 16; ++d) dqacc[d] = f32x4{};
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    vm_wait(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const TiledBuf<HD>& cur = sm.buf[kb & 1];
+    f32x4 s[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int4 ck = *(const int4*)(cur.codes + 16 * kt + 4 * g);
+      const int kk[4] = {ck.x, ck.y, ck.z, ck.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float b = tiled_bias(cq, kk[i], code0, tab);
+        s[kt][i] = qv ? b : -INFINITY;  // queries past n: P = 0, nothing flows back
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) asm volatile("" : "+v"(s[kt]) : : "memory");
+    if (kb + 1 < nkb) {
+      TiledBuf<HD>& nx = sm.buf[(kb + 1) & 1];
+      tiled_stage<HD>(Kh, Vh, off, n, kb + 1, wv, lane, ci, a.win, nx.k, nx.v, nx.codes);
+    }
+    f32x4 ds[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int c = 0; c < NSUB; ++c) s[kt] = mfma16(*(const bf16x8*)(cur.k[c] + kq_off + 1024 * kt), bq[c], s[kt]);
+      f32x4 dp = {nd_q, nd_q, nd_q, nd_q};
+#pragma unroll
+      for (int c = 0; c < NSUB; ++c) dp = mfma16(*(const bf16x8*)(cur.v[c] + kq_off + 1024 * kt), bd[c], dp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ds[kt][i] = fast_exp2(s[kt][i] - lse_q) * dp[i];
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      bf16x8 db;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        db[i] = to_bf16(ds[2 * cc][i]);
+        db[4 + i] = to_bf16(ds[2 * cc + 1][i]);
+      }
+#pragma unroll
+      for (int sc = 0; sc < NSUB; ++sc) {
+        bf16x8 k0, k1;
+        tile_frag_tr2_at(cur.k[sc] + 2048 * cc, kt_off0, kt_off1, k0, k1);
+        dqacc[2 * sc] = mfma16(k0, db, dqacc[2 * sc]);
+        dqacc[2 * sc + 1] = mfma16(k1, db, dqacc[2 * sc + 1]);
+      }
+    }
+  }
+  if (qv) {
+    const int64_t grow = a.perm[off + q];
+    bf16* row = a.dqkv + grow * 3 * a.C + (int64_t)h * HD;
+#pragma unroll
+    for (int sc = 0; sc < NSUB; ++sc) {
+      bf16x4 o0, o1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o0[i] = to_bf16(dqacc[2 * sc][i] * a.tau);
+        o1[i] = to_bf16(dqacc[2 * sc + 1][i] * a.tau);
+      }
+      *(bf16x4*)(row + 32 * sc + 4 * g) = o0;
+      *(bf16x4*)(row + 32 * sc + 16 + 4 * g) = o1;
+    }
+  }
+}
+
+// Copies query block qb of q and dO (rows past n repeat row n-1) and its LSE, -D and codes.
+template <int HD>
+__device__ __forceinline__ void tiled_stage_q(const TiledArgs& a, const bf16* Qh, const bf16* dOh, int h, int64_t off,
+                                              int n, int qb, int wv, int lane, const ClassInfo& ci,
+                                              TiledQBuf<HD>& b) {
+  tiled_stage<HD>(Qh, dOh, off, n, qb, wv, lane, ci, a.win, b.q, b.d, nullptr);
+  if (wv == 1) {
+    const int qq = qb * kTB + lane;
+    const int qs = qq < n ? qq : n - 1;
+    // LSE and -D of the block's queries: straight into LDS, one dword per lane
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.lse + (int64_t)h * a.n_tok + off + qs),
+                                     (__attribute__((address_space(3))) void*)b.lse, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.dd + (int64_t)h * a.n_tok + off + qs),
+                                     (__attribute__((address_space(3))) void*)b.nd, 4, 0, 0);
+  }
+  if (wv == 0) {
+    const int qq = qb * kTB + lane;
+    b.codes[lane] = qq < n ? token_code(qq, ci.ext, ci.split, a.win) : kPadCode;
+  }
+}
+
+// 64-bit integer add to LDS, as inline assembly: the compiler treats its own LDS atomics as
+// possibly aliasing direct-to-LDS copies in flight and would wait for those copies first.
+// The bins are touched only by these additions, by the zeroing before the first barrier and
+// by the read-out after an explicit LDS wait and a barrier.
+__device__ __forceinline__ void lds_add_u64(unsigned long long* p, uint64_t v) {
+  asm volatile("ds_add_u64 %0, %1" : : "v"(lds_addr(p)), "v"(v));
+}
+
+template <int HD>
+__global__ __launch_bounds__(256, 1) void k_tiled_bwd_dkv(TiledArgs a) {
+  constexpr int NSUB = HD / 32;
+  __shared__ __attribute__((aligned(1024))) DkvSmem<HD> sm;
+  TiledQBuf<HD>* buf = sm.buf;
+  unsigned long long* bins = sm.bins;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, li = lane & 15;
+  const WorkItem wk = a.work[blockIdx.x];
+  const int h = blockIdx.y;
+  const ClassInfo ci = a.classes[wk.cls];
+  const int n = ci.n;
+  const int64_t off = a.win_off[wk.first];
+  const int k = wk.count * kTB + 16 * wv + li;  // window-local key of this lane
+  const bool kv = k < n;
+  const int kc = kv ? k : n - 1;
+  const size_t plane = (size_t)a.nh * a.n_tok * HD;
+  const bf16* Qh = a.qkv + (size_t)h * a.n_tok * HD;
+  const bf16* Kh = Qh + plane;
+  const bf16* Vh = Kh + plane;
+  const bf16* dOh = a.dO + (size_t)h * a.n_tok * HD;
+  const float* tab = a.table + (int64_t)h * a.nbins;
+  const int code0 = code0_of(a.win);
+  // keys past n take the padding code: every pair masked, nothing accumulated
+  const int ck = kv ? token_code(k, ci.ext, ci.split, a.win) : kPadCode;
+  const int nqb = (n + kTB - 1) / kTB;
+
+  for (int i = threadIdx.x; i < a.nbins; i += 256) bins[i] = 0ull;
+  tiled_stage_q<HD>(a, Qh, dOh, h, off, n, 0, wv, lane, ci, buf[0]);
+  // the lane's key and value: B operands of S = q K^T and dP = dO V^T
+  bf16x8 bk[NSUB], bv[NSUB];
+#pragma unroll
+  for (int c = 0; c < NSUB; ++c) {
+    bk[c] = *(const bf16x8*)(Kh + (off + kc) * HD + 32 * c + 8 * g);
+    bv[c] = *(const bf16x8*)(Vh + (off + kc) * HD + 32 * c + 8 * g);
+  }
+  vm_wait(0);
+#pragma unroll
+  for (int c = 0; c < NSUB; ++c) asm volatile("" : "+v"(bk[c]), "+v"(bv[c]));
+
+  const int qk_off = li * 64 + 16 * (g ^ swz(li));
+  const int vr = 4 * g + (li >> 2);
+  const int t_off0 = swz_off(vr, 4 * (li & 3)), t_off1 = swz_off(vr, 16 + 4 * (li & 3));
+  f32x4 dkacc[HD / 16], dvacc[HD / 16];
+#pragma unroll
+  for (int d = 0; d < HD / 16; ++d) {
+    dkacc[d] = f32x4{};
+    dvacc[d] = f32x4{};
+  }
+
+  for (int qb = 0; qb < nqb; ++qb) {
+    vm_wait(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const TiledQBuf<HD>& cur = buf[qb & 1];
+    // S = q K^T + bias: lane = key li, rows = queries 16 qt + 4 g + i
+    // all 16 table reads are issued before any is used
+    int cqs[16];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      const int4 cqv = *(const int4*)(cur.codes + 16 * qt + 4 * g);
+      cqs[4 * qt] = cqv.x;
+      cqs[4 * qt + 1] = cqv.y;
+      cqs[4 * qt + 2] = cqv.z;
+      cqs[4 * qt + 3] = cqv.w;
+    }
+    float tv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) tv[j] = tab[(cqs[j] & 0xffffff) - (ck & 0xffffff) + code0];
+    f32x4 s[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * qt + i;
+        // a padding key and a padding query share the padding label: mask on kv as well
+        s[qt][i] = (!kv || (cqs[j] >> 24) != (ck >> 24)) ? -INFINITY : tv[j] * kLog2e;
+      }
+    // the block's LSE and -D are read before the next block's copies are issued as well
+    f32x4 lsv[4], ndv[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      lsv[qt] = *(const f32x4*)(cur.lse + 16 * qt + 4 * g);
+      ndv[qt] = *(const f32x4*)(cur.nd + 16 * qt + 4 * g);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) asm volatile("" : "+v"(s[qt]), "+v"(lsv[qt]), "+v"(ndv[qt]) : : "memory");
+    if (qb + 1 < nqb) tiled_stage_q<HD>(a, Qh, dOh, h, off, n, qb + 1, wv, lane, ci, buf[(qb + 1) & 1]);
+    f32x4 p[4], ds[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+#pragma unroll
+      for (int c = 0; c < NSUB; ++c) s[qt] = mfma16(*(const bf16x8*)(cur.q[c] + qk_off + 1024 * qt), bk[c], s[qt]);
+      const f32x4 ls = lsv[qt];
+      f32x4 dp = ndv[qt];
+#pragma unroll
+      for (int c = 0; c < NSUB; ++c) dp = mfma16(*(const bf16x8*)(cur.d[c] + qk_off + 1024 * qt), bv[c], dp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[qt][i] = fast_exp2(s[qt][i] - ls[i]);
+        ds[qt][i] = p[qt][i] * dp[i];
+      }
+    }
+    // dT: every pair's dS into the workgroup's fixed-point bins (masked pairs add 0)
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long long v = (long long)rintf(ds[qt][i] * kFix);
+        if (v != 0) lds_add_u64(&bins[(cqs[4 * qt + i] & 0xffffff) - (ck & 0xffffff) + code0], (uint64_t)v);
+      }
+    // dV^T += dO^T P and dK^T += q^T dS: B operands are the lane's key column with the
+    // queries of two adjacent 16-query tiles
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      bf16x8 pb, db;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = to_bf16(p[2 * cc][i]);
+        pb[4 + i] = to_bf16(p[2 * cc + 1][i]);
+        db[i] = to_bf16(ds[2 * cc][i]);
+        db[4 + i] = to_bf16(ds[2 * cc + 1][i]);
+      }
+#pragma unroll
+      for (int sc = 0; sc < NSUB; ++sc) {
+        bf16x8 f0, f1;
+        tile_frag_tr2_at(cur.d[sc] + 2048 * cc, t_off0, t_off1, f0, f1);
+        dvacc[2 * sc] = mfma16(f0, pb, dvacc[2 * sc]);
+        dvacc[2 * sc + 1] = mfma16(f1, pb, dvacc[2 * sc + 1]);
+        tile_frag_tr2_at(cur.q[sc] + 2048 * cc, t_off0, t_off1, f0, f1);
+        dkacc[2 * sc] = mfma16(f0, db, dkacc[2 * sc]);
+        dkacc[2 * sc + 1] = mfma16(f1, db, dkacc[2 * sc + 1]);
+      }
+    }
+  }
+  if (kv) {
+    const int64_t grow = a.perm[off + k];
+    bf16* row = a.dqkv + grow * 3 * a.C + (int64_t)h * HD;
+    const float kscale = 1.f / kLog2e;  // q' = tau log2(e) q
+#pragma unroll
+    for (int sc = 0; sc < NSUB; ++sc) {
+      bf16x4 k0, k1, v0, v1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        k0[i] = to_bf16(dkacc[2 * sc][i] * kscale);
+        k1[i] = to_bf16(dkacc[2 * sc + 1][i] * kscale);
+        v0[i] = to_bf16(dvacc[2 * sc][i]);
+        v1[i] = to_bf16(dvacc[2 * sc + 1][i]);
+      }
+      *(bf16x4*)(row + a.C + 32 * sc + 4 * g) = k0;
+      *(bf16x4*)(row + a.C + 32 * sc + 16 + 4 * g) = k1;
+      *(bf16x4*)(row + 2 * a.C + 32 * sc + 4 * g) = v0;
+      *(bf16x4*)(row + 2 * a.C + 32 * sc + 16 + 4 * g) = v1;
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the bin additions above are inline assembly
+  __syncthreads();
+  unsigned long long* acc = a.dbias_acc + (int64_t)h * a.nbins;
+  for (int i = threadIdx.x; i < a.nbins; i += 256) {
+    const unsigned long long v = bins[i];
+    if (v) atomicAdd(acc + i, v);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fixed_zero(unsigned long long* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+
+__global__ __launch_bounds__(256) void k_fixed_to_f32(const unsigned long long* p, float* out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = (float)((double)(long long)p[i] * (1.0 / 4294967296.0));
+}
+
 static TiledArgs tiled_args(const swin_attn_plan* p) {
   TiledArgs a{};
   a.perm = p->dev.perm;
@@ -253,6 +603,43 @@ hipError_t launch_tiled_fwd_bf16(const swin_attn_plan* p, const void* qkv, const
     k_tiled_fwd<64><<<grid, 256, 0, s>>>(a);
   else
     k_tiled_fwd<128><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int HD>
+static hipError_t tiled_bwd_launch(const TiledArgs& a, unsigned items, int nh, hipStream_t s) {
+  const dim3 grid(items, (unsigned)nh);
+  k_tiled_bwd_dkv<HD><<<grid, 256, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_tiled_bwd_dq<HD><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tiled_bwd_bf16(const swin_attn_plan* p, const void* qkv, const float* lse, const void* dO,
+                                 const float* dd, const float* table, void* dqkv, unsigned long long* acc,
+                                 float* dtable, hipStream_t s) {
+  TiledArgs a = tiled_args(p);
+  a.qkv = (const bf16*)qkv;
+  a.lse = (float*)lse;
+  a.dO = (const bf16*)dO;
+  a.dd = dd;
+  a.table = table;
+  a.dqkv = (bf16*)dqkv;
+  a.dbias_acc = acc;
+  const int64_t nacc = (int64_t)p->nh * p->nbins;
+  k_fixed_zero<<<(unsigned)((nacc + 255) / 256), 256, 0, s>>>(acc, nacc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned items = (unsigned)p->tiled_work.size();
+  if (p->hd == 32)
+    e = tiled_bwd_launch<32>(a, items, p->nh, s);
+  else if (p->hd == 64)
+    e = tiled_bwd_launch<64>(a, items, p->nh, s);
+  else
+    e = tiled_bwd_launch<128>(a, items, p->nh, s);
+  if (e != hipSuccess) return e;
+  k_fixed_to_f32<<<(unsigned)((nacc + 255) / 256), 256, 0, s>>>(acc, dtable, nacc);
   return hipGetLastError();
 }
 

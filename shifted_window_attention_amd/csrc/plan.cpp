@@ -320,6 +320,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
   if (!p) return fail(SWIN_ERR_ARG, "out of host memory");
   p->d = *desc;
   p->tiled = tiled;
+  p->tiled_bwd = desc->dtype == SWIN_BF16 && (tiled || L.stats.max_tokens > 16 * kMaxBwdTiles);
   p->n_tok = L.n_tok;
   p->n_win = L.n_win;
   p->C = desc->channels;
@@ -346,7 +347,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
     }
   }
   build_work(p->classes, p->nh, 1024, 64, p->fwd_work, p->fwd_ranges);
-  if (p->tiled) {
+  if (p->tiled || p->tiled_bwd) {
     // one item per 64-token block of every window, windows in row-major order
     for (int64_t w = 0; w < p->n_win; ++w) {
       const int n = p->win_off[w + 1] - p->win_off[w];
@@ -373,7 +374,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
     const size_t part_proj = (size_t)p->wgrad_splits_proj * (C * C + C);
     p->bwd_part = align256(std::max(part_qkv, part_proj) * 4);
     // dT: per-work-item partials (one-tile path) or one fixed-point accumulator (tiled path)
-    p->bwd_dbias_part = p->tiled ? align256((size_t)p->nh * (size_t)p->nbins * 8)
+    p->bwd_dbias_part = p->tiled_bwd ? align256((size_t)p->nh * (size_t)p->nbins * 8)
                                  : align256(p->bwd_work.size() * (size_t)p->nh * (size_t)p->nbins * 4);
     p->bwd_dd = align256(nt * (size_t)p->nh * 4);
     p->bwd_total = p->bwd_do + p->bwd_dqkv + p->bwd_wt + p->bwd_part + p->bwd_dbias_part + p->bwd_dd;
@@ -386,7 +387,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
   if (e == hipSuccess) e = upload(&p->dev.classes, p->classes);
   if (e == hipSuccess) e = upload(&p->dev.fwd_work, p->fwd_work);
   if (e == hipSuccess) e = upload(&p->dev.bwd_work, p->bwd_work);
-  if (e == hipSuccess && p->tiled) e = upload(&p->dev.tiled_work, p->tiled_work);
+  if (e == hipSuccess && !p->tiled_work.empty()) e = upload(&p->dev.tiled_work, p->tiled_work);
   if (e != hipSuccess) {
     set_error(std::string("plan upload failed: ") + hipGetErrorString(e));
     free_dev(p);
@@ -473,11 +474,8 @@ swin_status swin_attn_bwd(const swin_attn_plan* plan, const void* dy, const void
   if (!dy || !x || !w_qkv || !w_proj || !bias_table || !saved || !dx || !dw_qkv || !dw_proj || !dbias_table)
     return fail(SWIN_ERR_ARG, "NULL input or output pointer");
   if (dx == dy || dx == x) return fail(SWIN_ERR_ARG, "dx must not alias dy or x");
-  if (!plan->tiled && plan->stats.max_tokens > 16 * kMaxBwdTiles)
-    return fail(SWIN_ERR_UNSUPPORTED, "backward supports windows of at most 160 tokens");
-  if (plan->tiled) return fail(SWIN_ERR_UNSUPPORTED, "tiled backward is not available yet");
-  if (plan->tiled && plan->nbins > kTiledMaxBwdBins)
-    return fail(SWIN_ERR_UNSUPPORTED, "tiled backward supports relative-position tables of at most 8192 bins");
+  if (plan->tiled_bwd && plan->nbins > kTiledMaxBwdBins)
+    return fail(SWIN_ERR_UNSUPPORTED, "backward supports relative-position tables of at most 8192 bins");
   if (!ws || ws_bytes < plan->bwd_total) return fail(SWIN_ERR_WORKSPACE, "backward workspace too small");
   return hip_status(launch_bwd_bf16(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_qkv, dw_proj,
                                     db_proj, dbias_table, ws, (hipStream_t)stream),

@@ -69,6 +69,7 @@ struct swin_attn_plan {
   std::vector<swin::WorkItem> fwd_work, bwd_work;
   std::vector<swin::WorkRange> fwd_ranges, bwd_ranges;
   bool tiled = false;                      // bf16 windows over 256 tokens, head_dim 64/128, large tables
+  bool tiled_bwd = false;                  // backward on the tiled kernels (tiled, or windows over 160 tokens)
   std::vector<swin::WorkItem> tiled_work;
   swin::DevTables dev;
   // workspace / saved-state layout (bytes)
@@ -124,6 +125,9 @@ void wgrad_split(int64_t n_tok, int64_t M, int64_t N, int* splits, int64_t* chun
 // tiled path (any window size, head_dim 32/64/128)
 hipError_t launch_tiled_fwd_bf16(const swin_attn_plan* p, const void* qkv, const float* table, void* o, float* lse,
                                  hipStream_t s);
+hipError_t launch_tiled_bwd_bf16(const swin_attn_plan* p, const void* qkv, const float* lse, const void* dO,
+                                 const float* dd, const float* table, void* dqkv, unsigned long long* acc,
+                                 float* dtable, hipStream_t s);
 
 // fp32 path (forward only)
 hipError_t launch_fwd_f32(const swin_attn_plan* p, const void* x, const void* w_qkv, const void* b_qkv,

@@ -1,9 +1,10 @@
 """Edge cases of the HIP path against the fp64 oracle (through the C ABI).
 
 Degenerate and boundary shapes of the method: a window covering the whole grid (global
-attention), one-token windows, the largest windows each pass supports (256 tokens forward,
-160 backward), axes that are all or none periodic, ragged 3-D windows, and the smallest
-channel count. Same bars as the other parity tests: max-abs 2e-2 (bf16) / 1e-5 (fp32) on
+attention), one-token windows, the largest windows of the one-tile kernels (256 tokens
+forward, 160 backward; 161-256-token windows go to the tiled backward), the backward's refusal
+of bias tables over 8192 bins, axes that are all or none periodic, ragged 3-D windows, and the
+smallest channel count. Same bars as the other parity tests: max-abs 2e-2 (bf16) / 1e-5 (fp32) on
 per-token outputs, 2e-2 * max(1, |ref|_inf) on reduced gradients."""
 import ctypes
 
@@ -81,13 +82,20 @@ def test_bf16_edge_case_vs_oracle(cfg):
     _check(cfg)
 
 
-def test_bf16_256_token_windows_forward_and_backward_refusal():
+def test_bf16_256_token_windows_forward_and_backward():
+    """256-token windows: one-tile forward, tiled backward (over 160 tokens)."""
+    cfg = _cfg("window_16x16", (1, 32, 40), (1, 16, 16), ((0, 8, 8),))
+    log("bf16 256-token windows", cfg.grid, cfg.window)
+    _check(cfg)
+
+
+def test_bf16_backward_refuses_tables_over_8192_bins():
     import torch
     from shifted_window_attention_amd import native as N
-    cfg = _cfg("window_16x16", (1, 32, 40), (1, 16, 16), ((0, 8, 8),), backward=False)
-    log("bf16 256-token windows", cfg.grid, cfg.window)
+    # global attention over 40 x 60 tokens: 79 x 119 = 9401 bins (the forward runs tiled)
+    cfg = _cfg("global_40x60", (1, 40, 60), (1, 40, 60), ((0, 0, 0),), periodic=0, backward=False)
+    log("bf16 backward refusal", cfg.grid, cfg.window)
     _check(cfg, with_bwd=False)
-    # the backward pass supports windows of at most 160 tokens and says so before launching
     inp = make_inputs(cfg)
     m = ModuleOnDevice(cfg, 0, inp.modules[0])
     x = to_dev(inp.x_dev, "bf16")
@@ -103,6 +111,7 @@ def test_bf16_256_token_windows_forward_and_backward_refusal():
     st = L.swin_attn_bwd(m.plan.handle, p(y), p(x), p(m.w_qkv), p(m.w_proj), p(m.table), p(m.saved), p(dx),
                          p(dwq), None, p(dwp), None, p(dtab), p(ws), ws.numel(), None)
     assert st == 2  # SWIN_ERR_UNSUPPORTED
+    assert b"8192" in L.swin_attn_last_error()
     torch.cuda.synchronize()
 
 

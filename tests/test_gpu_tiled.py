@@ -51,6 +51,54 @@ def _maxabs(a, b):
     return float(np.max(np.abs(np.asarray(a) - np.asarray(b))))
 
 
+def _check_grads(got, ref, label):
+    for i, (gm, rm) in enumerate(zip(got, ref)):
+        for k in ("w_qkv", "b_qkv", "w_proj", "b_proj", "table"):
+            r = np.asarray(rm[k]).reshape(-1)
+            g = np.asarray(gm[k]).reshape(-1)
+            err = float(np.abs(g - r).max())
+            bound = TOL * max(1.0, float(np.abs(r).max()))
+            log("  %s module %d d%s max-abs %.3e (bound %.3e)" % (label, i, k, err, bound))
+            assert err <= bound, (label, i, k, err, bound)
+
+
+# every forward case whose bias table fits the backward's 8192 LDS bins
+BWD_CASES = [c for c in FWD_CASES if c.name != "global2400"] + [
+    # 256-token windows with head_dim 32 (over the one-tile backward's 160 tokens)
+    cfg("w16x16", (1, 32, 48), 128, 4, (1, 16, 16), ((0, 0, 0), (0, 8, 8))),
+    # 3-D windows with 4 levels: 4 x 12 x 12 = 576 tokens, 7 x 23 x 23 = 3703 bins, batch 2
+    cfg("levels_4x12x12", (4, 24, 24), 128, 2, (4, 12, 12), ((2, 6, 6),), batch=2),
+]
+
+
+@pytest.mark.parametrize("c", BWD_CASES, ids=lambda c: c.name)
+def test_tiled_backward_vs_oracle(c):
+    log("tiled fwd+bwd", c.name, c.grid, "window", c.window, "C", c.channels, "heads", c.heads)
+    inp = make_inputs(c)
+    got = run_chain(c, inp)
+    ref = chain_full(c, inp)
+    ey, edx = _maxabs(got["y"], ref["y"]), _maxabs(got["dx"], ref["dx"])
+    log("  y max-abs %.3e  dx max-abs %.3e" % (ey, edx))
+    assert ey <= TOL and edx <= TOL
+    _check_grads(got["grads"], ref["grads"], c.name)
+
+
+def test_tiled_backward_is_deterministic():
+    import torch
+    c = BWD_CASES[0]
+    inp = make_inputs(c)
+    got = run_chain(c, inp)
+    m = got["mods"][-1]
+    x, dy = got["xs"][-2], torch.ones_like(got["xs"][-1])
+    m.fwd(x)
+    dx1, g1 = m.bwd(dy, x)
+    dx2, g2 = m.bwd(dy, x)
+    torch.cuda.synchronize()
+    assert torch.equal(dx1.view(torch.int16), dx2.view(torch.int16))
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+
+
 @pytest.mark.parametrize("c", FWD_CASES, ids=lambda c: c.name)
 def test_tiled_forward_vs_oracle(c):
     log("tiled forward", c.name, c.grid, "window", c.window, "C", c.channels, "heads", c.heads)
