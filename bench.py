@@ -375,6 +375,71 @@ def time_routes(hip, N, stream, cfg, ranks=8, reps=10):
     return res
 
 
+def time_tiled(hip, N, stream, base_cfg, steps=3):
+    """The tiled path on the same 540x1080 grid with the shape of TERRA Table V's largest model:
+    C = 1024 in 8 heads of 128, 32 x 32 windows (1024 tokens; ragged at the grid's edges, 33
+    x 17 windows), one SW-MSA module (shift 16, 16) forward and backward, inputs on the device.
+    Stage times come from the library's trace events; algorithmic FLOPs as for the chain."""
+    import numpy as np
+    import torch
+    from workloads.configs import SwinConfig
+    cfg = SwinConfig(name="w32_hd128", batch=1, grid=base_cfg.grid, channels=1024, heads=8, window=(1, 32, 32),
+                     shifts=((0, 16, 16),), dtype="bf16", backward=True, periodic=base_cfg.periodic,
+                     description="540x1080, C=1024, 8 heads x 128, 32x32 windows")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2)
+    C = cfg.channels
+    desc = N.make_desc(cfg.batch, cfg.grid, C, cfg.heads, cfg.window, cfg.shifts[0], cfg.periodic, N.SWIN_BF16)
+    plan = N.Plan(desc)
+    wq = (torch.randn(3 * C, C, device="cuda", generator=g) * (1.0 / (2 * C)) ** 0.5).to(torch.bfloat16)
+    wp = (torch.randn(C, C, device="cuda", generator=g) * (1.0 / C) ** 0.5).to(torch.bfloat16)
+    tab = torch.randn(cfg.bias_table_shape(), device="cuda", generator=g) * 0.02
+    shape = (1,) + tuple(cfg.grid) + (C,)
+    x = torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16)
+    dy = torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16)
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    saved, ws = plan.alloc_saved(), plan.alloc_bwd_ws()
+    gw = [torch.empty(3 * C, C, device="cuda"), torch.empty(C, C, device="cuda"), torch.empty_like(tab)]
+
+    def step():
+        N.swin_attn_fwd(plan.handle, x, wq, None, wp, None, tab, y, saved, stream=stream)
+        N.swin_attn_bwd(plan.handle, dy, x, wq, wp, tab, saved, dx, gw[0], None, gw[1], None, gw[2], ws,
+                        stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    per = len(FWD_STAGES) + 1 + len(BWD_STAGES) + 1
+    ev = hip.events(per * steps)
+    N.swin_attn_trace_events(ev)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    assert N.swin_attn_trace_cursor() == per * steps
+    N.swin_attn_trace_events(None)
+    dur = {st: [] for st in FWD_STAGES + BWD_STAGES}
+    k = 0
+    for _ in range(steps):
+        for stages in (FWD_STAGES, BWD_STAGES):
+            for j, st in enumerate(stages):
+                dur[st].append(hip.elapsed_ms(ev[k + j], ev[k + j + 1]))
+            k += len(stages) + 1
+    total = float(sum(np.mean(v) for v in dur.values()))
+    hip.destroy(ev)
+    f, _ = stage_flops_bytes(cfg, plan.stats["allowed_pairs"])
+    core_fwd, core_bwd = f["attn_fwd"], f["attn_bwd"]
+    res = {"config": cfg.description, "windows": int(plan.stats["n_windows"]),
+           "max_tokens": int(plan.stats["max_tokens"]), "steps": steps, "ms_per_step": round(total, 3),
+           "tflops": round(sum(f.values()) / (total * 1e-3) / 1e12, 1),
+           "mfma_peak_frac": round(sum(f.values()) / (total * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "attn_fwd_ms": round(float(np.mean(dur["attn_fwd"])), 3),
+           "attn_fwd_tflops": round(core_fwd / (np.mean(dur["attn_fwd"]) * 1e-3) / 1e12, 1),
+           "attn_bwd_ms": round(float(np.mean(dur["attn_bwd"])), 3),
+           "attn_bwd_tflops": round(core_bwd / (np.mean(dur["attn_bwd"]) * 1e-3) / 1e12, 1),
+           "stage_ms": {k2: round(float(np.mean(v)), 3) for k2, v in dur.items()}}
+    plan.close()
+    return res
+
+
 def time_block_chain(hip, N, stream, cfg, steps, warmup, hidden_mult=4):
     """Two Swin blocks (W-MSA block, then SW-MSA block: layer norms, attention module, GELU MLP of
     hidden width 4C, residuals) forward and backward on the full grid, inputs and weights drawn on
@@ -591,6 +656,7 @@ def main():
     torch.cuda.empty_cache()
     block = time_block_chain(hip, N, stream, cfg, max(1, args.steps // 5), max(1, args.warmup // 5))
     routes = time_routes(hip, N, stream, cfg)
+    tiled = time_tiled(hip, N, stream, cfg)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -611,7 +677,7 @@ def main():
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "roofline": roof, "kernels": kernels, "window_moves": moves, "shard_share_8way": shard,
         "swin_block_chain": block, "saved_offload": offload,
-        "token_routes_8_ranks": routes, "cpu_baseline": cpu,
+        "token_routes_8_ranks": routes, "tiled_w32_hd128": tiled, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
