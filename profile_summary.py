@@ -80,7 +80,9 @@ def cmd_trace(a):
     roles = trace_roles(find(a.dir, "kernel_trace.csv"))
     chain_avg = {}
     for phase, title in (("chain", "attention chain (W-MSA -> SW-MSA modules), every dispatch incl. warmup"),
-                         ("block", "Swin-block chain (W-MSA block -> SW-MSA block, MLP 4C), incl. warmup")):
+                         ("block", "Swin-block chain (W-MSA block -> SW-MSA block, MLP 4C), incl. warmup"),
+                         ("after", "token-route pack/restore and tiled-path attention kernels (their own "
+                                   "measurements), incl. warmup")):
         keys = [k for k in roles if k[0] == phase]
         if not keys:
             continue
@@ -120,9 +122,11 @@ def trace_roles(path):
         b = base(r["Kernel_Name"])
         if phase == "chain" and b == "k_window_move":
             phase = "moves"
-        if phase != "block" and b == BLOCK_START:
+        if phase not in ("block", "after") and b == BLOCK_START:
             phase, seq = "block", defaultdict(int)
-        if phase == "moves":
+        elif phase == "block" and (b == "k_window_move" or b.startswith("k_tiled")):
+            phase = "after"  # the route and tiled-path measurements that bench.py runs next
+        if phase == "moves" or (phase == "after" and not (b == "k_window_move" or b.startswith("k_tiled"))):
             continue
         ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
         if b == "k_gemm_nt":
@@ -139,26 +143,35 @@ def trace_roles(path):
 
 
 def per_dispatch(path, counter):
-    """{(kernel short name, role): [values]} in dispatch order."""
+    """{(kernel short name, role): [values]} in dispatch order, for the attention chain (every
+    dispatch before the first stand-alone window move) and for the calibration copy (the
+    window moves that bench.py times right after the chain, up to the next GEMM)."""
     rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))
     out = defaultdict(list)
     seq = defaultdict(int)
+    phase = "chain"
     for r in rows:
         name = short(r["Kernel_Name"])
         b = base(r["Kernel_Name"])
+        if phase == "chain" and b == "k_window_move":
+            phase = "moves"
+        elif phase == "moves" and b not in ("k_window_move",) and b.startswith("k_"):
+            phase = "rest"
+        if phase == "rest":
+            break
         v = float(r["Counter_Value"])
-        if b == "k_gemm_nt":
-            role = NT_ROLES[seq[b] % len(NT_ROLES)]
-        elif b == "k_gemm_tn":
-            role = TN_ROLES[seq[b] % len(TN_ROLES)]
-        elif b in SINGLE:
-            role = SINGLE[b]
+        role = None
+        if phase == "chain":
+            if b == "k_gemm_nt":
+                role = NT_ROLES[seq[b] % len(NT_ROLES)]
+            elif b == "k_gemm_tn":
+                role = TN_ROLES[seq[b] % len(TN_ROLES)]
+            elif b in SINGLE:
+                role = SINGLE[b]
+            seq[b] += 1
         elif name == COPY:
             role = "copy"
-        else:
-            role = None
-        seq[b] += 1
         if role:
             out[(name, role)].append(v)
     return out
