@@ -15,7 +15,7 @@
 // offset codes and the head's relative-position table in global memory.
 //
 // Backward (recomputing P from q, k and the saved LSE; dS = P (dP - D), D = rowsum(dO o)):
-//   k_tiled_bwd_dkv: one workgroup per (window, block of 64 keys, head), a wave per 16 keys;
+//   k_tiled_bwd_dkv: one workgroup per (window, block of 128 keys, head), a wave per 16 keys;
 //     query blocks (q, dO, LSE, -D, codes) stream through LDS; dV^T += dO^T P and
 //     dK^T += q^T dS accumulate in registers; dT is binned per workgroup in LDS as 64-bit
 //     fixed point (2^-32 units), then added to a global fixed-point accumulator. Integer sums
@@ -35,7 +35,8 @@ struct TiledArgs {
   bf16* o;                  // [n_tok][C], grid order
   const int32_t* perm;      // window-major slot -> grid row
   float* lse;               // [nh][n_tok], log2 units
-  const WorkItem* work;     // (class, window, block)
+  const WorkItem* work;     // (class, window, 64-token block)
+  const WorkItem* kv_work;  // (class, window, 128-token block): the dK/dV kernel's items
   const ClassInfo* classes;
   const int32_t* win_off;
   int64_t n_tok;
@@ -67,16 +68,18 @@ struct TiledFwdSmem {
 };
 
 // Copies rows [kb*64, kb*64 + 64) of the planes a and b of one window (rows past n repeat row
-// n-1) into the sub-tiles of buffer dst; wave wv issues HD/32 copies per plane. Threads < 64
-// also write the keys' codes.
-template <int HD>
+// n-1) into the sub-tiles of buffer dst; the 4 HD/32 copies per plane are spread over the NW
+// waves. Wave 0 also writes the keys' codes.
+template <int HD, int NW = 4>
 __device__ __forceinline__ void tiled_stage(const bf16* a, const bf16* b, int64_t off, int n, int kb, int wv,
                                             int lane, const ClassInfo& ci, const int* win, unsigned char (*da)[kTB * 64],
                                             unsigned char (*db)[kTB * 64], int* codes) {
   constexpr int NSUB = HD / 32;
+  constexpr int COPIES = 4 * NSUB;  // 1 KB copies per plane: 4 slabs of 16 rows per sub-tile
 #pragma unroll
-  for (int t = 0; t < NSUB; ++t) {
-    const int i = wv + 4 * t;
+  for (int t = 0; t < (COPIES + NW - 1) / NW; ++t) {
+    const int i = wv + NW * t;
+    if (COPIES % NW != 0 && i >= COPIES) break;  // wave-uniform
     const int c = i >> 2, j = i & 3;
     const int row = 16 * j + (lane >> 2);
     const int key = kb * kTB + row;
@@ -371,11 +374,11 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
 }
 
 // Copies query block qb of q and dO (rows past n repeat row n-1) and its LSE, -D and codes.
-template <int HD>
+template <int HD, int NW>
 __device__ __forceinline__ void tiled_stage_q(const TiledArgs& a, const bf16* Qh, const bf16* dOh, int h, int64_t off,
                                               int n, int qb, int wv, int lane, const ClassInfo& ci,
                                               TiledQBuf<HD>& b) {
-  tiled_stage<HD>(Qh, dOh, off, n, qb, wv, lane, ci, a.win, b.q, b.d, nullptr);
+  tiled_stage<HD, NW>(Qh, dOh, off, n, qb, wv, lane, ci, a.win, b.q, b.d, nullptr);
   if (wv == 1) {
     const int qq = qb * kTB + lane;
     const int qs = qq < n ? qq : n - 1;
@@ -399,8 +402,11 @@ __device__ __forceinline__ void lds_add_u64(unsigned long long* p, uint64_t v) {
   asm volatile("ds_add_u64 %0, %1" : : "v"(lds_addr(p)), "v"(v));
 }
 
+constexpr int kKvWaves = 8;  // dK/dV: 8 waves of 16 keys, so two waves share each SIMD
+
 template <int HD>
-__global__ __launch_bounds__(256, 1) void k_tiled_bwd_dkv(TiledArgs a) {
+__global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a) {
+  constexpr int NW = kKvWaves;
   constexpr int NSUB = HD / 32;
   __shared__ __attribute__((aligned(1024))) DkvSmem<HD> sm;
   TiledQBuf<HD>* buf = sm.buf;
@@ -408,12 +414,12 @@ __global__ __launch_bounds__(256, 1) void k_tiled_bwd_dkv(TiledArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, li = lane & 15;
-  const WorkItem wk = a.work[blockIdx.x];
+  const WorkItem wk = a.kv_work[blockIdx.x];
   const int h = blockIdx.y;
   const ClassInfo ci = a.classes[wk.cls];
   const int n = ci.n;
   const int64_t off = a.win_off[wk.first];
-  const int k = wk.count * kTB + 16 * wv + li;  // window-local key of this lane
+  const int k = wk.count * 16 * NW + 16 * wv + li;  // window-local key of this lane
   const bool kv = k < n;
   const int kc = kv ? k : n - 1;
   const size_t plane = (size_t)a.nh * a.n_tok * HD;
@@ -427,8 +433,8 @@ __global__ __launch_bounds__(256, 1) void k_tiled_bwd_dkv(TiledArgs a) {
   const int ck = kv ? token_code(k, ci.ext, ci.split, a.win) : kPadCode;
   const int nqb = (n + kTB - 1) / kTB;
 
-  for (int i = threadIdx.x; i < a.nbins; i += 256) bins[i] = 0ull;
-  tiled_stage_q<HD>(a, Qh, dOh, h, off, n, 0, wv, lane, ci, buf[0]);
+  for (int i = threadIdx.x; i < a.nbins; i += 64 * NW) bins[i] = 0ull;
+  tiled_stage_q<HD, NW>(a, Qh, dOh, h, off, n, 0, wv, lane, ci, buf[0]);
   // the lane's key and value: B operands of S = q K^T and dP = dO V^T
   bf16x8 bk[NSUB], bv[NSUB];
 #pragma unroll
@@ -487,7 +493,7 @@ __global__ __launch_bounds__(256, 1) void k_tiled_bwd_dkv(TiledArgs a) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) asm volatile("" : "+v"(s[qt]), "+v"(lsv[qt]), "+v"(ndv[qt]) : : "memory");
-    if (qb + 1 < nqb) tiled_stage_q<HD>(a, Qh, dOh, h, off, n, qb + 1, wv, lane, ci, buf[(qb + 1) & 1]);
+    if (qb + 1 < nqb) tiled_stage_q<HD, NW>(a, Qh, dOh, h, off, n, qb + 1, wv, lane, ci, buf[(qb + 1) & 1]);
     f32x4 p[4], ds[4];
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
@@ -558,7 +564,7 @@ __global__ __launch_bounds__(256, 1) void k_tiled_bwd_dkv(TiledArgs a) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the bin additions above are inline assembly
   __syncthreads();
   unsigned long long* acc = a.dbias_acc + (int64_t)h * a.nbins;
-  for (int i = threadIdx.x; i < a.nbins; i += 256) {
+  for (int i = threadIdx.x; i < a.nbins; i += 64 * NW) {
     const unsigned long long v = bins[i];
     if (v) atomicAdd(acc + i, v);
   }
@@ -578,6 +584,7 @@ static TiledArgs tiled_args(const swin_attn_plan* p) {
   TiledArgs a{};
   a.perm = p->dev.perm;
   a.work = p->dev.tiled_work;
+  a.kv_work = p->dev.tiled_kv_work;
   a.classes = p->dev.classes;
   a.win_off = p->dev.win_off;
   a.n_tok = p->n_tok;
@@ -607,12 +614,11 @@ hipError_t launch_tiled_fwd_bf16(const swin_attn_plan* p, const void* qkv, const
 }
 
 template <int HD>
-static hipError_t tiled_bwd_launch(const TiledArgs& a, unsigned items, int nh, hipStream_t s) {
-  const dim3 grid(items, (unsigned)nh);
-  k_tiled_bwd_dkv<HD><<<grid, 256, 0, s>>>(a);
+static hipError_t tiled_bwd_launch(const TiledArgs& a, unsigned items, unsigned kv_items, int nh, hipStream_t s) {
+  k_tiled_bwd_dkv<HD><<<dim3(kv_items, (unsigned)nh), 64 * kKvWaves, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_tiled_bwd_dq<HD><<<grid, 256, 0, s>>>(a);
+  k_tiled_bwd_dq<HD><<<dim3(items, (unsigned)nh), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -631,13 +637,13 @@ hipError_t launch_tiled_bwd_bf16(const swin_attn_plan* p, const void* qkv, const
   k_fixed_zero<<<(unsigned)((nacc + 255) / 256), 256, 0, s>>>(acc, nacc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned items = (unsigned)p->tiled_work.size();
+  const unsigned items = (unsigned)p->tiled_work.size(), kv_items = (unsigned)p->tiled_kv_work.size();
   if (p->hd == 32)
-    e = tiled_bwd_launch<32>(a, items, p->nh, s);
+    e = tiled_bwd_launch<32>(a, items, kv_items, p->nh, s);
   else if (p->hd == 64)
-    e = tiled_bwd_launch<64>(a, items, p->nh, s);
+    e = tiled_bwd_launch<64>(a, items, kv_items, p->nh, s);
   else
-    e = tiled_bwd_launch<128>(a, items, p->nh, s);
+    e = tiled_bwd_launch<128>(a, items, kv_items, p->nh, s);
   if (e != hipSuccess) return e;
   k_fixed_to_f32<<<(unsigned)((nacc + 255) / 256), 256, 0, s>>>(acc, dtable, nacc);
   return hipGetLastError();

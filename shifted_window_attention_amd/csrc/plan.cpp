@@ -220,6 +220,7 @@ static void free_dev(swin_attn_plan* p) {
     hipFree(p->dev.fwd_work);
     hipFree(p->dev.bwd_work);
     hipFree(p->dev.tiled_work);
+    hipFree(p->dev.tiled_kv_work);
     if (cur >= 0) (void)hipSetDevice(cur);
   }
   p->dev = DevTables{};
@@ -352,6 +353,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
     for (int64_t w = 0; w < p->n_win; ++w) {
       const int n = p->win_off[w + 1] - p->win_off[w];
       for (int b = 0; b * 64 < n; ++b) p->tiled_work.push_back(WorkItem{L.win_cls[w], (int32_t)w, b, 0});
+      for (int b = 0; b * 128 < n; ++b) p->tiled_kv_work.push_back(WorkItem{L.win_cls[w], (int32_t)w, b, 0});
     }
   }
   // the backward bins its bias gradient once per work item: fewer, longer items (1 WG per CU)
@@ -388,6 +390,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
   if (e == hipSuccess) e = upload(&p->dev.fwd_work, p->fwd_work);
   if (e == hipSuccess) e = upload(&p->dev.bwd_work, p->bwd_work);
   if (e == hipSuccess && !p->tiled_work.empty()) e = upload(&p->dev.tiled_work, p->tiled_work);
+  if (e == hipSuccess && !p->tiled_kv_work.empty()) e = upload(&p->dev.tiled_kv_work, p->tiled_kv_work);
   if (e != hipSuccess) {
     set_error(std::string("plan upload failed: ") + hipGetErrorString(e));
     free_dev(p);

@@ -52,6 +52,7 @@ struct DevTables {
   WorkItem* fwd_work = nullptr;  // [n_fwd_work]
   WorkItem* bwd_work = nullptr;  // [n_bwd_work]
   WorkItem* tiled_work = nullptr;  // [n_tiled_work] (class, window, 64-token block) of the tiled path
+  WorkItem* tiled_kv_work = nullptr;  // (class, window, 128-token block): the tiled dK/dV kernel
 };
 
 }  // namespace swin
@@ -70,7 +71,7 @@ struct swin_attn_plan {
   std::vector<swin::WorkRange> fwd_ranges, bwd_ranges;
   bool tiled = false;                      // bf16 windows over 256 tokens, head_dim 64/128, large tables
   bool tiled_bwd = false;                  // backward on the tiled kernels (tiled, or windows over 160 tokens)
-  std::vector<swin::WorkItem> tiled_work;
+  std::vector<swin::WorkItem> tiled_work, tiled_kv_work;
   swin::DevTables dev;
   // workspace / saved-state layout (bytes)
   size_t saved_qkv = 0, saved_o = 0, saved_lse = 0, saved_total = 0;
