@@ -72,6 +72,8 @@ swin_status place(const swin_attn_desc& g, const swin_rank_layout& L, Placement&
   }
   if (L.kind != SWIN_LAYOUT_WINDOWS) return fail(SWIN_ERR_ARG, "unknown layout kind");
   swin_attn_desc d = g;
+  d.heads = 1;
+  d.scale = 0.f;
   for (int a = 0; a < 3; ++a) d.shift[a] = L.shift[a];
   std::vector<int64_t> perm(n);
   swin_status st = swin_attn_host_index_map(&d, perm.data(), nullptr);
@@ -116,12 +118,14 @@ struct HostRoute {
   std::vector<int64_t> src_base, dst_base;     // first row of each rank in the concatenations
 };
 
+// The route uses the descriptor's ndim, dtype, batch, grid, channels, window and periodic
+// fields; heads, shift and scale are ignored, so they are neutralised before validation.
 swin_status validate_grid(const swin_attn_desc* g) {
   if (!g) return fail(SWIN_ERR_ARG, "grid descriptor is NULL");
   swin_attn_desc d = *g;
   d.shift[0] = d.shift[1] = d.shift[2] = 0;
-  if (d.heads < 1) d.heads = 1;
-  if (d.channels % d.heads != 0) d.heads = 1;
+  d.heads = 1;
+  d.scale = 0.f;
   swin_attn_stats st{};
   return swin_attn_host_stats(&d, &st);  // validates grid, window, dtype, channels, sizes
 }

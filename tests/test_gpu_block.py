@@ -59,13 +59,30 @@ BLOCK_CASES = [
     ("levels3d", dict(grid=(4, 18, 36)), None),
     # C = 1024 (two 8-channel chunks per lane in the layer-norm kernels), 32 heads
     ("om4", dict(grid=(1, 12, 24), channels=1024, heads=32), 256),
+    # head_dim 64 (the tiled attention kernels inside the block)
+    ("highres", dict(grid=(1, 24, 36), channels=256, heads=4), None),
 ]
 
 
 def _ids(v):
     if isinstance(v, dict):
-        return "x".join(map(str, v["grid"])) + ("_c%d" % v["channels"] if "channels" in v else "")
+        return "x".join(map(str, v["grid"])) + ("_c%d_h%d" % (v["channels"], v["heads"]) if "channels" in v else "")
     return str(v)
+
+
+def test_block_with_large_windows():
+    """A W->SW block pair with 16 x 16 windows (256 tokens: the tiled backward inside the block)."""
+    from workloads.configs import SwinConfig
+    cfg = SwinConfig(name="block_w16", batch=1, grid=(1, 32, 48), channels=128, heads=4, window=(1, 16, 16),
+                     shifts=((0, 0, 0), (0, 8, 8)), dtype="bf16", backward=True, periodic=4, description="block_w16")
+    log("block fwd+bwd with 256-token windows", cfg.grid)
+    inp = make_inputs(cfg)
+    extras = make_block_extras(cfg)
+    got = run_block_chain(cfg, inp, extras)
+    ref = block_chain_full(cfg, inp, extras)
+    _check_tokens(got["y"], ref["y"], "y")
+    _check_tokens(got["dx"], ref["dx"], "dx")
+    _check_grads(got["grads"], ref["grads"], cfg.name)
 
 
 @pytest.mark.parametrize("name,kw,hidden", BLOCK_CASES, ids=_ids)
