@@ -146,8 +146,13 @@ swin_status swin_attn_host_stats(const swin_attn_desc* desc, swin_attn_stats* ou
  * classes and the slot -> grid index map, and uploads them to the current
  * HIP device. Errors: SWIN_ERR_ARG for an invalid descriptor (shift >= window,
  * window > grid, C % heads != 0, ...), SWIN_ERR_UNSUPPORTED for shapes the
- * kernels do not cover (bf16 needs head_dim 32, C % 64 == 0 and at most 256
- * tokens per window), SWIN_ERR_HIP if the upload fails. *out is NULL on error.
+ * kernels do not cover (bf16: head_dim 32, 64 or 128, C % 64 == 0, windows of
+ * any size, tables of fewer than 2^24 bins per head; fp32: head_dim <= 64 and
+ * at most 256 tokens per window), SWIN_ERR_HIP if the upload fails. *out is
+ * NULL on error. Windows over 256 tokens, head_dim 64/128 and tables over
+ * 2048 bins run on tiled kernels that stream keys and values through LDS with
+ * an online softmax [TERRA VII-A: FlashAttention from w >= 32; Table V:
+ * head_dim 128].
  */
 swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** out);
 void swin_attn_plan_destroy(swin_attn_plan* plan);
@@ -197,8 +202,12 @@ swin_status swin_attn_fwd(const swin_attn_plan* plan, const void* x, const void*
  *   dbias_table  fp32 [heads, 2wd-1, 2wh-1, 2ww-1].
  * dT[h, bin] sums dS over every window and allowed pair (the inverse routes
  * carry gradients back to their sources [TERRA IV-D]); all reductions run in
- * a fixed order, so repeated calls are bitwise identical.
- * Only SWIN_BF16 is supported (SWIN_ERR_UNSUPPORTED for fp32).
+ * a fixed order (on the tiled kernels dT is summed in 2^-32 fixed point, whose
+ * integer sums do not depend on order), so repeated calls are bitwise identical.
+ * Only SWIN_BF16 is supported (SWIN_ERR_UNSUPPORTED for fp32), with relative-
+ * position tables of at most 8192 bins per head when a window has more than
+ * 160 tokens, head_dim is 64/128 or the table exceeds 2048 bins
+ * (SWIN_ERR_UNSUPPORTED otherwise).
  */
 swin_status swin_attn_bwd(const swin_attn_plan* plan, const void* dy, const void* x, const void* w_qkv,
                           const void* w_proj, const float* bias_table, const void* saved, void* dx,
