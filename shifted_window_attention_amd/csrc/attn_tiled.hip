@@ -62,9 +62,38 @@ struct TiledBuf {
   int codes[kTB];
 };
 
+// Relative-position tables of up to kTabLds bins are held in LDS as fp16 in log2 units
+// (|error| <= 2^-11 |bias|, the precision the one-tile kernels keep their bias in) with a -inf
+// entry after the last bin, and the tokens' codes are staged in an encoding that makes a
+// pair's table address one subtraction and one unsigned min:
+//   key side   K = 2 local + (label << 16),   query side   Q = 2 (local + code0) + (label << 16).
+// Q - K is twice the pair's bin when the wrap labels agree and lies outside [0, 2 nbins)
+// otherwise; padding tokens take K = kPadK and Q = kPadQ, outside as well, so
+// min(Q - K, 2 nbins) (unsigned) addresses the bin's entry or the -inf one. Larger tables are
+// read from global memory with the plain codes.
+constexpr int kTabLds = 4096;
+constexpr int kPadK = 0x40000000, kPadQ = 0x7fffffff;
+
+__device__ __forceinline__ int enc_key(int code) { return 2 * (code & 0xffffff) + ((code >> 24) << 16); }
+__device__ __forceinline__ int enc_query(int code, int code0) {
+  return 2 * ((code & 0xffffff) + code0) + ((code >> 24) << 16);
+}
+__device__ __forceinline__ float fast_bias(int Q, int K, const _Float16* tab16, uint32_t lim) {
+  const uint32_t ib = min((uint32_t)(Q - K), lim);
+  return (float)*(const _Float16*)((const char*)tab16 + ib);
+}
+
+// Fills the LDS table (bins, then -inf) when it fits; made visible by the first barrier.
+__device__ __forceinline__ void tiled_tab_fill(_Float16* dst, const float* tab, int nbins, int nthreads) {
+  if (nbins > kTabLds) return;
+  for (int i = threadIdx.x; i <= nbins; i += nthreads)
+    dst[i] = i < nbins ? (_Float16)(tab[i] * kLog2e) : (_Float16)(-INFINITY);
+}
+
 template <int HD>
 struct TiledFwdSmem {
   TiledBuf<HD> buf[2];
+  _Float16 tab[kTabLds + 8];
 };
 
 // Copies rows [kb*64, kb*64 + 64) of the planes a and b of one window (rows past n repeat row
@@ -73,7 +102,7 @@ struct TiledFwdSmem {
 template <int HD, int NW = 4>
 __device__ __forceinline__ void tiled_stage(const bf16* a, const bf16* b, int64_t off, int n, int kb, int wv,
                                             int lane, const ClassInfo& ci, const int* win, unsigned char (*da)[kTB * 64],
-                                            unsigned char (*db)[kTB * 64], int* codes) {
+                                            unsigned char (*db)[kTB * 64], int* codes, bool fast = false) {
   constexpr int NSUB = HD / 32;
   constexpr int COPIES = 4 * NSUB;  // 1 KB copies per plane: 4 slabs of 16 rows per sub-tile
 #pragma unroll
@@ -91,7 +120,10 @@ __device__ __forceinline__ void tiled_stage(const bf16* a, const bf16* b, int64_
   }
   if (codes && wv == 0) {
     const int key = kb * kTB + lane;
-    codes[lane] = key < n ? token_code(key, ci.ext, ci.split, win) : kPadCode;
+    if (fast)
+      codes[lane] = key < n ? enc_key(token_code(key, ci.ext, ci.split, win)) : kPadK;
+    else
+      codes[lane] = key < n ? token_code(key, ci.ext, ci.split, win) : kPadCode;
   }
 }
 
@@ -104,8 +136,9 @@ __device__ __forceinline__ float tiled_bias(int cq, int ck, int code0, const flo
   return (cq >> 24) != (ck >> 24) ? -INFINITY : t * kLog2e;
 }
 
-template <int HD>
-__global__ __launch_bounds__(256, 2) void k_tiled_fwd(TiledArgs a) {
+// NW waves of 16 queries: blocks of 16 NW queries share every staged key/value block.
+template <int HD, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void k_tiled_fwd(TiledArgs a) {
   constexpr int NSUB = HD / 32;
   __shared__ __attribute__((aligned(1024))) TiledFwdSmem<HD> sm;
   const int lane = threadIdx.x & 63;
@@ -116,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void k_tiled_fwd(TiledArgs a) {
   const ClassInfo ci = a.classes[wk.cls];
   const int n = ci.n;
   const int64_t off = a.win_off[wk.first];
-  const int q = wk.count * kTB + 16 * wv + li;  // window-local query of this lane
+  const int q = wk.count * 16 * NW + 16 * wv + li;  // window-local query of this lane
   const bool qv = q < n;
   const int qc = qv ? q : n - 1;
   const size_t plane = (size_t)a.nh * a.n_tok * HD;
@@ -127,8 +160,12 @@ __global__ __launch_bounds__(256, 2) void k_tiled_fwd(TiledArgs a) {
   const int code0 = code0_of(a.win);
   const int cq = token_code(qc, ci.ext, ci.split, a.win);
   const int nkb = (n + kTB - 1) / kTB;
+  const bool fast = a.nbins <= kTabLds;
+  const int qenc = qv ? enc_query(cq, code0) : kPadQ;
+  const uint32_t lim = 2u * (uint32_t)a.nbins;
 
-  tiled_stage<HD>(Kh, Vh, off, n, 0, wv, lane, ci, a.win, sm.buf[0].k, sm.buf[0].v, sm.buf[0].codes);
+  tiled_tab_fill(sm.tab, tab, a.nbins, 64 * NW);
+  tiled_stage<HD, NW>(Kh, Vh, off, n, 0, wv, lane, ci, a.win, sm.buf[0].k, sm.buf[0].v, sm.buf[0].codes, fast);
   // the lane's query: B operand of S^T = K Q^T, hd values 32 c + 8 g .. + 7
   bf16x8 bq[NSUB];
 #pragma unroll
@@ -165,10 +202,15 @@ __global__ __launch_bounds__(256, 2) void k_tiled_fwd(TiledArgs a) {
     for (int kt = 0; kt < 4; ++kt) {
       const int4 ck = *(const int4*)(cur.codes + 16 * kt + 4 * g);
       const int kk[4] = {ck.x, ck.y, ck.z, ck.w};
+      if (fast) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float b = tiled_bias(cq, kk[i], code0, tab);
-        s[kt][i] = qv ? b : 0.f;
+        for (int i = 0; i < 4; ++i) s[kt][i] = fast_bias(qenc, kk[i], sm.tab, lim);  // queries past n: -inf
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float b = tiled_bias(cq, kk[i], code0, tab);
+          s[kt][i] = qv ? b : 0.f;
+        }
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -176,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void k_tiled_fwd(TiledArgs a) {
     for (int kt = 0; kt < 4; ++kt) asm volatile("" : "+v"(s[kt]) : : "memory");
     if (kb + 1 < nkb) {
       TiledBuf<HD>& nx = sm.buf[(kb + 1) & 1];
-      tiled_stage<HD>(Kh, Vh, off, n, kb + 1, wv, lane, ci, a.win, nx.k, nx.v, nx.codes);
+      tiled_stage<HD, NW>(Kh, Vh, off, n, kb + 1, wv, lane, ci, a.win, nx.k, nx.v, nx.codes, fast);
     }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -257,6 +299,7 @@ template <int HD>
 struct DkvSmem {
   TiledQBuf<HD> buf[2];
   unsigned long long bins[kTiledMaxBwdBins];
+  _Float16 tab[kTabLds + 8];
 };
 
 // dQ: the forward's structure with lse fixed; dP^T = V dO^T starts from -D.
@@ -284,8 +327,12 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
   const int code0 = code0_of(a.win);
   const int cq = token_code(qc, ci.ext, ci.split, a.win);
   const int nkb = (n + kTB - 1) / kTB;
+  const bool fast = a.nbins <= kTabLds;
+  const int qenc = qv ? enc_query(cq, code0) : kPadQ;
+  const uint32_t lim = 2u * (uint32_t)a.nbins;
 
-  tiled_stage<HD>(Kh, Vh, off, n, 0, wv, lane, ci, a.win, sm.buf[0].k, sm.buf[0].v, sm.buf[0].codes);
+  tiled_tab_fill(sm.tab, tab, a.nbins, 256);
+  tiled_stage<HD>(Kh, Vh, off, n, 0, wv, lane, ci, a.win, sm.buf[0].k, sm.buf[0].v, sm.buf[0].codes, fast);
   bf16x8 bq[NSUB], bd[NSUB];
 #pragma unroll
   for (int c = 0; c < NSUB; ++c) {
@@ -315,10 +362,15 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
     for (int kt = 0; kt < 4; ++kt) {
       const int4 ck = *(const int4*)(cur.codes + 16 * kt + 4 * g);
       const int kk[4] = {ck.x, ck.y, ck.z, ck.w};
+      if (fast) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float b = tiled_bias(cq, kk[i], code0, tab);
-        s[kt][i] = qv ? b : -INFINITY;  // queries past n: P = 0, nothing flows back
+        for (int i = 0; i < 4; ++i) s[kt][i] = fast_bias(qenc, kk[i], sm.tab, lim);  // queries past n: -inf
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float b = tiled_bias(cq, kk[i], code0, tab);
+          s[kt][i] = qv ? b : -INFINITY;  // queries past n: P = 0, nothing flows back
+        }
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -326,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
     for (int kt = 0; kt < 4; ++kt) asm volatile("" : "+v"(s[kt]) : : "memory");
     if (kb + 1 < nkb) {
       TiledBuf<HD>& nx = sm.buf[(kb + 1) & 1];
-      tiled_stage<HD>(Kh, Vh, off, n, kb + 1, wv, lane, ci, a.win, nx.k, nx.v, nx.codes);
+      tiled_stage<HD>(Kh, Vh, off, n, kb + 1, wv, lane, ci, a.win, nx.k, nx.v, nx.codes, fast);
     }
     f32x4 ds[4];
 #pragma unroll
@@ -390,7 +442,10 @@ __device__ __forceinline__ void tiled_stage_q(const TiledArgs& a, const bf16* Qh
   }
   if (wv == 0) {
     const int qq = qb * kTB + lane;
-    b.codes[lane] = qq < n ? token_code(qq, ci.ext, ci.split, a.win) : kPadCode;
+    if (a.nbins <= kTabLds)
+      b.codes[lane] = qq < n ? enc_query(token_code(qq, ci.ext, ci.split, a.win), code0_of(a.win)) : kPadQ;
+    else
+      b.codes[lane] = qq < n ? token_code(qq, ci.ext, ci.split, a.win) : kPadCode;
   }
 }
 
@@ -432,8 +487,12 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
   // keys past n take the padding code: every pair masked, nothing accumulated
   const int ck = kv ? token_code(k, ci.ext, ci.split, a.win) : kPadCode;
   const int nqb = (n + kTB - 1) / kTB;
+  const bool fast = a.nbins <= kTabLds;
+  const int kenc = kv ? enc_key(ck) : kPadK;
+  const uint32_t lim = 2u * (uint32_t)a.nbins;
 
   for (int i = threadIdx.x; i < a.nbins; i += 64 * NW) bins[i] = 0ull;
+  tiled_tab_fill(sm.tab, tab, a.nbins, 64 * NW);
   tiled_stage_q<HD, NW>(a, Qh, dOh, h, off, n, 0, wv, lane, ci, buf[0]);
   // the lane's key and value: B operands of S = q K^T and dP = dO V^T
   bf16x8 bk[NSUB], bv[NSUB];
@@ -471,18 +530,25 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
       cqs[4 * qt + 2] = cqv.z;
       cqs[4 * qt + 3] = cqv.w;
     }
-    float tv[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) tv[j] = tab[(cqs[j] & 0xffffff) - (ck & 0xffffff) + code0];
     f32x4 s[4];
+    if (fast) {
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt)
+      for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 4 * qt + i;
-        // a padding key and a padding query share the padding label: mask on kv as well
-        s[qt][i] = (!kv || (cqs[j] >> 24) != (ck >> 24)) ? -INFINITY : tv[j] * kLog2e;
-      }
+        for (int i = 0; i < 4; ++i) s[qt][i] = fast_bias(cqs[4 * qt + i], kenc, sm.tab, lim);
+    } else {
+      float tv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) tv[j] = tab[(cqs[j] & 0xffffff) - (ck & 0xffffff) + code0];
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 4 * qt + i;
+          // a padding key and a padding query share the padding label: mask on kv as well
+          s[qt][i] = (!kv || (cqs[j] >> 24) != (ck >> 24)) ? -INFINITY : tv[j] * kLog2e;
+        }
+    }
     // the block's LSE and -D are read before the next block's copies are issued as well
     f32x4 lsv[4], ndv[4];
 #pragma unroll
@@ -515,7 +581,9 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const long long v = (long long)rintf(ds[qt][i] * kFix);
-        if (v != 0) lds_add_u64(&bins[(cqs[4 * qt + i] & 0xffffff) - (ck & 0xffffff) + code0], (uint64_t)v);
+        // an allowed pair (v != 0 only then): its bin from either code encoding
+        const int bin = fast ? (cqs[4 * qt + i] - kenc) >> 1 : (cqs[4 * qt + i] & 0xffffff) - (ck & 0xffffff) + code0;
+        if (v != 0) lds_add_u64(&bins[bin], (uint64_t)v);
       }
     // dV^T += dO^T P and dK^T += q^T dS: B operands are the lane's key column with the
     // queries of two adjacent 16-query tiles
@@ -603,13 +671,15 @@ hipError_t launch_tiled_fwd_bf16(const swin_attn_plan* p, const void* qkv, const
   a.table = table;
   a.o = (bf16*)o;
   a.lse = lse;
-  const dim3 grid((unsigned)p->tiled_work.size(), (unsigned)p->nh);
+  // 8 waves: blocks of 128 queries (the 128-token work items), two workgroups per CU
+  a.work = p->dev.tiled_kv_work;
+  const dim3 grid((unsigned)p->tiled_kv_work.size(), (unsigned)p->nh);
   if (p->hd == 32)
-    k_tiled_fwd<32><<<grid, 256, 0, s>>>(a);
+    k_tiled_fwd<32, 8><<<grid, 512, 0, s>>>(a);
   else if (p->hd == 64)
-    k_tiled_fwd<64><<<grid, 256, 0, s>>>(a);
+    k_tiled_fwd<64, 8><<<grid, 512, 0, s>>>(a);
   else
-    k_tiled_fwd<128><<<grid, 256, 0, s>>>(a);
+    k_tiled_fwd<128, 8><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 
