@@ -42,6 +42,7 @@ struct TiledArgs {
   int64_t n_tok;
   int nh, C, nbins;
   int win[3];
+  const int32_t* codes;     // per class: key codes, then query codes (see kCodeRound)
   // backward
   const bf16* dO;           // [nh][n_tok][hd] window-major
   const float* dd;          // -D = -rowsum(dO o), [nh][n_tok]
@@ -50,11 +51,6 @@ struct TiledArgs {
   float tau;
 };
 
-// Token codes of tokens past the window's end: a wrap label no real token has, so every pair
-// of such a token with a real one is masked. Two padding tokens share the label, so the
-// kernels also mask on the query's or key's own validity where both can be padding.
-constexpr int kPadCode = 0x7f << 24;
-
 template <int HD>
 struct TiledBuf {
   unsigned char k[HD / 32][kTB * 64];  // 32-column sub-tiles of the block, swizzled 64-byte rows
@@ -62,22 +58,6 @@ struct TiledBuf {
   int codes[kTB];
 };
 
-// Relative-position tables of up to kTabLds bins are held in LDS as fp16 in log2 units
-// (|error| <= 2^-11 |bias|, the precision the one-tile kernels keep their bias in) with a -inf
-// entry after the last bin, and the tokens' codes are staged in an encoding that makes a
-// pair's table address one subtraction and one unsigned min:
-//   key side   K = 2 local + (label << 16),   query side   Q = 2 (local + code0) + (label << 16).
-// Q - K is twice the pair's bin when the wrap labels agree and lies outside [0, 2 nbins)
-// otherwise; padding tokens take K = kPadK and Q = kPadQ, outside as well, so
-// min(Q - K, 2 nbins) (unsigned) addresses the bin's entry or the -inf one. Larger tables are
-// read from global memory with the plain codes.
-constexpr int kTabLds = 4096;
-constexpr int kPadK = 0x40000000, kPadQ = 0x7fffffff;
-
-__device__ __forceinline__ int enc_key(int code) { return 2 * (code & 0xffffff) + ((code >> 24) << 16); }
-__device__ __forceinline__ int enc_query(int code, int code0) {
-  return 2 * ((code & 0xffffff) + code0) + ((code >> 24) << 16);
-}
 __device__ __forceinline__ float fast_bias(int Q, int K, const _Float16* tab16, uint32_t lim) {
   const uint32_t ib = min((uint32_t)(Q - K), lim);
   return (float)*(const _Float16*)((const char*)tab16 + ib);
@@ -90,19 +70,20 @@ __device__ __forceinline__ void tiled_tab_fill(_Float16* dst, const float* tab, 
     dst[i] = i < nbins ? (_Float16)(tab[i] * kLog2e) : (_Float16)(-INFINITY);
 }
 
+// The table comes first so that its reads take their base from the instruction's offset field.
 template <int HD>
 struct TiledFwdSmem {
-  TiledBuf<HD> buf[2];
   _Float16 tab[kTabLds + 8];
+  alignas(1024) TiledBuf<HD> buf[2];
 };
 
 // Copies rows [kb*64, kb*64 + 64) of the planes a and b of one window (rows past n repeat row
 // n-1) into the sub-tiles of buffer dst; the 4 HD/32 copies per plane are spread over the NW
-// waves. Wave 0 also writes the keys' codes.
+// waves. Wave 0 also copies the block's 64 token codes from the class table csrc.
 template <int HD, int NW = 4>
 __device__ __forceinline__ void tiled_stage(const bf16* a, const bf16* b, int64_t off, int n, int kb, int wv,
-                                            int lane, const ClassInfo& ci, const int* win, unsigned char (*da)[kTB * 64],
-                                            unsigned char (*db)[kTB * 64], int* codes, bool fast = false) {
+                                            int lane, const int32_t* csrc, unsigned char (*da)[kTB * 64],
+                                            unsigned char (*db)[kTB * 64], int* codes) {
   constexpr int NSUB = HD / 32;
   constexpr int COPIES = 4 * NSUB;  // 1 KB copies per plane: 4 slabs of 16 rows per sub-tile
 #pragma unroll
@@ -118,13 +99,9 @@ __device__ __forceinline__ void tiled_stage(const bf16* a, const bf16* b, int64_
     lds_copy16(a + src, da[c] + 1024 * j);
     if (db) lds_copy16(b + src, db[c] + 1024 * j);
   }
-  if (codes && wv == 0) {
-    const int key = kb * kTB + lane;
-    if (fast)
-      codes[lane] = key < n ? enc_key(token_code(key, ci.ext, ci.split, win)) : kPadK;
-    else
-      codes[lane] = key < n ? token_code(key, ci.ext, ci.split, win) : kPadCode;
-  }
+  if (csrc && wv == 0)
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(csrc + kb * kTB + lane),
+                                     (__attribute__((address_space(3))) void*)codes, 4, 0, 0);
 }
 
 // Bias + mask of a pair in log2 units, without branches: the table index is in range for
@@ -136,20 +113,50 @@ __device__ __forceinline__ float tiled_bias(int cq, int ck, int code0, const flo
   return (cq >> 24) != (ck >> 24) ? -INFINITY : t * kLog2e;
 }
 
-// NW waves of 16 queries: blocks of 16 NW queries share every staged key/value block.
-template <int HD, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void k_tiled_fwd(TiledArgs a) {
-  constexpr int NSUB = HD / 32;
+// Four transposing reads for 32x32x16 V^T operands: f0 = the rows at offa and offb (keys
+// 4 hh + i/4 and 8 + 4 hh + i/4 of a 16-key step), f1 = the rows 16 further (the next step);
+// ended by their own LDS wait (see tile_frag_tr2_at).
+__device__ __forceinline__ void tile_frag_tr32(const unsigned char* tile, int offa, int offb, bf16x8& f0,
+                                               bf16x8& f1) {
+  const uint32_t base = lds_addr(tile);
+  u32x2 v0, v1, v2, v3;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+      : "v"(base + offa), "v"(base + offb)
+      : "memory");
+  f0 = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+  f1 = __builtin_bit_cast(bf16x8, u32x4{v2[0], v2[1], v3[0], v3[1]});
+}
+
+// Forward with 32 queries per wave: 4 waves, 128-query blocks, S^T = K Q^T and O^T = V^T P^T
+// on v_mfma_f32_32x32x16_bf16. A lane holds one query (lane % 32) and 32 keys of each 64-key
+// block (rows 32 t + 8 j + 4 hh + i, hh = lane / 32), so every K and V fragment read from LDS
+// serves 32 queries. The exponent offset m moves only when a block's maximum exceeds it by
+// more than kRescale (log2 units), so most blocks skip the rescaling of O; the probabilities
+// then lie in [0, 2^kRescale] and the final normalisation is unchanged. The bias enters the S
+// accumulator already shifted by -m (one mixed-precision FMA per pair), and the row sums are
+// taken from the same bf16 probabilities as the PV product (bf16 dot products).
+constexpr float kRescale = 8.f;
+
+template <int HD>
+__global__ __launch_bounds__(256, 2) void k_tiled_fwd32(TiledArgs a) {
+  constexpr int NSUB = HD / 32;  // 32-column sub-tiles (O^T row tiles)
+  constexpr int KS = HD / 16;    // 16-deep k steps of S
   __shared__ __attribute__((aligned(1024))) TiledFwdSmem<HD> sm;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4, li = lane & 15;
+  const int lq = lane & 31, hh = lane >> 5;
   const WorkItem wk = a.work[blockIdx.x];
   const int h = blockIdx.y;
   const ClassInfo ci = a.classes[wk.cls];
   const int n = ci.n;
   const int64_t off = a.win_off[wk.first];
-  const int q = wk.count * 16 * NW + 16 * wv + li;  // window-local query of this lane
+  const int q = wk.count * 128 + 32 * wv + lq;  // window-local query of this lane
   const bool qv = q < n;
   const int qc = qv ? q : n - 1;
   const size_t plane = (size_t)a.nh * a.n_tok * HD;
@@ -164,118 +171,137 @@ __global__ __launch_bounds__(64 * NW, 2) void k_tiled_fwd(TiledArgs a) {
   const int qenc = qv ? enc_query(cq, code0) : kPadQ;
   const uint32_t lim = 2u * (uint32_t)a.nbins;
 
-  tiled_tab_fill(sm.tab, tab, a.nbins, 64 * NW);
-  tiled_stage<HD, NW>(Kh, Vh, off, n, 0, wv, lane, ci, a.win, sm.buf[0].k, sm.buf[0].v, sm.buf[0].codes, fast);
-  // the lane's query: B operand of S^T = K Q^T, hd values 32 c + 8 g .. + 7
-  bf16x8 bq[NSUB];
+  tiled_tab_fill(sm.tab, tab, a.nbins, 256);
+  const int32_t* kcodes = a.codes + wk.codes;  // the class's key codes
+  tiled_stage<HD, 4>(Kh, Vh, off, n, 0, wv, lane, kcodes, sm.buf[0].k, sm.buf[0].v, sm.buf[0].codes);
+  // the lane's query: B operand of S^T, hd 16 s + 8 hh .. + 7 for k step s
+  bf16x8 bq[KS];
 #pragma unroll
-  for (int c = 0; c < NSUB; ++c) bq[c] = *(const bf16x8*)(Qh + (off + qc) * HD + 32 * c + 8 * g);
-  // The fragments are laundered through empty asm after an explicit wait, here and for the
-  // bias values below, so the compiler sees no load result in flight across the copies of the
-  // next block (it would otherwise wait for those copies too before the first use).
+  for (int s = 0; s < KS; ++s) bq[s] = *(const bf16x8*)(Qh + (off + qc) * HD + 16 * s + 8 * hh);
   vm_wait(0);
 #pragma unroll
-  for (int c = 0; c < NSUB; ++c) asm volatile("" : "+v"(bq[c]));
+  for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(bq[s]));
 
-  const int kq_off = li * 64 + 16 * (g ^ swz(li));
-  const int vr = 4 * g + (li >> 2);
-  const int vt_off0 = swz_off(vr, 4 * (li & 3)), vt_off1 = swz_off(vr, 16 + 4 * (li & 3));
-  bf16x8 ones;
+  // K fragment of step s: row 32 t + lq of sub-tile s / 2, logical chunk 2 (s % 2) + hh (rows a
+  // multiple of 16 apart share a swizzle)
+  const int k_off0 = lq * 64 + 16 * (hh ^ swz(lq)), k_off1 = lq * 64 + 16 * ((2 + hh) ^ swz(lq));
+  // V^T fragments: the 16-lane group lane / 16 reads hd columns 16 ((lane / 16) % 2) + i of the
+  // keys 4 hh + r and 8 + 4 hh + r (r < 4) of a 16-key step; lane i addresses row i / 4
+  const int i16 = lane & 15;
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+  const int v_offa = swz_off(4 * hh + (i16 >> 2), vcol), v_offb = swz_off(8 + 4 * hh + (i16 >> 2), vcol);
+  bf16x2 ones2;
+  ones2[0] = to_bf16(1.f);
+  ones2[1] = to_bf16(1.f);
+  float m_run = -INFINITY, l = 0.f;  // -inf: no allowed key seen yet
+  f32x16 oacc[NSUB];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = to_bf16(1.f);
-  float m = -INFINITY, l = 0.f;
-  f32x4 oacc[HD / 16];
-#pragma unroll
-  for (int d = 0; d < HD / 16; ++d) oacc[d] = f32x4{};
+  for (int d = 0; d < NSUB; ++d) oacc[d] = f32x16{};
 
   for (int kb = 0; kb < nkb; ++kb) {
-    // this wave's copies of block kb have landed (no other vector-memory operation is in
-    // flight here); the barrier then covers every wave's copies and codes, and every wave is
-    // done with the buffer the next block goes to
     vm_wait(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const TiledBuf<HD>& cur = sm.buf[kb & 1];
-    // bias + mask first: its table reads finish before the next block's copies are issued,
-    // so waiting for them never waits for those copies
-    f32x4 s[4];
+    const float m_eff = m_run == -INFINITY ? 0.f : m_run;
+    // bias - m for the lane's 32 keys, read before the next block's copies are issued
+    f32x16 sacc[2];
+    int kk[32];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int4 ck = *(const int4*)(cur.codes + 16 * kt + 4 * g);
-      const int kk[4] = {ck.x, ck.y, ck.z, ck.w};
-      if (fast) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[kt][i] = fast_bias(qenc, kk[i], sm.tab, lim);  // queries past n: -inf
-      } else {
+      for (int j = 0; j < 4; ++j) {
+        const int4 ck = *(const int4*)(cur.codes + 32 * t + 8 * j + 4 * hh);
+        kk[16 * t + 4 * j] = ck.x;
+        kk[16 * t + 4 * j + 1] = ck.y;
+        kk[16 * t + 4 * j + 2] = ck.z;
+        kk[16 * t + 4 * j + 3] = ck.w;
+      }
+    if (fast) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float b = tiled_bias(cq, kk[i], code0, tab);
-          s[kt][i] = qv ? b : 0.f;
-        }
+      for (int r = 0; r < 32; ++r) {
+        const uint32_t ib = min((uint32_t)(qenc - kk[r]), lim);
+        const uint32_t raw = *(const unsigned short*)((const char*)sm.tab + ib);
+        sacc[r >> 4][r & 15] = half_lo_minus(raw, m_eff);  // masked pairs and queries past n: -inf
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const float b = tiled_bias(cq, kk[r], code0, tab);
+        sacc[r >> 4][r & 15] = (qv ? b : 0.f) - m_eff;
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) asm volatile("" : "+v"(s[kt]) : : "memory");
+    for (int t = 0; t < 2; ++t) asm volatile("" : "+v"(sacc[t]) : : "memory");
     if (kb + 1 < nkb) {
       TiledBuf<HD>& nx = sm.buf[(kb + 1) & 1];
-      tiled_stage<HD, NW>(Kh, Vh, off, n, kb + 1, wv, lane, ci, a.win, nx.k, nx.v, nx.codes, fast);
+      tiled_stage<HD, 4>(Kh, Vh, off, n, kb + 1, wv, lane, kcodes, nx.k, nx.v, nx.codes);
     }
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int c = 0; c < NSUB; ++c) s[kt] = mfma16(*(const bf16x8*)(cur.k[c] + kq_off + 1024 * kt), bq[c], s[kt]);
+      for (int t = 0; t < 2; ++t)
+        sacc[t] = mfma32(*(const bf16x8*)(cur.k[s >> 1] + 2048 * t + ((s & 1) ? k_off1 : k_off0)), bq[s], sacc[t]);
     float mb = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mb = fmaxf(mb, s[kt][i]);
-    mb = wave_max_xor16_32(mb);
-    const float mn = fmaxf(m, mb);
-    const float ms = mn == -INFINITY ? 0.f : mn;  // nothing allowed yet: keep every term at 0
-    const float corr = fast_exp2(m - ms);
+      for (int r = 0; r < 16; ++r) mb = fmaxf(mb, sacc[t][r]);
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    // move m when the block's maximum exceeds it by more than kRescale, or to the first
+    // allowed key of the row
+    const bool need = mb > kRescale || (m_run == -INFINITY && mb != -INFINITY);
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float d = need ? mb : 0.f;
+      const float corr = fast_exp2(-d);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int dd = 0; dd < NSUB; ++dd) oacc[dd] *= corr;
+      l *= corr;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[kt][i] = fast_exp2(s[kt][i] - ms);
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int d = 0; d < HD / 16; ++d) oacc[d] *= corr;
-    f32x4 lacc = f32x4{};
+        for (int r = 0; r < 16; ++r) sacc[t][r] -= d;
+      m_run = need ? m_eff + d : m_run;
+    }
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      bf16x8 pb;
+    for (int t = 0; t < 2; ++t) {
+      // P^T operands of the 16-key steps 32 t and 32 t + 16: the lane's rows 16 u + 4 hh + i
+      // and 16 u + 8 + 4 hh + i
+      bf16x8 pb[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = to_bf16(s[2 * cc][i]);
-        pb[4 + i] = to_bf16(s[2 * cc + 1][i]);
-      }
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[u][i] = to_bf16(fast_exp2(sacc[t][8 * u + i]));
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[u][2 * e], pb[u][2 * e + 1]}, ones2, l, false);
 #pragma unroll
       for (int sc = 0; sc < NSUB; ++sc) {
-        bf16x8 v0, v1;
-        tile_frag_tr2_at(cur.v[sc] + 2048 * cc, vt_off0, vt_off1, v0, v1);
-        oacc[2 * sc] = mfma16(v0, pb, oacc[2 * sc]);
-        oacc[2 * sc + 1] = mfma16(v1, pb, oacc[2 * sc + 1]);
+        bf16x8 f0, f1;
+        tile_frag_tr32(cur.v[sc] + 2048 * t, v_offa, v_offb, f0, f1);
+        oacc[sc] = mfma32(f0, pb[0], oacc[sc]);
+        oacc[sc] = mfma32(f1, pb[1], oacc[sc]);
       }
-      lacc = mfma16(ones, pb, lacc);
     }
-    l = l * corr + lacc[0];
-    m = mn;
   }
+  l += __shfl_xor(l, 32);
   if (qv) {
     const float inv = __builtin_amdgcn_rcpf(l);
     const int64_t grow = a.perm[off + q];
     bf16* orow = a.o + grow * a.C + (int64_t)h * HD;
+    // O^T rows hd 32 sc + 8 j + 4 hh + i of the lane's query
 #pragma unroll
-    for (int sc = 0; sc < NSUB; ++sc) {
-      bf16x4 o0, o1;
+    for (int sc = 0; sc < NSUB; ++sc)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o0[i] = to_bf16(oacc[2 * sc][i] * inv);
-        o1[i] = to_bf16(oacc[2 * sc + 1][i] * inv);
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = to_bf16(oacc[sc][4 * j + i] * inv);
+        *(bf16x4*)(orow + 32 * sc + 8 * j + 4 * hh) = o4;
       }
-      *(bf16x4*)(orow + 32 * sc + 4 * g) = o0;
-      *(bf16x4*)(orow + 32 * sc + 16 + 4 * g) = o1;
-    }
-    if (g == 0) a.lse[(int64_t)h * a.n_tok + off + q] = m + fast_log2(l);
+    if (hh == 0) a.lse[(int64_t)h * a.n_tok + off + q] = m_run + fast_log2(l);
   }
 }
 
@@ -297,9 +323,9 @@ struct TiledQBuf {
 // ordering of the direct-to-LDS copies against LDS reads to the explicit waits.
 template <int HD>
 struct DkvSmem {
-  TiledQBuf<HD> buf[2];
+  _Float16 tab[kTabLds + 8];  // first: its reads and the bin additions keep small offsets
   unsigned long long bins[kTiledMaxBwdBins];
-  _Float16 tab[kTabLds + 8];
+  alignas(1024) TiledQBuf<HD> buf[2];
 };
 
 // dQ: the forward's structure with lse fixed; dP^T = V dO^T starts from -D.
@@ -332,7 +358,8 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
   const uint32_t lim = 2u * (uint32_t)a.nbins;
 
   tiled_tab_fill(sm.tab, tab, a.nbins, 256);
-  tiled_stage<HD>(Kh, Vh, off, n, 0, wv, lane, ci, a.win, sm.buf[0].k, sm.buf[0].v, sm.buf[0].codes, fast);
+  const int32_t* kcodes = a.codes + wk.codes;  // the class's key codes
+  tiled_stage<HD>(Kh, Vh, off, n, 0, wv, lane, kcodes, sm.buf[0].k, sm.buf[0].v, sm.buf[0].codes);
   bf16x8 bq[NSUB], bd[NSUB];
 #pragma unroll
   for (int c = 0; c < NSUB; ++c) {
@@ -378,7 +405,7 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
     for (int kt = 0; kt < 4; ++kt) asm volatile("" : "+v"(s[kt]) : : "memory");
     if (kb + 1 < nkb) {
       TiledBuf<HD>& nx = sm.buf[(kb + 1) & 1];
-      tiled_stage<HD>(Kh, Vh, off, n, kb + 1, wv, lane, ci, a.win, nx.k, nx.v, nx.codes, fast);
+      tiled_stage<HD>(Kh, Vh, off, n, kb + 1, wv, lane, kcodes, nx.k, nx.v, nx.codes);
     }
     f32x4 ds[4];
 #pragma unroll
@@ -428,9 +455,9 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
 // Copies query block qb of q and dO (rows past n repeat row n-1) and its LSE, -D and codes.
 template <int HD, int NW>
 __device__ __forceinline__ void tiled_stage_q(const TiledArgs& a, const bf16* Qh, const bf16* dOh, int h, int64_t off,
-                                              int n, int qb, int wv, int lane, const ClassInfo& ci,
+                                              int n, int qb, int wv, int lane, const int32_t* qcodes,
                                               TiledQBuf<HD>& b) {
-  tiled_stage<HD, NW>(Qh, dOh, off, n, qb, wv, lane, ci, a.win, b.q, b.d, nullptr);
+  tiled_stage<HD, NW>(Qh, dOh, off, n, qb, wv, lane, qcodes, b.q, b.d, b.codes);
   if (wv == 1) {
     const int qq = qb * kTB + lane;
     const int qs = qq < n ? qq : n - 1;
@@ -439,13 +466,6 @@ __device__ __forceinline__ void tiled_stage_q(const TiledArgs& a, const bf16* Qh
                                      (__attribute__((address_space(3))) void*)b.lse, 4, 0, 0);
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.dd + (int64_t)h * a.n_tok + off + qs),
                                      (__attribute__((address_space(3))) void*)b.nd, 4, 0, 0);
-  }
-  if (wv == 0) {
-    const int qq = qb * kTB + lane;
-    if (a.nbins <= kTabLds)
-      b.codes[lane] = qq < n ? enc_query(token_code(qq, ci.ext, ci.split, a.win), code0_of(a.win)) : kPadQ;
-    else
-      b.codes[lane] = qq < n ? token_code(qq, ci.ext, ci.split, a.win) : kPadCode;
   }
 }
 
@@ -493,7 +513,9 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
 
   for (int i = threadIdx.x; i < a.nbins; i += 64 * NW) bins[i] = 0ull;
   tiled_tab_fill(sm.tab, tab, a.nbins, 64 * NW);
-  tiled_stage_q<HD, NW>(a, Qh, dOh, h, off, n, 0, wv, lane, ci, buf[0]);
+  // the class's query codes follow its key codes
+  const int32_t* qcodes = a.codes + wk.codes + (n + kCodeRound - 1) / kCodeRound * kCodeRound;
+  tiled_stage_q<HD, NW>(a, Qh, dOh, h, off, n, 0, wv, lane, qcodes, buf[0]);
   // the lane's key and value: B operands of S = q K^T and dP = dO V^T
   bf16x8 bk[NSUB], bv[NSUB];
 #pragma unroll
@@ -559,7 +581,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) asm volatile("" : "+v"(s[qt]), "+v"(lsv[qt]), "+v"(ndv[qt]) : : "memory");
-    if (qb + 1 < nqb) tiled_stage_q<HD, NW>(a, Qh, dOh, h, off, n, qb + 1, wv, lane, ci, buf[(qb + 1) & 1]);
+    if (qb + 1 < nqb) tiled_stage_q<HD, NW>(a, Qh, dOh, h, off, n, qb + 1, wv, lane, qcodes, buf[(qb + 1) & 1]);
     f32x4 p[4], ds[4];
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
@@ -653,6 +675,7 @@ static TiledArgs tiled_args(const swin_attn_plan* p) {
   a.perm = p->dev.perm;
   a.work = p->dev.tiled_work;
   a.kv_work = p->dev.tiled_kv_work;
+  a.codes = p->dev.tiled_codes;
   a.classes = p->dev.classes;
   a.win_off = p->dev.win_off;
   a.n_tok = p->n_tok;
@@ -671,15 +694,15 @@ hipError_t launch_tiled_fwd_bf16(const swin_attn_plan* p, const void* qkv, const
   a.table = table;
   a.o = (bf16*)o;
   a.lse = lse;
-  // 8 waves: blocks of 128 queries (the 128-token work items), two workgroups per CU
+  // 4 waves of 32 queries: blocks of 128 queries (the 128-token work items), two workgroups per CU
   a.work = p->dev.tiled_kv_work;
   const dim3 grid((unsigned)p->tiled_kv_work.size(), (unsigned)p->nh);
   if (p->hd == 32)
-    k_tiled_fwd<32, 8><<<grid, 512, 0, s>>>(a);
+    k_tiled_fwd32<32><<<grid, 256, 0, s>>>(a);
   else if (p->hd == 64)
-    k_tiled_fwd<64, 8><<<grid, 512, 0, s>>>(a);
+    k_tiled_fwd32<64><<<grid, 256, 0, s>>>(a);
   else
-    k_tiled_fwd<128, 8><<<grid, 512, 0, s>>>(a);
+    k_tiled_fwd32<128><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -46,22 +46,6 @@ __device__ __forceinline__ float wave_sum_xor16_32(float v) {
   return v;
 }
 
-// ---- relative-position bins ----
-// Linear code of a token's local offsets (ld, lh, lw) in a window with nominal extents
-// (wd, wh, ww): code = (ld (2wh-1) + lh) (2ww-1) + lw. The bias-table bin of a query/key pair
-// is then code(q) - code(k) + code0 with code0 = code(wd-1, wh-1, ww-1). The wrap-label bits
-// (ld >= split_d, lh >= split_h, lw >= split_w) sit above bit 24.
-__device__ __forceinline__ int token_code(int j, const int* ext, const int* split, const int* win) {
-  const int lw = j % ext[2];
-  const int r = j / ext[2];
-  const int lh = r % ext[1];
-  const int ld = r / ext[1];
-  const int lab = (ld >= split[0] ? 1 : 0) | (lh >= split[1] ? 2 : 0) | (lw >= split[2] ? 4 : 0);
-  return (lab << 24) | ((ld * (2 * win[1] - 1) + lh) * (2 * win[2] - 1) + lw);
-}
-__device__ __forceinline__ int code0_of(const int* win) {
-  return ((win[0] - 1) * (2 * win[1] - 1) + (win[1] - 1)) * (2 * win[2] - 1) + (win[2] - 1);
-}
 // Logit offset (log2 units) of a pair from the two tokens' codes: -inf across wrap labels.
 __device__ __forceinline__ float pair_bias_codes(int cq, int ck, int code0, const float* tab2) {
   if ((cq >> 24) != (ck >> 24)) return -INFINITY;

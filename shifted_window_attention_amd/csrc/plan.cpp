@@ -221,6 +221,7 @@ static void free_dev(swin_attn_plan* p) {
     hipFree(p->dev.bwd_work);
     hipFree(p->dev.tiled_work);
     hipFree(p->dev.tiled_kv_work);
+    hipFree(p->dev.tiled_codes);
     if (cur >= 0) (void)hipSetDevice(cur);
   }
   p->dev = DevTables{};
@@ -349,11 +350,28 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
   }
   build_work(p->classes, p->nh, 1024, 64, p->fwd_work, p->fwd_ranges);
   if (p->tiled || p->tiled_bwd) {
+    // token-code tables of every class: key codes, then query codes, kCodeRound-padded
+    const bool enc = p->nbins <= kTabLds;
+    const int code0 = code0_of(desc->window);
+    std::vector<int32_t> code_off(p->classes.size());
+    for (size_t c = 0; c < p->classes.size(); ++c) {
+      const ClassInfo& ci = p->classes[c];
+      const int nr = (ci.n + kCodeRound - 1) / kCodeRound * kCodeRound;
+      code_off[c] = (int32_t)p->tiled_codes.size();
+      p->tiled_codes.resize(p->tiled_codes.size() + 2 * (size_t)nr);
+      int32_t* kc = p->tiled_codes.data() + code_off[c];
+      for (int j = 0; j < nr; ++j) {
+        const int code = j < ci.n ? token_code(j, ci.ext, ci.split, desc->window) : 0;
+        kc[j] = j < ci.n ? (enc ? enc_key(code) : code) : (enc ? kPadK : kPadCode);
+        kc[nr + j] = j < ci.n ? (enc ? enc_query(code, code0) : code) : (enc ? kPadQ : kPadCode);
+      }
+    }
     // one item per 64-token block of every window, windows in row-major order
     for (int64_t w = 0; w < p->n_win; ++w) {
       const int n = p->win_off[w + 1] - p->win_off[w];
-      for (int b = 0; b * 64 < n; ++b) p->tiled_work.push_back(WorkItem{L.win_cls[w], (int32_t)w, b, 0});
-      for (int b = 0; b * 128 < n; ++b) p->tiled_kv_work.push_back(WorkItem{L.win_cls[w], (int32_t)w, b, 0});
+      const int c = L.win_cls[w];
+      for (int b = 0; b * 64 < n; ++b) p->tiled_work.push_back(WorkItem{c, (int32_t)w, b, code_off[c]});
+      for (int b = 0; b * 128 < n; ++b) p->tiled_kv_work.push_back(WorkItem{c, (int32_t)w, b, code_off[c]});
     }
   }
   // the backward bins its bias gradient once per work item: fewer, longer items (1 WG per CU)
@@ -391,6 +409,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
   if (e == hipSuccess) e = upload(&p->dev.bwd_work, p->bwd_work);
   if (e == hipSuccess && !p->tiled_work.empty()) e = upload(&p->dev.tiled_work, p->tiled_work);
   if (e == hipSuccess && !p->tiled_kv_work.empty()) e = upload(&p->dev.tiled_kv_work, p->tiled_kv_work);
+  if (e == hipSuccess && !p->tiled_codes.empty()) e = upload(&p->dev.tiled_codes, p->tiled_codes);
   if (e != hipSuccess) {
     set_error(std::string("plan upload failed: ") + hipGetErrorString(e));
     free_dev(p);

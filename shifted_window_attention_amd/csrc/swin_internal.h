@@ -23,13 +23,53 @@ struct ClassInfo {
   int32_t nqt;       // 16-token tiles per window, ceil(n/16)
 };
 
-// A contiguous chunk of one class's windows, processed by one workgroup per head.
+// A contiguous chunk of one class's windows, processed by one workgroup per head. Items of
+// the tiled path name one window (first) and one token block of it (count).
 struct WorkItem {
   int32_t cls;
-  int32_t first;  // offset into the class-sorted window list
+  int32_t first;  // offset into the class-sorted window list (tiled path: the window)
   int32_t count;
-  int32_t pad;
+  int32_t codes;  // tiled path: offset of the class's token-code tables (0 otherwise)
 };
+
+// ---- relative-position bins ----
+// Linear code of a token's local offsets (ld, lh, lw) in a window with nominal extents
+// (wd, wh, ww): code = (ld (2wh-1) + lh) (2ww-1) + lw. The bias-table bin of a query/key pair
+// is then code(q) - code(k) + code0 with code0 = code(wd-1, wh-1, ww-1). The wrap-label bits
+// (ld >= split_d, lh >= split_h, lw >= split_w) sit above bit 24.
+__host__ __device__ inline int token_code(int j, const int* ext, const int* split, const int* win) {
+  const int lw = j % ext[2];
+  const int r = j / ext[2];
+  const int lh = r % ext[1];
+  const int ld = r / ext[1];
+  const int lab = (ld >= split[0] ? 1 : 0) | (lh >= split[1] ? 2 : 0) | (lw >= split[2] ? 4 : 0);
+  return (lab << 24) | ((ld * (2 * win[1] - 1) + lh) * (2 * win[2] - 1) + lw);
+}
+__host__ __device__ inline int code0_of(const int* win) {
+  return ((win[0] - 1) * (2 * win[1] - 1) + (win[1] - 1)) * (2 * win[2] - 1) + (win[2] - 1);
+}
+
+// Token codes of the tiled path. Tokens past a window's end take the padding code: a wrap
+// label no real token has, so every pair of such a token with a real one is masked (two
+// padding tokens share the label, so the kernels also mask on their own validity).
+constexpr int kPadCode = 0x7f << 24;
+// Relative-position tables of up to kTabLds bins are held in LDS as fp16 in log2 units
+// (|error| <= 2^-11 |bias|) with a -inf entry after the last bin, and the codes are then
+// staged in an encoding that makes a pair's table address one subtraction and one unsigned
+// min:  key side K = 2 local + (label << 16),  query side Q = 2 (local + code0) + (label << 16).
+// Q - K is twice the pair's bin when the wrap labels agree and lies outside [0, 2 nbins)
+// otherwise; padding tokens take K = kPadK and Q = kPadQ, outside as well, so
+// min(Q - K, 2 nbins) (unsigned) addresses the bin's entry or the -inf one. Larger tables are
+// read from global memory with the plain codes.
+constexpr int kTabLds = 4096;
+constexpr int kPadK = 0x40000000, kPadQ = 0x7fffffff;
+__host__ __device__ inline int enc_key(int code) { return 2 * (code & 0xffffff) + ((code >> 24) << 16); }
+__host__ __device__ inline int enc_query(int code, int code0) {
+  return 2 * ((code & 0xffffff) + code0) + ((code >> 24) << 16);
+}
+// Per class, the plan keeps the key and the query codes of tokens 0 .. kCodeRound-rounded n - 1
+// (padding past n), in the encoding above when the table fits LDS, else plain.
+constexpr int kCodeRound = 128;
 
 // Work items of one tile count (ceil(n/16)), contiguous in the work list.
 struct WorkRange {
@@ -53,6 +93,7 @@ struct DevTables {
   WorkItem* bwd_work = nullptr;  // [n_bwd_work]
   WorkItem* tiled_work = nullptr;  // [n_tiled_work] (class, window, 64-token block) of the tiled path
   WorkItem* tiled_kv_work = nullptr;  // (class, window, 128-token block): the tiled dK/dV kernel
+  int32_t* tiled_codes = nullptr;     // per class: key codes, then query codes (tiled path)
 };
 
 }  // namespace swin
@@ -72,6 +113,7 @@ struct swin_attn_plan {
   bool tiled = false;                      // bf16 windows over 256 tokens, head_dim 64/128, large tables
   bool tiled_bwd = false;                  // backward on the tiled kernels (tiled, or windows over 160 tokens)
   std::vector<swin::WorkItem> tiled_work, tiled_kv_work;
+  std::vector<int32_t> tiled_codes;
   swin::DevTables dev;
   // workspace / saved-state layout (bytes)
   size_t saved_qkv = 0, saved_o = 0, saved_lse = 0, saved_total = 0;
