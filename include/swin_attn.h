@@ -202,8 +202,9 @@ swin_status swin_attn_fwd(const swin_attn_plan* plan, const void* x, const void*
  *   dbias_table  fp32 [heads, 2wd-1, 2wh-1, 2ww-1].
  * dT[h, bin] sums dS over every window and allowed pair (the inverse routes
  * carry gradients back to their sources [TERRA IV-D]); all reductions run in
- * a fixed order (on the tiled kernels dT is summed in 2^-32 fixed point, whose
- * integer sums do not depend on order), so repeated calls are bitwise identical.
+ * a fixed order (on the tiled kernels every dS term of dT is rounded to an
+ * integer multiple of 2^-20, saturating at magnitude 2^11, and the integers are
+ * summed exactly, in any order), so repeated calls are bitwise identical.
  * Only SWIN_BF16 is supported (SWIN_ERR_UNSUPPORTED for fp32), with relative-
  * position tables of at most 8192 bins per head when a window has more than
  * 160 tokens, head_dim is 64/128 or the table exceeds 2048 bins

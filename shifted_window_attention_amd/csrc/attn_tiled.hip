@@ -104,6 +104,38 @@ __device__ __forceinline__ void tiled_stage(const bf16* a, const bf16* b, int64_
                                      (__attribute__((address_space(3))) void*)codes, 4, 0, 0);
 }
 
+// Copy of rows [kb*64, kb*64 + 64) of one window's plane into the swizzled 32-column sub-tiles
+// dst[c] through buffer loads straight to LDS. The resource spans the window's n rows, so rows
+// past n arrive as zeros. The 4 HD/32 one-kilobyte copies are spread over the NW waves (NW a
+// multiple of 4): wave w copies the 16-row slab w % 4 of sub-tiles w/4 + NW/4 t. voff is the
+// lane's byte offset inside a block (stage_voff).
+template <int HD, int NW>
+__device__ __forceinline__ void stage_plane(__amdgpu_buffer_rsrc_t src, int kb, int wv, uint32_t voff,
+                                            unsigned char (*dst)[kTB * 64]) {
+  constexpr int NSUB = HD / 32;
+  constexpr int PER = (4 * NSUB + NW - 1) / NW;
+  static_assert(NW % 4 == 0, "whole slabs per wave");
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int c = (wv >> 2) + (NW / 4) * t;
+    if ((4 * NSUB) % NW != 0 && c >= NSUB) break;  // wave-uniform
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(dst[c] + 1024 * (wv & 3)),
+                                             16, voff + (uint32_t)(kb * kTB * HD * 2 + 64 * c), 0, 0, 0);
+  }
+}
+// Lane offset of stage_plane: row 16 (w % 4) + lane/4 of the block, logical 16-byte chunk
+// (lane % 4) ^ swz(row) of each 32-column sub-tile (the chunk lands in slot lane % 4).
+template <int HD>
+__device__ __forceinline__ uint32_t stage_voff(int wv, int lane) {
+  const int row = 16 * (wv & 3) + (lane >> 2);
+  return (uint32_t)(row * HD * 2 + 16 * ((lane & 3) ^ swz(row)));
+}
+// The 64 codes of block kb from a class code table (resource over its entries).
+__device__ __forceinline__ void stage_codes(__amdgpu_buffer_rsrc_t src, int kb, int lane, int* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4,
+                                           (uint32_t)(4 * (kb * kTB + lane)), 0, 0, 0);
+}
+
 // Bias + mask of a pair in log2 units, without branches: the table index is in range for
 // every pair of real tokens and for a real query against a padding key (code 0 in the low
 // bits; local codes never exceed code0), so the read is issued for all lanes and the label
@@ -305,10 +337,225 @@ __global__ __launch_bounds__(256, 2) void k_tiled_fwd32(TiledArgs a) {
   }
 }
 
+// LDS of the pipelined forward: K runs one block ahead of V, codes two (ring of four).
+template <int HD>
+struct FwdPipeSmem {
+  _Float16 tab[kTabLds + 8];
+  alignas(1024) unsigned char k[2][HD / 32][kTB * 64];
+  unsigned char v[2][HD / 32][kTB * 64];
+  int codes[4][kTB];
+};
+
+// The forward of k_tiled_fwd32, software-pipelined so that each wave's matrix and vector work
+// overlap: in step kb the S MFMAs of block kb+1 run beside the exponentials of block kb, and the
+// PV MFMAs of block kb beside the bias reads of block kb+2. Buffers: K(kb+1) and V(kb) are read
+// in step kb while K(kb+2), V(kb+1) and the codes of block kb+3 are copied in.
+// FAST: the bias table is in LDS (nbins <= kTabLds; the code tables are then encoded).
+template <int HD, bool FAST>
+__global__ __launch_bounds__(256, 2) void k_tiled_fwd_pipe(TiledArgs a) {
+  constexpr int NSUB = HD / 32;
+  constexpr int KS = HD / 16;
+  __shared__ __attribute__((aligned(1024))) FwdPipeSmem<HD> sm;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lq = lane & 31, hh = lane >> 5;
+  const WorkItem wk = a.work[blockIdx.x];
+  const int h = blockIdx.y;
+  const ClassInfo ci = a.classes[wk.cls];
+  const int n = ci.n;
+  const int64_t off = a.win_off[wk.first];
+  const int q = wk.count * 128 + 32 * wv + lq;
+  const bool qv = q < n;
+  const int qc = qv ? q : n - 1;
+  const size_t plane = (size_t)a.nh * a.n_tok * HD;
+  const bf16* Qh = a.qkv + (size_t)h * a.n_tok * HD;
+  const bf16* Kh = Qh + plane;
+  const bf16* Vh = Kh + plane;
+  const float* tab = a.table + (int64_t)h * a.nbins;
+  const int code0 = code0_of(a.win);
+  const int cq = token_code(qc, ci.ext, ci.split, a.win);
+  const int nkb = (n + kTB - 1) / kTB;
+  const int qenc = qv ? enc_query(cq, code0) : kPadQ;
+  const uint32_t lim = 2u * (uint32_t)a.nbins;
+  const int nr = (n + kCodeRound - 1) / kCodeRound * kCodeRound;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + off * HD, (uint32_t)n * HD * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + off * HD, (uint32_t)n * HD * 2);
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes + wk.codes, (uint32_t)nr * 4);  // the class's key codes
+  const uint32_t voff = stage_voff<HD>(wv, lane);
+  auto stage_k = [&](int j) { stage_plane<HD, 4>(rk, j, wv, voff, sm.k[j & 1]); };
+  auto stage_v = [&](int j) { stage_plane<HD, 4>(rv, j, wv, voff, sm.v[j & 1]); };
+  auto stage_c = [&](int j) {
+    if (wv == 0) stage_codes(rc, j, lane, sm.codes[j & 3]);
+  };
+  // bias - m of the lane's 32 keys of block j (rows 32 t + 8 r/4 ... as in k_tiled_fwd32)
+  auto bias_init = [&](int j, float m_eff, f32x16 (&S)[2]) {
+    if constexpr (FAST) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int4 ck = *(const int4*)(sm.codes[j & 3] + 32 * t + 8 * jj + 4 * hh);
+          const int kk[4] = {ck.x, ck.y, ck.z, ck.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t ib = min((uint32_t)(qenc - kk[i]), lim);
+            const uint32_t raw = *(const unsigned short*)((const char*)sm.tab + ib);
+            S[t][4 * jj + i] = half_lo_minus(raw, m_eff);
+          }
+        }
+    } else {
+      int kk[32];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int4 ck = *(const int4*)(sm.codes[j & 3] + 32 * t + 8 * jj + 4 * hh);
+          kk[16 * t + 4 * jj] = ck.x;
+          kk[16 * t + 4 * jj + 1] = ck.y;
+          kk[16 * t + 4 * jj + 2] = ck.z;
+          kk[16 * t + 4 * jj + 3] = ck.w;
+        }
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const float b = tiled_bias(cq, kk[r], code0, tab);
+        S[r >> 4][r & 15] = (qv ? b : 0.f) - m_eff;
+      }
+    }
+  };
+
+  tiled_tab_fill(sm.tab, tab, a.nbins, 256);
+  stage_k(0);
+  stage_c(0);
+  if (nkb > 1) stage_c(1);
+  bf16x8 bq[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) bq[s] = *(const bf16x8*)(Qh + (off + qc) * HD + 16 * s + 8 * hh);
+  vm_wait(0);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(bq[s]));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  const int k_off0 = lq * 64 + 16 * (hh ^ swz(lq)), k_off1 = lq * 64 + 16 * ((2 + hh) ^ swz(lq));
+  const int i16 = lane & 15;
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+  const int v_offa = swz_off(4 * hh + (i16 >> 2), vcol), v_offb = swz_off(8 + 4 * hh + (i16 >> 2), vcol);
+  bf16x2 ones2;
+  ones2[0] = to_bf16(1.f);
+  ones2[1] = to_bf16(1.f);
+  float m_run = -INFINITY, l = 0.f;
+  f32x16 oacc[NSUB];
+#pragma unroll
+  for (int d = 0; d < NSUB; ++d) oacc[d] = f32x16{};
+
+  auto s_mfma = [&](int j, f32x16 (&S)[2]) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        S[t] = mfma32(*(const bf16x8*)(sm.k[j & 1][s >> 1] + 2048 * t + ((s & 1) ? k_off1 : k_off0)), bq[s], S[t]);
+  };
+
+  // prologue: S(0) complete, bias of block 1 in Sb; K(1), V(0) and the codes of block 2 in flight
+  f32x16 Sa[2], Sb[2];
+  bias_init(0, 0.f, Sa);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (nkb > 1) stage_k(1);
+  stage_v(0);
+  if (nkb > 2) stage_c(2);
+  s_mfma(0, Sa);
+  if (nkb > 1) bias_init(1, 0.f, Sb);
+
+  // one step: Sc = S(kb) (complete), Sn = bias(kb+1) - m; ends with Sc = bias(kb+2) - m and
+  // Sn = S(kb+1) complete
+  auto step = [&](int kb, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
+    vm_wait(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kb + 2 < nkb) stage_k(kb + 2);
+    if (kb + 1 < nkb) stage_v(kb + 1);
+    if (kb + 3 < nkb) stage_c(kb + 3);
+    const float m_old = m_run == -INFINITY ? 0.f : m_run;
+    float mb = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mb = fmaxf(mb, Sc[t][r]);
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const bool need = mb > kRescale || (m_run == -INFINITY && mb != -INFINITY);
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float d = need ? mb : 0.f;
+      const float corr = fast_exp2(-d);
+#pragma unroll
+      for (int dd = 0; dd < NSUB; ++dd) oacc[dd] *= corr;
+      l *= corr;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          Sc[t][r] -= d;
+          Sn[t][r] -= d;
+        }
+      m_run = need ? m_old + d : m_run;
+    }
+    // S(kb+1) on the matrix cores beside P(kb) on the vector ALUs. Past the last block both run
+    // on stale buffers (in-bounds LDS reads, results unused), so no branch splits the step.
+    s_mfma(kb + 1, Sn);
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[t][u][i] = to_bf16(fast_exp2(Sc[t][8 * u + i]));
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[t][u][2 * e], pb[t][u][2 * e + 1]}, ones2, l, false);
+    // PV(kb) beside the bias of block kb+2
+    const float m_eff = m_run == -INFINITY ? 0.f : m_run;
+    // stale codes only address the LDS table (clamped); the global table needs the guard
+    if (FAST || kb + 2 < nkb) bias_init(kb + 2, m_eff, Sc);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int sc = 0; sc < NSUB; ++sc) {
+        bf16x8 f0, f1;
+        tile_frag_tr32(sm.v[kb & 1][sc] + 2048 * t, v_offa, v_offb, f0, f1);
+        oacc[sc] = mfma32(f0, pb[t][0], oacc[sc]);
+        oacc[sc] = mfma32(f1, pb[t][1], oacc[sc]);
+      }
+  };
+  for (int kb = 0; kb < nkb; kb += 2) {
+    step(kb, Sa, Sb);
+    if (kb + 1 < nkb) step(kb + 1, Sb, Sa);
+  }
+  l += __shfl_xor(l, 32);
+  if (qv) {
+    const float inv = __builtin_amdgcn_rcpf(l);
+    const int64_t grow = a.perm[off + q];
+    bf16* orow = a.o + grow * a.C + (int64_t)h * HD;
+#pragma unroll
+    for (int sc = 0; sc < NSUB; ++sc)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = to_bf16(oacc[sc][4 * j + i] * inv);
+        *(bf16x4*)(orow + 32 * sc + 8 * j + 4 * hh) = o4;
+      }
+    if (hh == 0) a.lse[(int64_t)h * a.n_tok + off + q] = m_run + fast_log2(l);
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // backward
 // ---------------------------------------------------------------------------------------
-constexpr float kFix = 4294967296.f;  // 2^32: fixed-point scale of the dT accumulator
+// dT is summed in fixed point: every dS term is rounded to a 32-bit integer in units of 2^-20
+// (terms of magnitude 2^11 and beyond saturate) and added into 64-bit integer bins, so the
+// sums are exact and do not depend on the order of the additions.
+constexpr float kFix = 1048576.f;  // 2^20
 
 template <int HD>
 struct TiledQBuf {
@@ -324,12 +571,12 @@ struct TiledQBuf {
 template <int HD>
 struct DkvSmem {
   _Float16 tab[kTabLds + 8];  // first: its reads and the bin additions keep small offsets
-  unsigned long long bins[kTiledMaxBwdBins];
+  unsigned long long bins[kTiledMaxBwdBins + 8];  // entry nbins: the masked pairs' (zero) terms
   alignas(1024) TiledQBuf<HD> buf[2];
 };
 
 // dQ: the forward's structure with lse fixed; dP^T = V dO^T starts from -D.
-template <int HD>
+template <int HD, bool FAST>
 __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
   constexpr int NSUB = HD / 32;
   __shared__ __attribute__((aligned(1024))) TiledFwdSmem<HD> sm;
@@ -353,7 +600,6 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
   const int code0 = code0_of(a.win);
   const int cq = token_code(qc, ci.ext, ci.split, a.win);
   const int nkb = (n + kTB - 1) / kTB;
-  const bool fast = a.nbins <= kTabLds;
   const int qenc = qv ? enc_query(cq, code0) : kPadQ;
   const uint32_t lim = 2u * (uint32_t)a.nbins;
 
@@ -389,14 +635,17 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
     for (int kt = 0; kt < 4; ++kt) {
       const int4 ck = *(const int4*)(cur.codes + 16 * kt + 4 * g);
       const int kk[4] = {ck.x, ck.y, ck.z, ck.w};
-      if (fast) {
+      if constexpr (FAST) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[kt][i] = fast_bias(qenc, kk[i], sm.tab, lim);  // queries past n: -inf
+        for (int i = 0; i < 4; ++i) {  // bias - lse; queries past n: -inf
+          const uint32_t ib = min((uint32_t)(qenc - kk[i]), lim);
+          s[kt][i] = half_lo_minus(*(const unsigned short*)((const char*)sm.tab + ib), lse_q);
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float b = tiled_bias(cq, kk[i], code0, tab);
-          s[kt][i] = qv ? b : -INFINITY;  // queries past n: P = 0, nothing flows back
+          s[kt][i] = qv ? b - lse_q : -INFINITY;  // queries past n: P = 0, nothing flows back
         }
       }
     }
@@ -416,7 +665,7 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
 #pragma unroll
       for (int c = 0; c < NSUB; ++c) dp = mfma16(*(const bf16x8*)(cur.v[c] + kq_off + 1024 * kt), bd[c], dp);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ds[kt][i] = fast_exp2(s[kt][i] - lse_q) * dp[i];
+      for (int i = 0; i < 4; ++i) ds[kt][i] = fast_exp2(s[kt][i]) * dp[i];
     }
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
@@ -476,10 +725,14 @@ __device__ __forceinline__ void tiled_stage_q(const TiledArgs& a, const bf16* Qh
 __device__ __forceinline__ void lds_add_u64(unsigned long long* p, uint64_t v) {
   asm volatile("ds_add_u64 %0, %1" : : "v"(lds_addr(p)), "v"(v));
 }
+__device__ __forceinline__ void lds_add_u64_at(uint32_t addr, uint64_t v) {
+  asm volatile("ds_add_u64 %0, %1" : : "v"(addr), "v"(v));
+}
 
 constexpr int kKvWaves = 8;  // dK/dV: 8 waves of 16 keys, so two waves share each SIMD
 
-template <int HD>
+// FAST: the bias table is in LDS (nbins <= kTabLds; the code tables are then encoded).
+template <int HD, bool FAST>
 __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a) {
   constexpr int NW = kKvWaves;
   constexpr int NSUB = HD / 32;
@@ -507,11 +760,11 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
   // keys past n take the padding code: every pair masked, nothing accumulated
   const int ck = kv ? token_code(k, ci.ext, ci.split, a.win) : kPadCode;
   const int nqb = (n + kTB - 1) / kTB;
-  const bool fast = a.nbins <= kTabLds;
   const int kenc = kv ? enc_key(ck) : kPadK;
   const uint32_t lim = 2u * (uint32_t)a.nbins;
 
-  for (int i = threadIdx.x; i < a.nbins; i += 64 * NW) bins[i] = 0ull;
+  for (int i = threadIdx.x; i <= a.nbins; i += 64 * NW) bins[i] = 0ull;
+  const uint32_t bins_base = lds_addr(bins);
   tiled_tab_fill(sm.tab, tab, a.nbins, 64 * NW);
   // the class's query codes follow its key codes
   const int32_t* qcodes = a.codes + wk.codes + (n + kCodeRound - 1) / kCodeRound * kCodeRound;
@@ -541,23 +794,33 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
     vm_wait(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const TiledQBuf<HD>& cur = buf[qb & 1];
-    // S = q K^T + bias: lane = key li, rows = queries 16 qt + 4 g + i
-    // all 16 table reads are issued before any is used
+    // S - lse = q K^T + bias - lse: lane = key li, rows = queries 16 qt + 4 g + i. The block's
+    // LSE and -D and the bias are read before the next block's copies are issued.
+    f32x4 lsv[4], ndv[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      lsv[qt] = *(const f32x4*)(cur.lse + 16 * qt + 4 * g);
+      ndv[qt] = *(const f32x4*)(cur.nd + 16 * qt + 4 * g);
+    }
+    // FAST: the pair's clamped table offset (twice its bin, or 2 nbins for masked pairs), which
+    // is also its dT bin; otherwise the queries' plain codes
     int cqs[16];
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
       const int4 cqv = *(const int4*)(cur.codes + 16 * qt + 4 * g);
-      cqs[4 * qt] = cqv.x;
-      cqs[4 * qt + 1] = cqv.y;
-      cqs[4 * qt + 2] = cqv.z;
-      cqs[4 * qt + 3] = cqv.w;
+      const int c4[4] = {cqv.x, cqv.y, cqv.z, cqv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cqs[4 * qt + i] = FAST ? (int)min((uint32_t)(c4[i] - kenc), lim) : c4[i];
     }
     f32x4 s[4];
-    if (fast) {
+    if constexpr (FAST) {
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[qt][i] = fast_bias(cqs[4 * qt + i], kenc, sm.tab, lim);
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t raw = *(const unsigned short*)((const char*)sm.tab + cqs[4 * qt + i]);
+          s[qt][i] = half_lo_minus(raw, lsv[qt][i]);
+        }
     } else {
       float tv[16];
 #pragma unroll
@@ -568,44 +831,42 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
         for (int i = 0; i < 4; ++i) {
           const int j = 4 * qt + i;
           // a padding key and a padding query share the padding label: mask on kv as well
-          s[qt][i] = (!kv || (cqs[j] >> 24) != (ck >> 24)) ? -INFINITY : tv[j] * kLog2e;
+          s[qt][i] = (!kv || (cqs[j] >> 24) != (ck >> 24)) ? -INFINITY : tv[j] * kLog2e - lsv[qt][i];
         }
-    }
-    // the block's LSE and -D are read before the next block's copies are issued as well
-    f32x4 lsv[4], ndv[4];
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      lsv[qt] = *(const f32x4*)(cur.lse + 16 * qt + 4 * g);
-      ndv[qt] = *(const f32x4*)(cur.nd + 16 * qt + 4 * g);
     }
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) asm volatile("" : "+v"(s[qt]), "+v"(lsv[qt]), "+v"(ndv[qt]) : : "memory");
+    for (int qt = 0; qt < 4; ++qt) asm volatile("" : "+v"(s[qt]), "+v"(ndv[qt]) : : "memory");
     if (qb + 1 < nqb) tiled_stage_q<HD, NW>(a, Qh, dOh, h, off, n, qb + 1, wv, lane, qcodes, buf[(qb + 1) & 1]);
     f32x4 p[4], ds[4];
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
 #pragma unroll
       for (int c = 0; c < NSUB; ++c) s[qt] = mfma16(*(const bf16x8*)(cur.q[c] + qk_off + 1024 * qt), bk[c], s[qt]);
-      const f32x4 ls = lsv[qt];
       f32x4 dp = ndv[qt];
 #pragma unroll
       for (int c = 0; c < NSUB; ++c) dp = mfma16(*(const bf16x8*)(cur.d[c] + qk_off + 1024 * qt), bv[c], dp);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[qt][i] = fast_exp2(s[qt][i] - ls[i]);
+        p[qt][i] = fast_exp2(s[qt][i]);
         ds[qt][i] = p[qt][i] * dp[i];
       }
     }
-    // dT: every pair's dS into the workgroup's fixed-point bins (masked pairs add 0)
+    // dT: every pair's dS into the workgroup's fixed-point bins
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const long long v = (long long)rintf(ds[qt][i] * kFix);
-        // an allowed pair (v != 0 only then): its bin from either code encoding
-        const int bin = fast ? (cqs[4 * qt + i] - kenc) >> 1 : (cqs[4 * qt + i] & 0xffffff) - (ck & 0xffffff) + code0;
-        if (v != 0) lds_add_u64(&bins[bin], (uint64_t)v);
+        const int v = (int)rintf(ds[qt][i] * kFix);
+        if constexpr (FAST) {
+          // the clamped offset is even (both encodings are even and the odd padding query code
+          // always clamps to 2 nbins), so bin * 8 = offset * 4; masked pairs: bin nbins, v = 0
+          lds_add_u64_at(bins_base + ((uint32_t)cqs[4 * qt + i] << 2), (uint64_t)(int64_t)v);
+        } else {
+          // an allowed pair (v != 0 only then)
+          const int bin = (cqs[4 * qt + i] & 0xffffff) - (ck & 0xffffff) + code0;
+          if (v != 0) lds_add_u64(&bins[bin], (uint64_t)(int64_t)v);
+        }
       }
     // dV^T += dO^T P and dK^T += q^T dS: B operands are the lane's key column with the
     // queries of two adjacent 16-query tiles
@@ -667,7 +928,7 @@ __global__ __launch_bounds__(256) void k_fixed_zero(unsigned long long* p, int64
 
 __global__ __launch_bounds__(256) void k_fixed_to_f32(const unsigned long long* p, float* out, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) out[i] = (float)((double)(long long)p[i] * (1.0 / 4294967296.0));
+  if (i < n) out[i] = (float)((double)(long long)p[i] * (1.0 / kFix));
 }
 
 static TiledArgs tiled_args(const swin_attn_plan* p) {
@@ -695,23 +956,30 @@ hipError_t launch_tiled_fwd_bf16(const swin_attn_plan* p, const void* qkv, const
   a.o = (bf16*)o;
   a.lse = lse;
   // 4 waves of 32 queries: blocks of 128 queries (the 128-token work items), two workgroups per CU
+  const bool fast = p->nbins <= kTabLds;
   a.work = p->dev.tiled_kv_work;
   const dim3 grid((unsigned)p->tiled_kv_work.size(), (unsigned)p->nh);
   if (p->hd == 32)
-    k_tiled_fwd32<32><<<grid, 256, 0, s>>>(a);
+    fast ? k_tiled_fwd_pipe<32, true><<<grid, 256, 0, s>>>(a) : k_tiled_fwd_pipe<32, false><<<grid, 256, 0, s>>>(a);
   else if (p->hd == 64)
-    k_tiled_fwd32<64><<<grid, 256, 0, s>>>(a);
+    fast ? k_tiled_fwd_pipe<64, true><<<grid, 256, 0, s>>>(a) : k_tiled_fwd_pipe<64, false><<<grid, 256, 0, s>>>(a);
   else
-    k_tiled_fwd32<128><<<grid, 256, 0, s>>>(a);
+    fast ? k_tiled_fwd_pipe<128, true><<<grid, 256, 0, s>>>(a) : k_tiled_fwd_pipe<128, false><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int HD>
 static hipError_t tiled_bwd_launch(const TiledArgs& a, unsigned items, unsigned kv_items, int nh, hipStream_t s) {
-  k_tiled_bwd_dkv<HD><<<dim3(kv_items, (unsigned)nh), 64 * kKvWaves, 0, s>>>(a);
+  if (a.nbins <= kTabLds)
+    k_tiled_bwd_dkv<HD, true><<<dim3(kv_items, (unsigned)nh), 64 * kKvWaves, 0, s>>>(a);
+  else
+    k_tiled_bwd_dkv<HD, false><<<dim3(kv_items, (unsigned)nh), 64 * kKvWaves, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_tiled_bwd_dq<HD><<<dim3(items, (unsigned)nh), 256, 0, s>>>(a);
+  if (a.nbins <= kTabLds)
+    k_tiled_bwd_dq<HD, true><<<dim3(items, (unsigned)nh), 256, 0, s>>>(a);
+  else
+    k_tiled_bwd_dq<HD, false><<<dim3(items, (unsigned)nh), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
