@@ -77,33 +77,6 @@ struct TiledFwdSmem {
   alignas(1024) TiledBuf<HD> buf[2];
 };
 
-// Copies rows [kb*64, kb*64 + 64) of the planes a and b of one window (rows past n repeat row
-// n-1) into the sub-tiles of buffer dst; the 4 HD/32 copies per plane are spread over the NW
-// waves. Wave 0 also copies the block's 64 token codes from the class table csrc.
-template <int HD, int NW = 4>
-__device__ __forceinline__ void tiled_stage(const bf16* a, const bf16* b, int64_t off, int n, int kb, int wv,
-                                            int lane, const int32_t* csrc, unsigned char (*da)[kTB * 64],
-                                            unsigned char (*db)[kTB * 64], int* codes) {
-  constexpr int NSUB = HD / 32;
-  constexpr int COPIES = 4 * NSUB;  // 1 KB copies per plane: 4 slabs of 16 rows per sub-tile
-#pragma unroll
-  for (int t = 0; t < (COPIES + NW - 1) / NW; ++t) {
-    const int i = wv + NW * t;
-    if (COPIES % NW != 0 && i >= COPIES) break;  // wave-uniform
-    const int c = i >> 2, j = i & 3;
-    const int row = 16 * j + (lane >> 2);
-    const int key = kb * kTB + row;
-    const int src_row = key < n ? key : n - 1;
-    const int lc = (lane & 3) ^ swz(row);
-    const int64_t src = (off + src_row) * HD + 32 * c + 8 * lc;
-    lds_copy16(a + src, da[c] + 1024 * j);
-    if (db) lds_copy16(b + src, db[c] + 1024 * j);
-  }
-  if (csrc && wv == 0)
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(csrc + kb * kTB + lane),
-                                     (__attribute__((address_space(3))) void*)codes, 4, 0, 0);
-}
-
 // Copy of rows [kb*64, kb*64 + 64) of one window's plane into the swizzled 32-column sub-tiles
 // dst[c] through buffer loads straight to LDS. The resource spans the window's n rows, so rows
 // past n arrive as zeros. The 4 HD/32 one-kilobyte copies are spread over the NW waves (NW a
@@ -130,8 +103,9 @@ __device__ __forceinline__ uint32_t stage_voff(int wv, int lane) {
   const int row = 16 * (wv & 3) + (lane >> 2);
   return (uint32_t)(row * HD * 2 + 16 * ((lane & 3) ^ swz(row)));
 }
-// The 64 codes of block kb from a class code table (resource over its entries).
-__device__ __forceinline__ void stage_codes(__amdgpu_buffer_rsrc_t src, int kb, int lane, int* dst) {
+// Dwords [kb*64, kb*64 + 64) of a per-token table (codes, LSE, -D; resource over the window's
+// or class's entries, zeros past them) into 64 consecutive LDS dwords.
+__device__ __forceinline__ void stage_dwords(__amdgpu_buffer_rsrc_t src, int kb, int lane, void* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4,
                                            (uint32_t)(4 * (kb * kTB + lane)), 0, 0, 0);
 }
@@ -175,168 +149,6 @@ __device__ __forceinline__ void tile_frag_tr32(const unsigned char* tile, int of
 // taken from the same bf16 probabilities as the PV product (bf16 dot products).
 constexpr float kRescale = 8.f;
 
-template <int HD>
-__global__ __launch_bounds__(256, 2) void k_tiled_fwd32(TiledArgs a) {
-  constexpr int NSUB = HD / 32;  // 32-column sub-tiles (O^T row tiles)
-  constexpr int KS = HD / 16;    // 16-deep k steps of S
-  __shared__ __attribute__((aligned(1024))) TiledFwdSmem<HD> sm;
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lq = lane & 31, hh = lane >> 5;
-  const WorkItem wk = a.work[blockIdx.x];
-  const int h = blockIdx.y;
-  const ClassInfo ci = a.classes[wk.cls];
-  const int n = ci.n;
-  const int64_t off = a.win_off[wk.first];
-  const int q = wk.count * 128 + 32 * wv + lq;  // window-local query of this lane
-  const bool qv = q < n;
-  const int qc = qv ? q : n - 1;
-  const size_t plane = (size_t)a.nh * a.n_tok * HD;
-  const bf16* Qh = a.qkv + (size_t)h * a.n_tok * HD;
-  const bf16* Kh = Qh + plane;
-  const bf16* Vh = Kh + plane;
-  const float* tab = a.table + (int64_t)h * a.nbins;
-  const int code0 = code0_of(a.win);
-  const int cq = token_code(qc, ci.ext, ci.split, a.win);
-  const int nkb = (n + kTB - 1) / kTB;
-  const bool fast = a.nbins <= kTabLds;
-  const int qenc = qv ? enc_query(cq, code0) : kPadQ;
-  const uint32_t lim = 2u * (uint32_t)a.nbins;
-
-  tiled_tab_fill(sm.tab, tab, a.nbins, 256);
-  const int32_t* kcodes = a.codes + wk.codes;  // the class's key codes
-  tiled_stage<HD, 4>(Kh, Vh, off, n, 0, wv, lane, kcodes, sm.buf[0].k, sm.buf[0].v, sm.buf[0].codes);
-  // the lane's query: B operand of S^T, hd 16 s + 8 hh .. + 7 for k step s
-  bf16x8 bq[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) bq[s] = *(const bf16x8*)(Qh + (off + qc) * HD + 16 * s + 8 * hh);
-  vm_wait(0);
-#pragma unroll
-  for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(bq[s]));
-
-  // K fragment of step s: row 32 t + lq of sub-tile s / 2, logical chunk 2 (s % 2) + hh (rows a
-  // multiple of 16 apart share a swizzle)
-  const int k_off0 = lq * 64 + 16 * (hh ^ swz(lq)), k_off1 = lq * 64 + 16 * ((2 + hh) ^ swz(lq));
-  // V^T fragments: the 16-lane group lane / 16 reads hd columns 16 ((lane / 16) % 2) + i of the
-  // keys 4 hh + r and 8 + 4 hh + r (r < 4) of a 16-key step; lane i addresses row i / 4
-  const int i16 = lane & 15;
-  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
-  const int v_offa = swz_off(4 * hh + (i16 >> 2), vcol), v_offb = swz_off(8 + 4 * hh + (i16 >> 2), vcol);
-  bf16x2 ones2;
-  ones2[0] = to_bf16(1.f);
-  ones2[1] = to_bf16(1.f);
-  float m_run = -INFINITY, l = 0.f;  // -inf: no allowed key seen yet
-  f32x16 oacc[NSUB];
-#pragma unroll
-  for (int d = 0; d < NSUB; ++d) oacc[d] = f32x16{};
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    vm_wait(0);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const TiledBuf<HD>& cur = sm.buf[kb & 1];
-    const float m_eff = m_run == -INFINITY ? 0.f : m_run;
-    // bias - m for the lane's 32 keys, read before the next block's copies are issued
-    f32x16 sacc[2];
-    int kk[32];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int4 ck = *(const int4*)(cur.codes + 32 * t + 8 * j + 4 * hh);
-        kk[16 * t + 4 * j] = ck.x;
-        kk[16 * t + 4 * j + 1] = ck.y;
-        kk[16 * t + 4 * j + 2] = ck.z;
-        kk[16 * t + 4 * j + 3] = ck.w;
-      }
-    if (fast) {
-#pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        const uint32_t ib = min((uint32_t)(qenc - kk[r]), lim);
-        const uint32_t raw = *(const unsigned short*)((const char*)sm.tab + ib);
-        sacc[r >> 4][r & 15] = half_lo_minus(raw, m_eff);  // masked pairs and queries past n: -inf
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        const float b = tiled_bias(cq, kk[r], code0, tab);
-        sacc[r >> 4][r & 15] = (qv ? b : 0.f) - m_eff;
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int t = 0; t < 2; ++t) asm volatile("" : "+v"(sacc[t]) : : "memory");
-    if (kb + 1 < nkb) {
-      TiledBuf<HD>& nx = sm.buf[(kb + 1) & 1];
-      tiled_stage<HD, 4>(Kh, Vh, off, n, kb + 1, wv, lane, kcodes, nx.k, nx.v, nx.codes);
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        sacc[t] = mfma32(*(const bf16x8*)(cur.k[s >> 1] + 2048 * t + ((s & 1) ? k_off1 : k_off0)), bq[s], sacc[t]);
-    float mb = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mb = fmaxf(mb, sacc[t][r]);
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    // move m when the block's maximum exceeds it by more than kRescale, or to the first
-    // allowed key of the row
-    const bool need = mb > kRescale || (m_run == -INFINITY && mb != -INFINITY);
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float d = need ? mb : 0.f;
-      const float corr = fast_exp2(-d);
-#pragma unroll
-      for (int dd = 0; dd < NSUB; ++dd) oacc[dd] *= corr;
-      l *= corr;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[t][r] -= d;
-      m_run = need ? m_eff + d : m_run;
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      // P^T operands of the 16-key steps 32 t and 32 t + 16: the lane's rows 16 u + 4 hh + i
-      // and 16 u + 8 + 4 hh + i
-      bf16x8 pb[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pb[u][i] = to_bf16(fast_exp2(sacc[t][8 * u + i]));
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[u][2 * e], pb[u][2 * e + 1]}, ones2, l, false);
-#pragma unroll
-      for (int sc = 0; sc < NSUB; ++sc) {
-        bf16x8 f0, f1;
-        tile_frag_tr32(cur.v[sc] + 2048 * t, v_offa, v_offb, f0, f1);
-        oacc[sc] = mfma32(f0, pb[0], oacc[sc]);
-        oacc[sc] = mfma32(f1, pb[1], oacc[sc]);
-      }
-    }
-  }
-  l += __shfl_xor(l, 32);
-  if (qv) {
-    const float inv = __builtin_amdgcn_rcpf(l);
-    const int64_t grow = a.perm[off + q];
-    bf16* orow = a.o + grow * a.C + (int64_t)h * HD;
-    // O^T rows hd 32 sc + 8 j + 4 hh + i of the lane's query
-#pragma unroll
-    for (int sc = 0; sc < NSUB; ++sc)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x4 o4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] = to_bf16(oacc[sc][4 * j + i] * inv);
-        *(bf16x4*)(orow + 32 * sc + 8 * j + 4 * hh) = o4;
-      }
-    if (hh == 0) a.lse[(int64_t)h * a.n_tok + off + q] = m_run + fast_log2(l);
-  }
-}
-
 // LDS of the pipelined forward: K runs one block ahead of V, codes two (ring of four).
 template <int HD>
 struct FwdPipeSmem {
@@ -346,13 +158,14 @@ struct FwdPipeSmem {
   int codes[4][kTB];
 };
 
-// The forward of k_tiled_fwd32, software-pipelined so that each wave's matrix and vector work
+// The forward, software-pipelined so that each wave's matrix and vector work
 // overlap: in step kb the S MFMAs of block kb+1 run beside the exponentials of block kb, and the
 // PV MFMAs of block kb beside the bias reads of block kb+2. Buffers: K(kb+1) and V(kb) are read
 // in step kb while K(kb+2), V(kb+1) and the codes of block kb+3 are copied in.
-// FAST: the bias table is in LDS (nbins <= kTabLds; the code tables are then encoded).
+// FAST: the bias table is in LDS (nbins <= kTabLds; the code tables are then encoded). The
+// global-table variant needs more registers than two workgroups per CU leave at head_dim 128.
 template <int HD, bool FAST>
-__global__ __launch_bounds__(256, 2) void k_tiled_fwd_pipe(TiledArgs a) {
+__global__ __launch_bounds__(256, (FAST || HD < 128) ? 2 : 1) void k_tiled_fwd_pipe(TiledArgs a) {
   constexpr int NSUB = HD / 32;
   constexpr int KS = HD / 16;
   __shared__ __attribute__((aligned(1024))) FwdPipeSmem<HD> sm;
@@ -382,12 +195,13 @@ __global__ __launch_bounds__(256, 2) void k_tiled_fwd_pipe(TiledArgs a) {
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + off * HD, (uint32_t)n * HD * 2);
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes + wk.codes, (uint32_t)nr * 4);  // the class's key codes
   const uint32_t voff = stage_voff<HD>(wv, lane);
+  const __amdgpu_buffer_rsrc_t rtab = make_rsrc(tab, (uint32_t)a.nbins * 4);  // global-table variant
   auto stage_k = [&](int j) { stage_plane<HD, 4>(rk, j, wv, voff, sm.k[j & 1]); };
   auto stage_v = [&](int j) { stage_plane<HD, 4>(rv, j, wv, voff, sm.v[j & 1]); };
   auto stage_c = [&](int j) {
-    if (wv == 0) stage_codes(rc, j, lane, sm.codes[j & 3]);
+    if (wv == 0) stage_dwords(rc, j, lane, sm.codes[j & 3]);
   };
-  // bias - m of the lane's 32 keys of block j (rows 32 t + 8 r/4 ... as in k_tiled_fwd32)
+  // bias - m of the lane's 32 keys of block j
   auto bias_init = [&](int j, float m_eff, f32x16 (&S)[2]) {
     if constexpr (FAST) {
 #pragma unroll
@@ -404,22 +218,21 @@ __global__ __launch_bounds__(256, 2) void k_tiled_fwd_pipe(TiledArgs a) {
           }
         }
     } else {
-      int kk[32];
+      // the head's table through a buffer resource (32-bit offsets), four pairs at a time
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int4 ck = *(const int4*)(sm.codes[j & 3] + 32 * t + 8 * jj + 4 * hh);
-          kk[16 * t + 4 * jj] = ck.x;
-          kk[16 * t + 4 * jj + 1] = ck.y;
-          kk[16 * t + 4 * jj + 2] = ck.z;
-          kk[16 * t + 4 * jj + 3] = ck.w;
-        }
+          const int kk[4] = {ck.x, ck.y, ck.z, ck.w};
 #pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        const float b = tiled_bias(cq, kk[r], code0, tab);
-        S[r >> 4][r & 15] = (qv ? b : 0.f) - m_eff;
-      }
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t idx = (uint32_t)((cq & 0xffffff) - (kk[i] & 0xffffff) + code0);
+            const float tv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rtab, 4 * idx, 0, 0));
+            const float b = (cq >> 24) != (kk[i] >> 24) ? -INFINITY : tv * kLog2e;
+            S[t][4 * jj + i] = (qv ? b : 0.f) - m_eff;
+          }
+        }
     }
   };
 
@@ -604,8 +417,17 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
   const uint32_t lim = 2u * (uint32_t)a.nbins;
 
   tiled_tab_fill(sm.tab, tab, a.nbins, 256);
-  const int32_t* kcodes = a.codes + wk.codes;  // the class's key codes
-  tiled_stage<HD>(Kh, Vh, off, n, 0, wv, lane, kcodes, sm.buf[0].k, sm.buf[0].v, sm.buf[0].codes);
+  const int nr = (n + kCodeRound - 1) / kCodeRound * kCodeRound;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + off * HD, (uint32_t)n * HD * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + off * HD, (uint32_t)n * HD * 2);
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes + wk.codes, (uint32_t)nr * 4);  // the class's key codes
+  const uint32_t voff = stage_voff<HD>(wv, lane);
+  auto stage = [&](int j, TiledBuf<HD>& b) {
+    stage_plane<HD, 4>(rk, j, wv, voff, b.k);
+    stage_plane<HD, 4>(rv, j, wv, voff, b.v);
+    if (wv == 0) stage_dwords(rc, j, lane, b.codes);
+  };
+  stage(0, sm.buf[0]);
   bf16x8 bq[NSUB], bd[NSUB];
 #pragma unroll
   for (int c = 0; c < NSUB; ++c) {
@@ -654,7 +476,7 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
     for (int kt = 0; kt < 4; ++kt) asm volatile("" : "+v"(s[kt]) : : "memory");
     if (kb + 1 < nkb) {
       TiledBuf<HD>& nx = sm.buf[(kb + 1) & 1];
-      tiled_stage<HD>(Kh, Vh, off, n, kb + 1, wv, lane, kcodes, nx.k, nx.v, nx.codes);
+      stage(kb + 1, nx);
     }
     f32x4 ds[4];
 #pragma unroll
@@ -698,23 +520,6 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
       *(bf16x4*)(row + 32 * sc + 4 * g) = o0;
       *(bf16x4*)(row + 32 * sc + 16 + 4 * g) = o1;
     }
-  }
-}
-
-// Copies query block qb of q and dO (rows past n repeat row n-1) and its LSE, -D and codes.
-template <int HD, int NW>
-__device__ __forceinline__ void tiled_stage_q(const TiledArgs& a, const bf16* Qh, const bf16* dOh, int h, int64_t off,
-                                              int n, int qb, int wv, int lane, const int32_t* qcodes,
-                                              TiledQBuf<HD>& b) {
-  tiled_stage<HD, NW>(Qh, dOh, off, n, qb, wv, lane, qcodes, b.q, b.d, b.codes);
-  if (wv == 1) {
-    const int qq = qb * kTB + lane;
-    const int qs = qq < n ? qq : n - 1;
-    // LSE and -D of the block's queries: straight into LDS, one dword per lane
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.lse + (int64_t)h * a.n_tok + off + qs),
-                                     (__attribute__((address_space(3))) void*)b.lse, 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.dd + (int64_t)h * a.n_tok + off + qs),
-                                     (__attribute__((address_space(3))) void*)b.nd, 4, 0, 0);
   }
 }
 
@@ -766,9 +571,25 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
   for (int i = threadIdx.x; i <= a.nbins; i += 64 * NW) bins[i] = 0ull;
   const uint32_t bins_base = lds_addr(bins);
   tiled_tab_fill(sm.tab, tab, a.nbins, 64 * NW);
-  // the class's query codes follow its key codes
-  const int32_t* qcodes = a.codes + wk.codes + (n + kCodeRound - 1) / kCodeRound * kCodeRound;
-  tiled_stage_q<HD, NW>(a, Qh, dOh, h, off, n, 0, wv, lane, qcodes, buf[0]);
+  // query block j of q and dO (zeros past n) with its codes (the class's query codes follow its
+  // key codes), LSE and -D
+  const int nr = (n + kCodeRound - 1) / kCodeRound * kCodeRound;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + off * HD, (uint32_t)n * HD * 2);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(dOh + off * HD, (uint32_t)n * HD * 2);
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes + wk.codes + nr, (uint32_t)nr * 4);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + (int64_t)h * a.n_tok + off, (uint32_t)n * 4);
+  const __amdgpu_buffer_rsrc_t rn = make_rsrc(a.dd + (int64_t)h * a.n_tok + off, (uint32_t)n * 4);
+  const uint32_t voff = stage_voff<HD>(wv, lane);
+  auto stage_q = [&](int j, TiledQBuf<HD>& b) {
+    stage_plane<HD, NW>(rq, j, wv, voff, b.q);
+    stage_plane<HD, NW>(rd, j, wv, voff, b.d);
+    if (wv == 0) stage_dwords(rc, j, lane, b.codes);
+    if (wv == 1) {
+      stage_dwords(rl, j, lane, b.lse);
+      stage_dwords(rn, j, lane, b.nd);
+    }
+  };
+  stage_q(0, buf[0]);
   // the lane's key and value: B operands of S = q K^T and dP = dO V^T
   bf16x8 bk[NSUB], bv[NSUB];
 #pragma unroll
@@ -837,7 +658,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) asm volatile("" : "+v"(s[qt]), "+v"(ndv[qt]) : : "memory");
-    if (qb + 1 < nqb) tiled_stage_q<HD, NW>(a, Qh, dOh, h, off, n, qb + 1, wv, lane, qcodes, buf[(qb + 1) & 1]);
+    if (qb + 1 < nqb) stage_q(qb + 1, buf[(qb + 1) & 1]);
     f32x4 p[4], ds[4];
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {

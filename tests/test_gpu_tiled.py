@@ -44,6 +44,10 @@ FWD_CASES = [
     cfg("hd128", (1, 32, 48), 512, 4, (1, 8, 8), ((0, 4, 4),)),
     # head_dim 128 and 576-token windows
     cfg("hd128_w24", (1, 48, 48), 256, 2, (1, 24, 24), ((0, 12, 12),)),
+    # 40 x 40 windows: 79 x 79 = 6241 bins, over the 4096 an LDS table holds (global-table kernels)
+    cfg("w40_table6241", (1, 80, 80), 128, 2, (1, 40, 40), ((0, 20, 20),)),
+    # global attention at head_dim 128 with the table in global memory (9401 bins)
+    cfg("global2400_hd128", (1, 40, 60), 256, 2, (1, 40, 60), ((0, 0, 0),), periodic=0),
 ]
 
 
@@ -63,7 +67,7 @@ def _check_grads(got, ref, label):
 
 
 # every forward case whose bias table fits the backward's 8192 LDS bins
-BWD_CASES = [c for c in FWD_CASES if c.name != "global2400"] + [
+BWD_CASES = [c for c in FWD_CASES if not c.name.startswith("global2400")] + [
     # 256-token windows with head_dim 32 (over the one-tile backward's 160 tokens)
     cfg("w16x16", (1, 32, 48), 128, 4, (1, 16, 16), ((0, 0, 0), (0, 8, 8))),
     # 3-D windows with 4 levels: 4 x 12 x 12 = 576 tokens, 7 x 23 x 23 = 3703 bins, batch 2
