@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
   const int n = ci.n;
   const int key = 16 * kt + li;
   const float* tab = a.table + (int64_t)h * a.nbins;
-  if (tid < wk.count) offs[tid] = a.win_off[a.class_win[wk.first + tid]];
+  for (int i = tid; i < wk.count; i += NT) offs[i] = a.win_off[a.class_win[wk.first + i]];
   if (tid < 16 * NKT) codes[tid] = tid < n ? token_code(tid, ci.ext, ci.split, a.win) : 0;
   const int64_t off0 = a.win_off[a.class_win[wk.first]];
 

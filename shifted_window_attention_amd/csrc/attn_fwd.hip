@@ -89,7 +89,7 @@ __global__ __launch_bounds__(64 * NKT, FwdSmem<NKT>::MIN_BLOCKS) void k_attn_fwd
   const bool qv = q < n;
   const float* tab = a.table + (int64_t)h * a.nbins;
   for (int i = threadIdx.x; i < a.nbins; i += 64 * NKT) sm.tab[i] = tab[i] * kLog2e;
-  if (threadIdx.x < wk.count) sm.offs[threadIdx.x] = a.win_off[a.class_win[wk.first + threadIdx.x]];
+  for (int i = threadIdx.x; i < wk.count; i += 64 * NKT) sm.offs[i] = a.win_off[a.class_win[wk.first + i]];
   if (threadIdx.x < 16 * NKT)
     sm.codes[threadIdx.x] = threadIdx.x < n ? token_code(threadIdx.x, ci.ext, ci.split, a.win) : 0;
   // V rows past the copied 16 NKT (odd tile count) feed the last PV chunk: keep them zero

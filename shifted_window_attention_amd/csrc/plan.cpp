@@ -348,7 +348,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
       p->class_win[p->classes[c].first + fill[c]++] = (int32_t)w;
     }
   }
-  build_work(p->classes, p->nh, 1024, 64, p->fwd_work, p->fwd_ranges);
+  build_work(p->classes, p->nh, 1024, kMaxChunk, p->fwd_work, p->fwd_ranges);
   if (p->tiled || p->tiled_bwd) {
     // token-code tables of every class: key codes, then query codes, kCodeRound-padded
     const bool enc = p->nbins <= kTabLds;
