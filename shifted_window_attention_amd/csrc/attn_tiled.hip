@@ -4,24 +4,23 @@
 // w >= 32, and BEAST's models use windows of thousands of tokens) and for wider heads
 // (TERRA Table V: head_dim 128).
 //
-// Forward: one workgroup per (window, block of 64 queries, head), a wave per 16 queries. The
-// window's keys and values stream through LDS in blocks of 64 rows, double-buffered by direct
-// global->LDS copies, and the softmax is the online one: per block the running row max m,
-// row sum l and output accumulator are rescaled by exp2(m_old - m_new). Logits are computed
-// transposed (S^T = K Q^T, v_mfma_f32_16x16x32_bf16), so a lane holds one query and 4 keys of
-// every 16-key tile, and its probabilities are directly the B operand of O^T = V^T P^T (the
-// V^T operand comes from the transposing LDS read); the row sums come from the matrix core
-// (an all-ones operand against the same bf16 P). Bias + mask come from the tokens' local
-// offset codes and the head's relative-position table in global memory.
+// Forward (k_tiled_fwd_pipe): one workgroup per (window, block of 128 queries, head), a wave
+// per 32 queries. The window's keys and values stream through LDS in blocks of 64 rows
+// (buffer loads straight to LDS), and the softmax is the online one with a lazily moved
+// exponent offset. Logits are computed transposed (S^T = K Q^T, v_mfma_f32_32x32x16_bf16), so
+// a lane holds one query and 32 keys of each block, and its probabilities are directly the B
+// operand of O^T = V^T P^T (the V^T operand comes from the transposing LDS read). Bias + mask
+// come from per-class token-code tables and the head's relative-position table (fp16 in LDS
+// when it has at most kTabLds bins, else fp32 in global memory).
 //
 // Backward (recomputing P from q, k and the saved LSE; dS = P (dP - D), D = rowsum(dO o)):
 //   k_tiled_bwd_dkv: one workgroup per (window, block of 128 keys, head), a wave per 16 keys;
 //     query blocks (q, dO, LSE, -D, codes) stream through LDS; dV^T += dO^T P and
 //     dK^T += q^T dS accumulate in registers; dT is binned per workgroup in LDS as 64-bit
-//     fixed point (2^-32 units), then added to a global fixed-point accumulator. Integer sums
-//     do not depend on the order of the additions, so dT is bitwise reproducible.
-//   k_tiled_bwd_dq: one workgroup per (window, block of 64 queries, head), the forward's
-//     layout: key blocks stream through LDS and dQ^T += K^T dS^T.
+//     fixed point (units of 2^-20), then added to a global fixed-point accumulator. Integer
+//     sums do not depend on the order of the additions, so dT is bitwise reproducible.
+//   k_tiled_bwd_dq: one workgroup per (window, block of 64 queries, head), a wave per 16
+//     queries on v_mfma_f32_16x16x32_bf16: key blocks stream through LDS and dQ^T += K^T dS^T.
 #include "device_common.h"
 #include "swin_internal.h"
 
@@ -47,7 +46,7 @@ struct TiledArgs {
   const bf16* dO;           // [nh][n_tok][hd] window-major
   const float* dd;          // -D = -rowsum(dO o), [nh][n_tok]
   bf16* dqkv;               // [n_tok][3C], grid order
-  unsigned long long* dbias_acc;  // [nh][nbins] fixed point (2^-32 units, two's complement)
+  unsigned long long* dbias_acc;  // [nh][nbins] fixed point (units of 1/kFix, two's complement)
   float tau;
 };
 
@@ -58,11 +57,6 @@ struct TiledBuf {
   int codes[kTB];
 };
 
-__device__ __forceinline__ float fast_bias(int Q, int K, const _Float16* tab16, uint32_t lim) {
-  const uint32_t ib = min((uint32_t)(Q - K), lim);
-  return (float)*(const _Float16*)((const char*)tab16 + ib);
-}
-
 // Fills the LDS table (bins, then -inf) when it fits; made visible by the first barrier.
 __device__ __forceinline__ void tiled_tab_fill(_Float16* dst, const float* tab, int nbins, int nthreads) {
   if (nbins > kTabLds) return;
@@ -70,7 +64,8 @@ __device__ __forceinline__ void tiled_tab_fill(_Float16* dst, const float* tab, 
     dst[i] = i < nbins ? (_Float16)(tab[i] * kLog2e) : (_Float16)(-INFINITY);
 }
 
-// The table comes first so that its reads take their base from the instruction's offset field.
+// LDS of the dQ kernel. The table comes first so that its reads take their base from the
+// instruction's offset field.
 template <int HD>
 struct TiledFwdSmem {
   _Float16 tab[kTabLds + 8];
