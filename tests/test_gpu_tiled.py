@@ -44,6 +44,11 @@ FWD_CASES = [
     cfg("hd128", (1, 32, 48), 512, 4, (1, 8, 8), ((0, 4, 4),)),
     # head_dim 128 and 576-token windows
     cfg("hd128_w24", (1, 48, 48), 256, 2, (1, 24, 24), ((0, 12, 12),)),
+    # head_dim 128, ragged 16 x 16 windows: 40 = 2*16 + 8 rows, 52 = 3*16 + 4 columns (windows of 256, 128,
+    # 64 and 32 tokens, so some end inside a 64-token block)
+    cfg("hd128_ragged", (1, 40, 52), 256, 2, (1, 16, 16), ((0, 8, 8),)),
+    # head_dim 64, ragged 12 x 20 windows (240, 80, 72 and 24 tokens)
+    cfg("hd64_ragged", (1, 30, 44), 128, 2, (1, 12, 20), ((0, 6, 10),)),
     # 40 x 40 windows: 79 x 79 = 6241 bins, over the 4096 an LDS table holds (global-table kernels)
     cfg("w40_table6241", (1, 80, 80), 128, 2, (1, 40, 40), ((0, 20, 20),)),
     # global attention at head_dim 128 with the table in global memory (9401 bins)
