@@ -175,7 +175,7 @@ __device__ __forceinline__ void epilogue_f32(const f32x16 (&acc)[NtCfg<BM, BN>::
 }
 
 template <int BM, int BN>
-__global__ __launch_bounds__(256, 2) void k_gemm_nt(const bf16* __restrict__ A, int64_t lda,
+__global__ __launch_bounds__(256, BM == 128 ? 3 : 2) void k_gemm_nt(const bf16* __restrict__ A, int64_t lda,
                                                     const int32_t* __restrict__ a_rows,
                                                     const bf16* __restrict__ B, int64_t ldb, int64_t M, int N,
                                                     int K, EpiParams ep) {
@@ -576,9 +576,17 @@ __global__ void k_transpose_bf16(const bf16* __restrict__ in, bf16* __restrict__
 // ---------------------------------------------------------------------------
 static hipError_t gemm_nt(const bf16* A, int64_t lda, const int32_t* a_rows, const bf16* B, int64_t ldb, int64_t M,
                           int N, int K, const EpiParams& ep, hipStream_t s) {
-  constexpr int BM = 256, BN = 128;
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  k_gemm_nt<BM, BN><<<xcd_grid(tiles), 256, 0, s>>>(A, lda, a_rows, B, ldb, M, N, K, ep);
+  if (ep.dot_o) {
+    // the row-dot epilogue holds a whole column of dot_o chunks per thread: 128-row tiles keep
+    // three workgroups per CU (measured faster than 256 x 128 for this epilogue only)
+    constexpr int BM = 128, BN = 128;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    k_gemm_nt<BM, BN><<<xcd_grid(tiles), 256, 0, s>>>(A, lda, a_rows, B, ldb, M, N, K, ep);
+  } else {
+    constexpr int BM = 256, BN = 128;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    k_gemm_nt<BM, BN><<<xcd_grid(tiles), 256, 0, s>>>(A, lda, a_rows, B, ldb, M, N, K, ep);
+  }
   return hipGetLastError();
 }
 
