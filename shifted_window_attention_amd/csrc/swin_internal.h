@@ -91,8 +91,8 @@ struct DevTables {
   ClassInfo* classes = nullptr;  // [n_cls]
   WorkItem* fwd_work = nullptr;  // [n_fwd_work]
   WorkItem* bwd_work = nullptr;  // [n_bwd_work]
-  WorkItem* tiled_work = nullptr;  // [n_tiled_work] (class, window, 64-token block) of the tiled path
-  WorkItem* tiled_kv_work = nullptr;  // (class, window, 128-token block): the tiled dK/dV kernel
+  WorkItem* tiled_work = nullptr;  // [n_tiled_work] (class, window, 64-token block): the tiled dQ kernel
+  WorkItem* tiled_kv_work = nullptr;  // (class, window, 128-token block): the tiled forward and dK/dV kernels
   int32_t* tiled_codes = nullptr;     // per class: key codes, then query codes (tiled path)
 };
 
