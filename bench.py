@@ -516,8 +516,9 @@ def main():
                          "host recipe: starts in seconds, for profiler runs; implies --no-cpu-baseline")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this library has no multi-GPU path "
-              "(see DESIGN.md for how the workload would shard); got --gpus %d" % args.gpus, file=sys.stderr)
+        print("bench.py runs on one GPU only: this library has no multi-GPU path (the window decomposition "
+              "would shard by lat stripes, one rank per GPU, with the token routes exchanging boundary windows); "
+              "got --gpus %d" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
