@@ -205,10 +205,10 @@ swin_status swin_attn_fwd(const swin_attn_plan* plan, const void* x, const void*
  * a fixed order (on the tiled kernels every dS term of dT is rounded to an
  * integer multiple of 2^-20, saturating at magnitude 2^11, and the integers are
  * summed exactly, in any order), so repeated calls are bitwise identical.
- * Only SWIN_BF16 is supported (SWIN_ERR_UNSUPPORTED for fp32), with relative-
- * position tables of at most 8192 bins per head when a window has more than
- * 160 tokens, head_dim is 64/128 or the table exceeds 2048 bins
- * (SWIN_ERR_UNSUPPORTED otherwise).
+ * Tables of more than 8192 bins per head (windows of thousands of tokens) are
+ * accumulated with global 64-bit integer atomics instead of workgroup LDS bins:
+ * slower, equally exact. Only SWIN_BF16 is supported (SWIN_ERR_UNSUPPORTED for
+ * fp32).
  */
 swin_status swin_attn_bwd(const swin_attn_plan* plan, const void* dy, const void* x, const void* w_qkv,
                           const void* w_proj, const float* bias_table, const void* saved, void* dx,

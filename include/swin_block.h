@@ -91,10 +91,8 @@ swin_status swin_block_fwd(const swin_block_plan* plan, const void* x, const swi
 
 /* Backward of swin_block_fwd with the same x and parameters and the saved state it wrote:
  * dx ([B, D, H, W, C] bf16, must not alias dy or x) and every parameter gradient.
- * Reductions run in a fixed order: repeated calls are bitwise identical. The attention
- * module's limits apply (SWIN_ERR_UNSUPPORTED for a relative-position table over 8192 bins
- * on its tiled backward). Errors as for swin_block_fwd, plus SWIN_ERR_WORKSPACE when ws is
- * smaller than bwd_ws. */
+ * Reductions run in a fixed order: repeated calls are bitwise identical. Errors as for
+ * swin_block_fwd, plus SWIN_ERR_WORKSPACE when ws is smaller than bwd_ws. */
 swin_status swin_block_bwd(const swin_block_plan* plan, const void* dy, const void* x,
                            const swin_block_params* params, const void* saved, void* dx,
                            const swin_block_grads* grads, void* ws, size_t ws_bytes, void* stream);

@@ -563,7 +563,13 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
   const int kenc = kv ? enc_key(ck) : kPadK;
   const uint32_t lim = 2u * (uint32_t)a.nbins;
 
-  for (int i = threadIdx.x; i <= a.nbins; i += 64 * NW) bins[i] = 0ull;
+  // tables over kTiledMaxBwdBins bins (global-table variant only): every allowed pair's term goes
+  // straight to the global accumulator (64-bit integer atomics: exact, order-free) and the LDS bins
+  // stay unused
+  const bool global_bins = !FAST && a.nbins > kTiledMaxBwdBins;
+  unsigned long long* acc = a.dbias_acc + (int64_t)h * a.nbins;
+  if (!global_bins)
+    for (int i = threadIdx.x; i <= a.nbins; i += 64 * NW) bins[i] = 0ull;
   const uint32_t bins_base = lds_addr(bins);
   tiled_tab_fill(sm.tab, tab, a.nbins, 64 * NW);
   // query block j of q and dO (zeros past n) with its codes (the class's query codes follow its
@@ -681,7 +687,12 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
         } else {
           // an allowed pair (v != 0 only then)
           const int bin = (cqs[4 * qt + i] & 0xffffff) - (ck & 0xffffff) + code0;
-          if (v != 0) lds_add_u64(&bins[bin], (uint64_t)(int64_t)v);
+          if (v != 0) {
+            if (global_bins)
+              atomicAdd(acc + bin, (unsigned long long)(int64_t)v);
+            else
+              lds_add_u64(&bins[bin], (uint64_t)(int64_t)v);
+          }
         }
       }
     // dV^T += dO^T P and dK^T += q^T dS: B operands are the lane's key column with the
@@ -728,9 +739,9 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
       *(bf16x4*)(row + 2 * a.C + 32 * sc + 16 + 4 * g) = v1;
     }
   }
+  if (global_bins) return;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the bin additions above are inline assembly
   __syncthreads();
-  unsigned long long* acc = a.dbias_acc + (int64_t)h * a.nbins;
   for (int i = threadIdx.x; i < a.nbins; i += 64 * NW) {
     const unsigned long long v = bins[i];
     if (v) atomicAdd(acc + i, v);

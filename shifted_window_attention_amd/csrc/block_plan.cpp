@@ -160,8 +160,6 @@ swin_status swin_block_bwd(const swin_block_plan* plan, const void* dy, const vo
       !gr->w1 || !gr->w2)
     return fail(SWIN_ERR_ARG, "NULL gradient pointer");
   if (dx == dy || dx == x) return fail(SWIN_ERR_ARG, "dx must not alias dy or x");
-  if (plan->attn->tiled_bwd && plan->attn->nbins > swin::kTiledMaxBwdBins)
-    return fail(SWIN_ERR_UNSUPPORTED, "backward supports relative-position tables of at most 8192 bins");
   if (!ws || ws_bytes < plan->w_total) return fail(SWIN_ERR_WORKSPACE, "backward workspace too small");
   const swin_attn_plan* ap = plan->attn;
   hipStream_t s = (hipStream_t)stream;

@@ -496,8 +496,6 @@ swin_status swin_attn_bwd(const swin_attn_plan* plan, const void* dy, const void
   if (!dy || !x || !w_qkv || !w_proj || !bias_table || !saved || !dx || !dw_qkv || !dw_proj || !dbias_table)
     return fail(SWIN_ERR_ARG, "NULL input or output pointer");
   if (dx == dy || dx == x) return fail(SWIN_ERR_ARG, "dx must not alias dy or x");
-  if (plan->tiled_bwd && plan->nbins > kTiledMaxBwdBins)
-    return fail(SWIN_ERR_UNSUPPORTED, "backward supports relative-position tables of at most 8192 bins");
   if (!ws || ws_bytes < plan->bwd_total) return fail(SWIN_ERR_WORKSPACE, "backward workspace too small");
   return hip_status(launch_bwd_bf16(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_qkv, dw_proj,
                                     db_proj, dbias_table, ws, (hipStream_t)stream),

@@ -82,7 +82,8 @@ constexpr int kMaxFwdTiles = 16;  // forward: windows of up to 256 tokens
 constexpr int kMaxBwdTiles = 10;  // backward: windows of up to 160 tokens (LDS budget)
 constexpr int kMaxChunk = 64;     // windows per attention work item
 constexpr int kMaxBins = 2048;    // bias-table bins per head (windows of <= 256 tokens have < 2048)
-constexpr int kTiledMaxBwdBins = 8192;  // tiled backward: bias-gradient bins per head held in LDS
+constexpr int kTiledMaxBwdBins = 8192;  // tiled backward: bias-gradient bins per head held in LDS (larger
+                                        // tables are accumulated with global integer atomics)
 
 struct DevTables {
   int32_t* perm = nullptr;       // [n_tok] window-major slot -> grid row
