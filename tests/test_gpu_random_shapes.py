@@ -1,0 +1,70 @@
+"""A seeded sweep of random module shapes against the fp64 oracle, through the C ABI: 2-D and
+3-D grids, ragged edges, head_dim 32/64/128, batch 1-2, every periodic combination of the lat
+and lon axes, windows from 16 to over 1000 tokens (so both the one-tile and the tiled kernels,
+tables held in LDS and in global memory), one or two chained modules. Same bars as the other
+parity tests: per-token outputs max-abs <= 2e-2, reduced gradients 2e-2 * max(1, |ref|_inf)."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import log, run_chain
+from tests.oracle_runner import chain_full
+from workloads import make_inputs
+from workloads.configs import SwinConfig
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def random_configs(n=16, seed=11):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        hd = int(rng.choice([32, 64, 128]))
+        heads = int(rng.choice({32: [2, 4], 64: [1, 2, 3], 128: [1, 2]}[hd]))
+        three_d = rng.random() < 0.3
+        D = int(rng.integers(2, 5)) if three_d else 1
+        large = rng.random() < 0.35  # windows of 33-60 x 33-72: tables over 4096 bins, many over 8192
+        if large:
+            three_d = False
+            D = 1
+            H, W = int(rng.integers(33, 61)), int(rng.integers(33, 73))
+        else:
+            H, W = int(rng.integers(8, 64)), int(rng.integers(8, 72))
+        wd = int(rng.integers(1, D + 1)) if three_d else 1
+        if large:
+            wh, ww = int(rng.integers(33, H + 1)), int(rng.integers(33, W + 1))
+        else:
+            wh, ww = int(rng.integers(4, min(H, 40) + 1)), int(rng.integers(4, min(W, 48) + 1))
+        batch = int(rng.integers(1, 3))
+        n_tok = batch * D * H * W
+        if n_tok > 8000 or wd * wh * ww > 4400:
+            continue
+        shift = tuple(int(rng.integers(0, w)) if g > w else 0 for g, w in zip((D, H, W), (wd, wh, ww)))
+        shifts = ((0, 0, 0), shift) if rng.random() < 0.4 else (shift,)
+        periodic = int(rng.choice([0, 2, 4, 6]))
+        name = "r%d_hd%d_g%dx%dx%d_w%dx%dx%d" % (len(out), hd, D, H, W, wd, wh, ww)
+        out.append(SwinConfig(name=name, batch=batch, grid=(D, H, W), channels=hd * heads, heads=heads,
+                              window=(wd, wh, ww), shifts=shifts, dtype="bf16", backward=True, periodic=periodic,
+                              description=name))
+    return out
+
+
+CASES = random_configs()
+
+
+@pytest.mark.parametrize("c", CASES, ids=lambda c: c.name)
+def test_random_shape_vs_oracle(c):
+    log("random shape", c.name, "batch", c.batch, "heads", c.heads, "shifts", c.shifts, "periodic", c.periodic)
+    inp = make_inputs(c)
+    got = run_chain(c, inp)
+    ref = chain_full(c, inp)
+    ey = float(np.abs(got["y"] - ref["y"]).max())
+    edx = float(np.abs(got["dx"] - ref["dx"]).max())
+    log("  y max-abs %.3e  dx max-abs %.3e" % (ey, edx))
+    assert ey <= TOL and edx <= TOL
+    for i, (gm, rm) in enumerate(zip(got["grads"], ref["grads"])):
+        for k in ("w_qkv", "b_qkv", "w_proj", "b_proj", "table"):
+            r, g = np.asarray(rm[k]).reshape(-1), np.asarray(gm[k]).reshape(-1)
+            err, bound = float(np.abs(g - r).max()), TOL * max(1.0, float(np.abs(r).max()))
+            assert err <= bound, (c.name, i, k, err, bound)
