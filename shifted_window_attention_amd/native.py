@@ -4,6 +4,14 @@ include/swin_offload.h, include/swin_route.h) and argument marshalling.
 Functions take torch tensors (device memory, already allocated by the caller)
 and pass their data pointers and the current HIP stream to the library.
 Host-only entry points (index map, stats) take numpy arrays.
+
+The C functions receive bare pointers and cannot see how large a buffer is, so
+before a device call this layer checks every tensor it passes against the
+plan's shapes: on a GPU, contiguous, of the element type the header names and
+at least as many bytes as the call reads or writes (a ValueError or TypeError
+otherwise, and nothing is launched). NULL pointers, aliasing, workspace sizes
+and rank numbers are left to the library's own checks, which report them as a
+status (SwinError).
 """
 import ctypes
 import os
@@ -140,6 +148,55 @@ def _check(status, where):
         raise SwinError(status, where)
 
 
+_ELEM_BYTES = {SWIN_F32: 4, SWIN_BF16: 2}
+
+
+def _torch_dtype(code):
+    import torch
+    return {SWIN_F32: torch.float32, SWIN_BF16: torch.bfloat16}.get(code)
+
+
+def check_buffer(t, what, nbytes, dtype=None):
+    """Checks that tensor t (None is passed through to the library's NULL checks) is a contiguous
+    GPU tensor of at least nbytes bytes and, when dtype is given, of that element type."""
+    if t is None:
+        return
+    if not (hasattr(t, "data_ptr") and hasattr(t, "is_cuda")):
+        raise TypeError("%s: expected a torch tensor, got %s" % (what, type(t).__name__))
+    if not t.is_cuda:
+        raise ValueError("%s: must be a GPU tensor (device %s)" % (what, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s: must be contiguous" % what)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (what, dtype, t.dtype))
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError("%s: %d bytes, the call needs %d" % (what, have, nbytes))
+
+
+class _AttnShape:
+    """What the buffer checks need to know of an attention plan."""
+
+    def __init__(self, desc, n_tokens, saved_bytes):
+        self.n_tok = int(n_tokens)
+        self.C = int(desc.channels)
+        w = [int(desc.window[a]) for a in range(3)]
+        self.table = int(desc.heads) * (2 * w[0] - 1) * (2 * w[1] - 1) * (2 * w[2] - 1)
+        self.dtype_code = int(desc.dtype)
+        self.elem = _ELEM_BYTES.get(self.dtype_code, 2)
+        self.saved_bytes = int(saved_bytes)
+
+
+_ATTN_SHAPES = {}   # plan handle value -> _AttnShape
+_BLOCK_SHAPES = {}  # block plan handle value -> (_AttnShape, hidden)
+
+
+def _key(handle):
+    if handle is None:
+        return None
+    return handle.value if isinstance(handle, ctypes.c_void_p) else int(handle)
+
+
 def make_desc(batch, grid, channels, heads, window, shift, periodic=SWIN_PERIODIC_LON, dtype=SWIN_BF16,
               scale=0.0, ndim=None):
     d = SwinAttnDesc()
@@ -187,10 +244,13 @@ def swin_status_string(status):
 def swin_attn_plan_create(desc):
     h = ctypes.c_void_p()
     _check(lib.swin_attn_plan_create(ctypes.byref(desc), ctypes.byref(h)), "swin_attn_plan_create")
+    _, _, saved = swin_attn_sizes(h)
+    _ATTN_SHAPES[h.value] = _AttnShape(desc, swin_attn_plan_stats(h)["n_tokens"], saved)
     return h
 
 
 def swin_attn_plan_destroy(plan):
+    _ATTN_SHAPES.pop(_key(plan), None)
     lib.swin_attn_plan_destroy(plan)
 
 
@@ -217,7 +277,24 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _check_attn_weights(sh, w_qkv, b_qkv, w_proj, b_proj, bias_table):
+    dt, e, C = _torch_dtype(sh.dtype_code), sh.elem, sh.C
+    check_buffer(w_qkv, "w_qkv", 3 * C * C * e, dt)
+    check_buffer(b_qkv, "b_qkv", 3 * C * e, dt)
+    check_buffer(w_proj, "w_proj", C * C * e, dt)
+    check_buffer(b_proj, "b_proj", C * e, dt)
+    check_buffer(bias_table, "bias_table", sh.table * 4, _torch_dtype(SWIN_F32))
+
+
 def swin_attn_fwd(plan, x, w_qkv, b_qkv, w_proj, b_proj, bias_table, y, saved, ws=None, stream=None):
+    sh = _ATTN_SHAPES.get(_key(plan))
+    if sh is not None:
+        rows = sh.n_tok * sh.C * sh.elem
+        check_buffer(x, "x", rows, _torch_dtype(sh.dtype_code))
+        check_buffer(y, "y", rows, _torch_dtype(sh.dtype_code))
+        _check_attn_weights(sh, w_qkv, b_qkv, w_proj, b_proj, bias_table)
+        check_buffer(saved, "saved", sh.saved_bytes)
+        check_buffer(ws, "ws", 0)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.swin_attn_fwd(plan, _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_proj), _ptr(b_proj), _ptr(bias_table),
                              _ptr(y), _ptr(saved), _ptr(ws), ws_bytes, _stream(stream)), "swin_attn_fwd")
@@ -225,6 +302,19 @@ def swin_attn_fwd(plan, x, w_qkv, b_qkv, w_proj, b_proj, bias_table, y, saved, w
 
 def swin_attn_bwd(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_qkv, dw_proj, db_proj, dbias_table,
                   ws, stream=None):
+    sh = _ATTN_SHAPES.get(_key(plan))
+    if sh is not None:
+        rows, dt, f32, C = sh.n_tok * sh.C * sh.elem, _torch_dtype(sh.dtype_code), _torch_dtype(SWIN_F32), sh.C
+        for t, what in ((dy, "dy"), (x, "x"), (dx, "dx")):
+            check_buffer(t, what, rows, dt)
+        _check_attn_weights(sh, w_qkv, None, w_proj, None, bias_table)
+        check_buffer(saved, "saved", sh.saved_bytes)
+        check_buffer(dw_qkv, "dw_qkv", 3 * C * C * 4, f32)
+        check_buffer(db_qkv, "db_qkv", 3 * C * 4, f32)
+        check_buffer(dw_proj, "dw_proj", C * C * 4, f32)
+        check_buffer(db_proj, "db_proj", C * 4, f32)
+        check_buffer(dbias_table, "dbias_table", sh.table * 4, f32)
+        check_buffer(ws, "ws", 0)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.swin_attn_bwd(plan, _ptr(dy), _ptr(x), _ptr(w_qkv), _ptr(w_proj), _ptr(bias_table), _ptr(saved),
                              _ptr(dx), _ptr(dw_qkv), _ptr(db_qkv), _ptr(dw_proj), _ptr(db_proj), _ptr(dbias_table),
@@ -243,11 +333,21 @@ def swin_attn_trace_cursor():
     return int(lib.swin_attn_trace_cursor())
 
 
+def _check_rows(plan, pairs):
+    # gather/scatter move rows bit for bit: any element type of the row's byte size will do
+    sh = _ATTN_SHAPES.get(_key(plan))
+    if sh is not None:
+        for t, what in pairs:
+            check_buffer(t, what, sh.n_tok * sh.C * sh.elem)
+
+
 def swin_window_gather(plan, x, xw, stream=None):
+    _check_rows(plan, ((x, "x"), (xw, "xw")))
     _check(lib.swin_window_gather(plan, _ptr(x), _ptr(xw), _stream(stream)), "swin_window_gather")
 
 
 def swin_window_scatter(plan, yw, y, stream=None):
+    _check_rows(plan, ((yw, "yw"), (y, "y")))
     _check(lib.swin_window_scatter(plan, _ptr(yw), _ptr(y), _stream(stream)), "swin_window_scatter")
 
 
@@ -274,11 +374,41 @@ def _struct_of(cls, tensors):
 def swin_block_plan_create(desc):
     h = ctypes.c_void_p()
     _check(lib.swin_block_plan_create(ctypes.byref(desc), ctypes.byref(h)), "swin_block_plan_create")
+    _, _, saved = swin_block_sizes(h)
+    n_tok = swin_attn_host_stats(desc.attn)["n_tokens"]
+    hidden = int(desc.hidden) if desc.hidden > 0 else 4 * int(desc.attn.channels)
+    _BLOCK_SHAPES[h.value] = (_AttnShape(desc.attn, n_tok, saved), hidden)
     return h
 
 
 def swin_block_plan_destroy(plan):
+    _BLOCK_SHAPES.pop(_key(plan), None)
     lib.swin_block_plan_destroy(plan)
+
+
+def _block_param_bytes(C, hidden, table):
+    """Elements of every block parameter (the same for its fp32 gradient)."""
+    return {"ln1_g": C, "ln1_b": C, "w_qkv": 3 * C * C, "b_qkv": 3 * C, "w_proj": C * C, "b_proj": C,
+            "bias_table": table, "ln2_g": C, "ln2_b": C, "w1": hidden * C, "b1": hidden, "w2": C * hidden, "b2": C}
+
+
+def _check_block(plan, acts, params, grads=None, saved=None, ws=None):
+    entry = _BLOCK_SHAPES.get(_key(plan))
+    if entry is None:
+        return
+    sh, hidden = entry
+    bf16, f32 = _torch_dtype(SWIN_BF16), _torch_dtype(SWIN_F32)
+    for t, what in acts:
+        check_buffer(t, what, sh.n_tok * sh.C * 2, bf16)
+    n = _block_param_bytes(sh.C, hidden, sh.table)
+    for f, t in params.items():
+        if f in n:
+            check_buffer(t, f, n[f] * (4 if f == "bias_table" else 2), f32 if f == "bias_table" else bf16)
+    for f, t in (grads or {}).items():
+        if f in n:
+            check_buffer(t, "grad " + f, n[f] * 4, f32)
+    check_buffer(saved, "saved", sh.saved_bytes)
+    check_buffer(ws, "ws", 0)
 
 
 def swin_block_sizes(plan):
@@ -289,6 +419,7 @@ def swin_block_sizes(plan):
 
 def swin_block_fwd(plan, x, params, y, saved, ws=None, stream=None):
     """params: mapping from field name (ln1_g, ..., b2) to a device tensor or None."""
+    _check_block(plan, ((x, "x"), (y, "y")), params, saved=saved, ws=ws)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     prm = _struct_of(SwinBlockParams, params)
     _check(lib.swin_block_fwd(plan, _ptr(x), ctypes.byref(prm), _ptr(y), _ptr(saved), _ptr(ws), ws_bytes,
@@ -297,6 +428,7 @@ def swin_block_fwd(plan, x, params, y, saved, ws=None, stream=None):
 
 def swin_block_bwd(plan, dy, x, params, saved, dx, grads, ws, stream=None):
     """params as for swin_block_fwd; grads: the same names mapped to fp32 device tensors (None: NULL)."""
+    _check_block(plan, ((dy, "dy"), (x, "x"), (dx, "dx")), params, grads, saved=saved, ws=ws)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     prm = _struct_of(SwinBlockParams, params)
     grd = _struct_of(SwinBlockGrads, grads)
@@ -377,7 +509,18 @@ def swin_offload_destroy(engine):
     lib.swin_offload_destroy(engine)
 
 
+def _check_span(p, what, nbytes):
+    """Byte-size check of a device tensor or pinned buffer; raw addresses are passed through."""
+    if isinstance(p, PinnedBuffer):
+        if p.ptr and p.nbytes < nbytes:
+            raise ValueError("%s: %d bytes, the call needs %d" % (what, p.nbytes, nbytes))
+    elif p is not None and hasattr(p, "data_ptr"):
+        check_buffer(p, what, nbytes)
+
+
 def swin_offload_store(engine, dev, host, nbytes, after=None):
+    _check_span(dev, "dev", nbytes)
+    _check_span(host, "host", nbytes)
     t = ctypes.c_uint64()
     _check(lib.swin_offload_store(engine, _addr(dev), _addr(host), nbytes, _stream(after), ctypes.byref(t)),
            "swin_offload_store")
@@ -385,6 +528,8 @@ def swin_offload_store(engine, dev, host, nbytes, after=None):
 
 
 def swin_offload_load(engine, host, dev, nbytes, after=None):
+    _check_span(host, "host", nbytes)
+    _check_span(dev, "dev", nbytes)
     t = ctypes.c_uint64()
     _check(lib.swin_offload_load(engine, _addr(host), _addr(dev), nbytes, _stream(after), ctypes.byref(t)),
            "swin_offload_load")
@@ -443,6 +588,7 @@ class RoutePlan:
                                           ctypes.byref(h)), "swin_route_plan_create")
         self.handle = h
         self.P, self.R = src.ranks, dst.ranks
+        self.row_bytes = int(grid_desc.channels) * _ELEM_BYTES.get(int(grid_desc.dtype), 2)
         self.counts = np.empty((self.P, self.R), dtype=np.int64)
         self.src_sizes = np.empty(self.P, dtype=np.int64)
         self.dst_sizes = np.empty(self.R, dtype=np.int64)
@@ -462,14 +608,29 @@ class RoutePlan:
 
 
 def swin_route_pack(plan, p, local, send, stream=None):
+    if 0 <= int(p) < plan.P:  # other ranks: the library reports the error
+        need = int(plan.src_sizes[int(p)]) * plan.row_bytes
+        check_buffer(local, "local", need)
+        check_buffer(send, "send", need)
     _check(lib.swin_route_pack(plan.handle, int(p), _ptr(local), _ptr(send), _stream(stream)), "swin_route_pack")
 
 
 def swin_route_unpack(plan, r, recv, local, stream=None):
+    if 0 <= int(r) < plan.R:
+        need = int(plan.dst_sizes[int(r)]) * plan.row_bytes
+        check_buffer(recv, "recv", need)
+        check_buffer(local, "local", need)
     _check(lib.swin_route_unpack(plan.handle, int(r), _ptr(recv), _ptr(local), _stream(stream)), "swin_route_unpack")
 
 
 def swin_route_loopback(plan, sends, recvs, stream=None):
+    if len(sends) != plan.P or len(recvs) != plan.R:
+        raise ValueError("swin_route_loopback: %d send and %d receive buffers for %d sources and %d destinations"
+                         % (len(sends), len(recvs), plan.P, plan.R))
+    for p, t in enumerate(sends):
+        check_buffer(t, "send[%d]" % p, int(plan.src_sizes[p]) * plan.row_bytes)
+    for r, t in enumerate(recvs):
+        check_buffer(t, "recv[%d]" % r, int(plan.dst_sizes[r]) * plan.row_bytes)
     s_arr = (ctypes.c_void_p * len(sends))(*[None if t is None else t.data_ptr() for t in sends])
     r_arr = (ctypes.c_void_p * len(recvs))(*[None if t is None else t.data_ptr() for t in recvs])
     _check(lib.swin_route_loopback(plan.handle, s_arr, r_arr, _stream(stream)), "swin_route_loopback")

@@ -151,3 +151,15 @@ def test_plan_create_rejects_before_touching_the_device(native):
 def test_status_strings(native):
     for s in range(5):
         assert native.swin_status_string(s).startswith("SWIN_")
+
+
+def test_binding_buffer_checks_without_gpu(native):
+    """The binding refuses, before any library call, tensors that are not on a GPU, not
+    tensors at all, or (checked on CPU tensors' size path through the same function) too small;
+    None is passed through to the library's NULL checks."""
+    import torch
+    native.check_buffer(None, "x", 1 << 40)
+    with pytest.raises(TypeError):
+        native.check_buffer(np.zeros(4, dtype=np.float32), "x", 16)
+    with pytest.raises(ValueError, match="GPU"):
+        native.check_buffer(torch.zeros(4), "x", 16)
