@@ -16,6 +16,8 @@
 #include "device_common.h"
 #include "swin_internal.h"
 
+#include <type_traits>
+
 namespace swin {
 
 struct EpiParams {
@@ -362,6 +364,14 @@ __global__ __launch_bounds__(256, BM == 128 ? 3 : 2) void k_gemm_nt(const bf16* 
 // tile row, 16-byte chunk c is stored at slot c ^ 4 (r & 3), which puts the 4 rows x 2
 // chunks that one 16-lane group reads, and the neighbouring group's, in 16 distinct banks.
 //
+// The LDS reads are inline assembly and the steps are ordered by explicit waits: the
+// compiler cannot tell a read of one stage buffer from the copies in flight into the other,
+// and with its own reads (or a __syncthreads) it waits for every copy, the next step's
+// included, before each step's first read. Each step starts by waiting for this wave's
+// copies of the step (issued a whole step earlier), then an LDS-only barrier, then issues
+// the next step's copies into the other buffer; fragment reads of K slice ks+1 are in flight
+// while slice ks multiplies.
+//
 // Workgroups of the first column tile also sum A's columns (the bias gradients) on the
 // vector ALUs from the same LDS tiles, combined in a fixed order.
 // ---------------------------------------------------------------------------
@@ -378,15 +388,38 @@ struct Stage {
 __device__ __forceinline__ int slot(int r, int c) { return c ^ (4 * (r & 3)); }
 }  // namespace tn
 
-// 32x32x16 fragment: 8 consecutive tokens k0 + 8 (g>>1) + 0..7 at column col0 + lane % 32.
-__device__ __forceinline__ bf16x8 tn_frag(const unsigned char* tile, int k0, int col0, int lane) {
+// 32x32x16 fragment: 8 consecutive tokens k0 + 8 (g>>1) + 0..7 at column col0 + lane % 32
+// (g = lane / 16, L = lane % 16). Its two transposing reads (token rows r and r + 4, where
+// r = k0 + 8 (g>>1) + L/4) start at the lane's byte address in the tile; column block
+// c32 = col0 / 32 puts logical chunk 4 c32 + lp (lp = 2 (g&1) + (L&3)/2) at slot
+// 4 (c32 ^ (r&3)) + lp, so the address is tn_lane_off(lane) + 64 (c32 ^ (r&3)) + K offset.
+// Issued without a wait: the caller waits (tn_wait) before the registers are used.
+__device__ __forceinline__ uint32_t tn_lane_off(int lane) {
   const int g = lane >> 4, L = lane & 15;
-  const int r = k0 + 8 * (g >> 1) + (L >> 2);
-  const int col = col0 + 16 * (g & 1) + 4 * (L & 3);
-  const int c = col >> 3, half = (L & 1) * 8;
-  const bf16x4 lo = lds_read_tr(tile + r * tn::ROWB + 16 * tn::slot(r, c) + half);
-  const bf16x4 hi = lds_read_tr(tile + (r + 4) * tn::ROWB + 16 * tn::slot(r + 4, c) + half);
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  const int rl = 8 * (g >> 1) + (L >> 2);
+  return (uint32_t)(rl * tn::ROWB + 16 * (2 * (g & 1) + ((L & 3) >> 1)) + 8 * (L & 1));
+}
+__device__ __forceinline__ int tn_lane_rr(int lane) { return ((lane & 15) >> 2) & 3; }  // (r & 3)
+
+template <int OFF>
+__device__ __forceinline__ bf16x8 tn_frag_issue(uint32_t addr) {
+  u32x2 lo, hi;
+  asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
+               : "=&v"(lo), "=&v"(hi)
+               : "v"(addr), "i"(OFF), "i"(OFF + 4 * tn::ROWB));
+  const bf16x4 l = __builtin_bit_cast(bf16x4, lo), h = __builtin_bit_cast(bf16x4, hi);
+  return bf16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+}
+
+// Waits for this wave's LDS reads and ties the registers to the wait, so that no use of them
+// is scheduled before it.
+template <int NA, int NB>
+__device__ __forceinline__ void tn_wait(bf16x8 (&fa)[NA], bf16x8 (&fb)[NB]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < NA; ++i) asm volatile("" : "+v"(fa[i]));
+#pragma unroll
+  for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(fb[j]));
 }
 
 // Copy rows [0, 64) x 256 columns of a token-major operand (row pitch ld elements) starting
@@ -414,8 +447,7 @@ __global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ 
                                                        const bf16* __restrict__ B, int64_t ldb, int64_t T, int M,
                                                        int N, int64_t chunk, int n_splits,
                                                        float* __restrict__ part, float* __restrict__ dbpart) {
-  __shared__ __attribute__((aligned(1024))) tn::Stage st0;
-  __shared__ __attribute__((aligned(1024))) tn::Stage st1;
+  __shared__ __attribute__((aligned(1024))) tn::Stage stg[2];
   __shared__ float colsum[tn::CROWS][tn::BM];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -441,54 +473,72 @@ __global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ 
   float csum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int crow = tid >> 5, cchunk = tid & 31;  // column sums: thread = 8 columns x 4 rows
 
+  // lane byte offsets of the fragments in stage 0 (stage 1 is one Stage further)
+  const uint32_t lane_off = tn_lane_off(lane), rr = (uint32_t)tn_lane_rr(lane);
+  uint32_t a_off[TM], b_off[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a_off[i] = lane_off + 64 * ((uint32_t)(wm * TM + i) ^ rr);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b_off[j] = lane_off + 64 * ((uint32_t)(wn * TN + j) ^ rr) + (uint32_t)tn::TILEB;
+  const uint32_t db_off = (uint32_t)(crow * tn::ROWB + 16 * tn::slot(crow, cchunk));
+  const uint32_t st_base = lds_addr(&stg[0]);
+
   auto stage = [&](int k, tn::Stage& st) {
     const int64_t t0 = t_begin + (int64_t)k * tn::BK;
     const int valid = (int)(t_end - t0 < tn::BK ? t_end - t0 : tn::BK);
     tn_stage(A + t0 * lda + m0, lda, valid, M - m0 < tn::BM ? M - m0 : tn::BM, st.a, wave, lane);
     tn_stage(B + t0 * ldb + n0, ldb, valid, N - n0 < tn::BN ? N - n0 : tn::BN, st.b, wave, lane);
   };
-  auto compute = [&](const tn::Stage& st) {
-    // one K slice of lookahead: the fragments of slice ks+1 are read while slice ks multiplies
-    bf16x8 fa[2][TM], fb[2][TN];
+  // fragments of K slice KS (16 tokens) of the stage at LDS address sb
+  auto issue = [&](uint32_t sb, auto ks, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
+    constexpr int OFF = 16 * decltype(ks)::value * tn::ROWB;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[0][i] = tn_frag(st.a, 0, wm * tn::WTM + 32 * i, lane);
+    for (int i = 0; i < TM; ++i) fa[i] = tn_frag_issue<OFF>(sb + a_off[i]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb[0][j] = tn_frag(st.b, 0, wn * tn::WTN + 32 * j, lane);
-#pragma unroll
-    for (int ks = 0; ks < tn::BK / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < tn::BK / 16) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = tn_frag(st.a, 16 * (ks + 1), wm * tn::WTM + 32 * i, lane);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = tn_frag(st.b, 16 * (ks + 1), wn * tn::WTN + 32 * j, lane);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fa[cur][i], fb[cur][j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (do_db) {
-#pragma unroll
-      for (int rr = 0; rr < tn::BK / tn::CROWS; ++rr) {
-        const int r = crow + tn::CROWS * rr;
-        const bf16x8 v = *(const bf16x8*)(st.a + r * tn::ROWB + 16 * tn::slot(r, cchunk));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) csum[e] += to_f32(v[e]);
-      }
-    }
+    for (int j = 0; j < TN; ++j) fb[j] = tn_frag_issue<OFF>(sb + b_off[j]);
   };
-  if (steps > 0) stage(0, st0);
-  __syncthreads();
-  for (int k = 0; k < steps; k += 2) {
-    if (k + 1 < steps) stage(k + 1, st1);
-    compute(st0);
-    __syncthreads();
-    if (k + 1 < steps) {
-      if (k + 2 < steps) stage(k + 2, st0);
-      compute(st1);
-      __syncthreads();
+  auto mma = [&](const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+  };
+  static_assert(tn::BK == 64, "four K slices per step");
+  constexpr int DB_ROWS = tn::BK / tn::CROWS;
+
+  if (steps > 0) stage(0, stg[0]);
+  for (int k = 0; k < steps; ++k) {
+    // this wave's copies of step k (issued a step ago) have landed; after the barrier every
+    // wave's have, and every wave is done reading the buffer the next copies go to
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (k + 1 < steps) stage(k + 1, stg[(k + 1) & 1]);
+    const uint32_t sb = st_base + (uint32_t)((k & 1) * sizeof(tn::Stage));
+    bf16x8 f0a[TM], f0b[TN], f1a[TM], f1b[TN];
+    issue(sb, std::integral_constant<int, 0>{}, f0a, f0b);
+    tn_wait(f0a, f0b);
+    issue(sb, std::integral_constant<int, 1>{}, f1a, f1b);
+    mma(f0a, f0b);
+    tn_wait(f1a, f1b);
+    issue(sb, std::integral_constant<int, 2>{}, f0a, f0b);
+    mma(f1a, f1b);
+    tn_wait(f0a, f0b);
+    issue(sb, std::integral_constant<int, 3>{}, f1a, f1b);
+    mma(f0a, f0b);
+    tn_wait(f1a, f1b);
+    mma(f1a, f1b);
+    if (do_db) {
+      bf16x8 v[DB_ROWS];
+#pragma unroll
+      for (int q = 0; q < DB_ROWS; ++q)
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v[q]) : "v"(sb + db_off), "i"(q * tn::CROWS * tn::ROWB));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int q = 0; q < DB_ROWS; ++q) asm volatile("" : "+v"(v[q]));
+#pragma unroll
+      for (int q = 0; q < DB_ROWS; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) csum[e] += to_f32(v[q][e]);
     }
   }
 
