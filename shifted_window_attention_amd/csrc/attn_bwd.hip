@@ -156,10 +156,12 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
   const float inv_log2e = 1.f / kLog2e;
   __syncthreads();
 
-  // A barrier's release fence waits for outstanding global stores, and that wait also
-  // covers the copies in flight. So no store is outstanding at the mid-window barrier: dK
-  // and dV are stored right after it, and dq at the start of the next window, after the
-  // next copies are issued.
+  // A __syncthreads() waits for every outstanding vector memory operation, the copies of
+  // the next window included: those copies land during the first half of the window (S, P,
+  // dP, dK, dV), before the mid-window barrier. (An LDS-only barrier there, which keeps them
+  // in flight through the dQ half, measured slower.) No store is outstanding at the
+  // mid-window barrier: dK and dV are stored right after it, and dq at the start of the
+  // next window, after the next copies are issued.
   bf16x4 pq[2] = {};
   int64_t prev_off = -1;
   int prev_row = 0;  // grid row of this lane's dq row in the previous window
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);  // bound live ranges to one query chunk
     }
-    __syncthreads();  // dS complete (no stores are outstanding here, so copies stay in flight)
+    __syncthreads();  // dS complete; the next window's copies have landed
     if (key < n) {
       bf16* row = a.dqkv + (int64_t)cur.grow[key] * (3 * C) + h * 32;
 #pragma unroll
