@@ -372,8 +372,13 @@ __global__ __launch_bounds__(256, BM == 128 ? 3 : 2) void k_gemm_nt(const bf16* 
 // the next step's copies into the other buffer; fragment reads of K slice ks+1 are in flight
 // while slice ks multiplies.
 //
-// Workgroups of the first column tile also sum A's columns (the bias gradients) on the
-// vector ALUs from the same LDS tiles, combined in a fixed order.
+// The bias gradients (A's column sums) come from the A fragments already in registers. The
+// Q = min(column tiles, 4) workgroups of the first Q column tiles share them: workgroup t
+// sums the 32-column fragments i with i % Q == t, so every column is summed by exactly one
+// workgroup and the work is spread over them. Inside a workgroup the four waves that share
+// a row of column blocks take one 16-token K slice each (two-term dot products with ones,
+// 8 tokens of one column per lane); the four slice sums are combined through LDS in a
+// fixed order.
 // ---------------------------------------------------------------------------
 namespace tn {
 constexpr int BM = 256, BN = 256, BK = 64;
@@ -381,7 +386,7 @@ constexpr int NT = 512, NW = NT / 64;    // threads, waves
 constexpr int WTM = 128, WTN = 64;       // per-wave tile
 constexpr int ROWB = 512;                // bytes per tile row (256 bf16)
 constexpr int TILEB = BK * ROWB;         // 32 KB per operand tile
-constexpr int CROWS = NT / 32;           // column-sum row groups (thread = 8 columns)
+constexpr int WN = BN / WTN;             // waves per row of column blocks = K slices per step
 struct Stage {
   unsigned char a[TILEB], b[TILEB];
 };
@@ -448,7 +453,7 @@ __global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ 
                                                        int N, int64_t chunk, int n_splits,
                                                        float* __restrict__ part, float* __restrict__ dbpart) {
   __shared__ __attribute__((aligned(1024))) tn::Stage stg[2];
-  __shared__ float colsum[tn::CROWS][tn::BM];
+  __shared__ float colsum[tn::WN][tn::BM];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
@@ -461,17 +466,18 @@ __global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ 
   const int s = (int)(ms / n_mt);
   const int64_t t_begin = (int64_t)s * chunk;
   const int64_t t_end = t_begin + chunk < T ? t_begin + chunk : T;
-  const bool do_db = dbpart != nullptr && ntile == 0;
   const int steps = t_end > t_begin ? (int)((t_end - t_begin + tn::BK - 1) / tn::BK) : 0;
 
   constexpr int TM = tn::WTM / 32, TN = tn::WTN / 32;
+  const int db_q = n_nt < TM ? n_nt : TM;       // workgroups sharing the column sums
+  const bool do_db = dbpart != nullptr && ntile < db_q;
+  const auto db_mine = [&](int i) { return i % db_q == ntile; };  // fragment i's columns here
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
-  float csum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const int crow = tid >> 5, cchunk = tid & 31;  // column sums: thread = 8 columns x 4 rows
+  float csum[TM] = {};  // column sums of K slice wn of every step, per A fragment
 
   // lane byte offsets of the fragments in stage 0 (stage 1 is one Stage further)
   const uint32_t lane_off = tn_lane_off(lane), rr = (uint32_t)tn_lane_rr(lane);
@@ -480,7 +486,6 @@ __global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ 
   for (int i = 0; i < TM; ++i) a_off[i] = lane_off + 64 * ((uint32_t)(wm * TM + i) ^ rr);
 #pragma unroll
   for (int j = 0; j < TN; ++j) b_off[j] = lane_off + 64 * ((uint32_t)(wn * TN + j) ^ rr) + (uint32_t)tn::TILEB;
-  const uint32_t db_off = (uint32_t)(crow * tn::ROWB + 16 * tn::slot(crow, cchunk));
   const uint32_t st_base = lds_addr(&stg[0]);
 
   auto stage = [&](int k, tn::Stage& st) {
@@ -503,8 +508,21 @@ __global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ 
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
   };
-  static_assert(tn::BK == 64, "four K slices per step");
-  constexpr int DB_ROWS = tn::BK / tn::CROWS;
+  static_assert(tn::BK == 64 && tn::WN == tn::BK / 16, "four K slices per step, one per column-block wave");
+  const bf16x2 ones2 = {(bf16)1.f, (bf16)1.f};
+  // bias gradients: the wave whose column-block index is KS adds the 8 tokens of each A
+  // fragment of slice KS (column wm * WTM + 32 i + lane % 32, token half lane / 32)
+  auto db_add = [&](auto ks, const bf16x8 (&fa)[TM]) {
+    if (do_db && wn == decltype(ks)::value) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        if (db_mine(i)) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            csum[i] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{fa[i][2 * e], fa[i][2 * e + 1]}, ones2, csum[i], false);
+        }
+    }
+  };
 
   if (steps > 0) stage(0, stg[0]);
   for (int k = 0; k < steps; ++k) {
@@ -515,31 +533,26 @@ __global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ 
     if (k + 1 < steps) stage(k + 1, stg[(k + 1) & 1]);
     const uint32_t sb = st_base + (uint32_t)((k & 1) * sizeof(tn::Stage));
     bf16x8 f0a[TM], f0b[TN], f1a[TM], f1b[TN];
-    issue(sb, std::integral_constant<int, 0>{}, f0a, f0b);
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
+    using K2 = std::integral_constant<int, 2>;
+    using K3 = std::integral_constant<int, 3>;
+    issue(sb, K0{}, f0a, f0b);
     tn_wait(f0a, f0b);
-    issue(sb, std::integral_constant<int, 1>{}, f1a, f1b);
+    issue(sb, K1{}, f1a, f1b);
     mma(f0a, f0b);
+    db_add(K0{}, f0a);
     tn_wait(f1a, f1b);
-    issue(sb, std::integral_constant<int, 2>{}, f0a, f0b);
+    issue(sb, K2{}, f0a, f0b);
     mma(f1a, f1b);
+    db_add(K1{}, f1a);
     tn_wait(f0a, f0b);
-    issue(sb, std::integral_constant<int, 3>{}, f1a, f1b);
+    issue(sb, K3{}, f1a, f1b);
     mma(f0a, f0b);
+    db_add(K2{}, f0a);
     tn_wait(f1a, f1b);
     mma(f1a, f1b);
-    if (do_db) {
-      bf16x8 v[DB_ROWS];
-#pragma unroll
-      for (int q = 0; q < DB_ROWS; ++q)
-        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v[q]) : "v"(sb + db_off), "i"(q * tn::CROWS * tn::ROWB));
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int q = 0; q < DB_ROWS; ++q) asm volatile("" : "+v"(v[q]));
-#pragma unroll
-      for (int q = 0; q < DB_ROWS; ++q)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) csum[e] += to_f32(v[q][e]);
-    }
+    db_add(K3{}, f1a);
   }
 
   // partial tile as P[s][m/4][n][m%4]: a lane's 4 consecutive rows m of one column n are one
@@ -561,12 +574,16 @@ __global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ 
       }
     }
   if (do_db) {
+    // the two token halves of a column (lanes l and l ^ 32), then the four K slices in order
 #pragma unroll
-    for (int e = 0; e < 8; ++e) colsum[crow][cchunk * 8 + e] = csum[e];
+    for (int i = 0; i < TM; ++i) {
+      const float v = csum[i] + __shfl_xor(csum[i], 32);
+      if (lane < 32) colsum[wn][wm * tn::WTM + 32 * i + lane] = v;
+    }
     __syncthreads();
-    if (tid < tn::BM && m0 + tid < M) {
+    if (tid < tn::BM && m0 + tid < M && db_mine((tid % tn::WTM) / 32)) {
       float v = 0.f;
-      for (int q = 0; q < tn::CROWS; ++q) v += colsum[q][tid];  // fixed order
+      for (int q = 0; q < tn::WN; ++q) v += colsum[q][tid];  // fixed order
       dbpart[(int64_t)s * M + m0 + tid] = v;
     }
   }
