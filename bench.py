@@ -217,7 +217,7 @@ def time_shard_share(hip, N, stream, base_cfg, steps, warmup):
     the grid's own latitude edges, so the per-GPU compute shape is the same."""
     import numpy as np
     import torch
-    from tests.gpu_util import ModuleOnDevice
+    from shifted_window_attention_amd.device import ModuleOnDevice
     from workloads.configs import small_variant
     cfg = small_variant(base_cfg, grid=(1, 72, base_cfg.grid[2]))
     inp = _device_inputs(cfg)
@@ -526,7 +526,7 @@ def main():
     from __graft_entry__ import _ensure_built
     _ensure_built()
     from shifted_window_attention_amd import native as N
-    from tests.gpu_util import ModuleOnDevice, to_dev
+    from shifted_window_attention_amd.device import ModuleOnDevice, to_dev
     from workloads import get_config, make_inputs
 
     cfg = get_config("highres")

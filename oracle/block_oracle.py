@@ -115,5 +115,5 @@ def block_bwd(dy: np.ndarray, x: np.ndarray, p: BlockParams, layout: O.Layout, h
 def block_flops(n_tokens: int, channels: int, hidden: int, heads: int, pairs: int) -> int:
     """Algorithmic forward FLOPs of a block: the attention module plus the two MLP products
     (layer normalisation, GELU and residual adds are not counted)."""
-    attn = sum(O.module_flops(n_tokens, channels, heads, pairs).values())
+    attn = O.module_flops(n_tokens, channels, heads, pairs)["fwd"]
     return attn + 2 * 2 * n_tokens * channels * hidden
