@@ -159,6 +159,14 @@ void swin_attn_plan_destroy(swin_attn_plan* plan);
 swin_status swin_attn_plan_stats(const swin_attn_plan* plan, swin_attn_stats* out);
 
 /*
+ * The plan's slot -> grid index map and wrap labels, as swin_attn_host_index_map gives them for
+ * the plan's descriptor (same layout and meaning), copied from the plan's host tables: no
+ * device call. host_map and host_labels are host buffers of n_tokens elements; either may be
+ * NULL. Errors: SWIN_ERR_ARG for a NULL plan.
+ */
+swin_status swin_attn_index_map(const swin_attn_plan* plan, int64_t* host_map, uint8_t* host_labels);
+
+/*
  * Sizes in bytes of the forward workspace, backward workspace and the saved
  * state that swin_attn_fwd writes for swin_attn_bwd.
  */

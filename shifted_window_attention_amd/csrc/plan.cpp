@@ -297,6 +297,15 @@ swin_status swin_attn_host_index_map(const swin_attn_desc* desc, int64_t* map, u
   return SWIN_OK;
 }
 
+swin_status swin_attn_index_map(const swin_attn_plan* plan, int64_t* map, uint8_t* labels) {
+  if (!plan) return fail(SWIN_ERR_ARG, "plan is NULL");
+  for (int64_t t = 0; t < plan->n_tok; ++t) {
+    if (map) map[t] = plan->perm[t];
+    if (labels) labels[t] = plan->labels[t];
+  }
+  return SWIN_OK;
+}
+
 swin_status swin_attn_host_stats(const swin_attn_desc* desc, swin_attn_stats* out) {
   if (!out) return fail(SWIN_ERR_ARG, "stats output is NULL");
   swin_status st = validate(desc);
@@ -332,6 +341,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
   p->tau = desc->scale > 0.f ? desc->scale : 1.0f / std::sqrt((float)p->hd);
   p->stats = L.stats;
   p->perm = std::move(L.perm);
+  p->labels = std::move(L.labels);
   p->win_off = std::move(L.win_off);
   p->classes = std::move(L.classes);
   // class-sorted window list (row-major order inside a class)

@@ -108,6 +108,7 @@ struct swin_attn_plan {
   int device = -1;
   swin_attn_stats stats{};
   std::vector<int32_t> perm, win_off, class_win;
+  std::vector<uint8_t> labels;  // slot -> wrap-label bits (host copy, for swin_attn_index_map)
   std::vector<swin::ClassInfo> classes;
   std::vector<swin::WorkItem> fwd_work, bwd_work;
   std::vector<swin::WorkRange> fwd_ranges, bwd_ranges;

@@ -100,6 +100,7 @@ def _load():
         "swin_attn_plan_create": (st, [P(SwinAttnDesc), P(vp)]),
         "swin_attn_plan_destroy": (None, [vp]),
         "swin_attn_plan_stats": (st, [vp, P(SwinAttnStats)]),
+        "swin_attn_index_map": (st, [vp, P(ctypes.c_int64), P(ctypes.c_uint8)]),
         "swin_attn_sizes": (st, [vp, P(sz), P(sz), P(sz)]),
         "swin_attn_fwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "swin_attn_bwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -258,6 +259,16 @@ def swin_attn_plan_stats(plan):
     st = SwinAttnStats()
     _check(lib.swin_attn_plan_stats(plan, ctypes.byref(st)), "swin_attn_plan_stats")
     return st.as_dict()
+
+
+def swin_attn_index_map(plan):
+    """The plan's slot -> grid map and wrap labels (host copies, no device call)."""
+    n = swin_attn_plan_stats(plan)["n_tokens"]
+    m = np.empty(n, dtype=np.int64)
+    lab = np.empty(n, dtype=np.uint8)
+    _check(lib.swin_attn_index_map(plan, m.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                   lab.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))), "swin_attn_index_map")
+    return m, lab
 
 
 def swin_attn_sizes(plan):

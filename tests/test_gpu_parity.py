@@ -51,7 +51,9 @@ def test_gather_scatter_bit_exact(name):
         desc = N.make_desc(cfg.batch, cfg.grid, cfg.channels, cfg.heads, cfg.window, shift, cfg.periodic,
                            N.SWIN_BF16 if cfg.dtype == "bf16" else N.SWIN_F32)
         plan = N.Plan(desc)
-        perm, _ = N.swin_attn_host_index_map(desc)
+        perm, labels = N.swin_attn_host_index_map(desc)
+        pmap, plab = N.swin_attn_index_map(plan.handle)   # the plan's own tables, same map
+        assert np.array_equal(pmap, perm) and np.array_equal(plab, labels)
         es = 2 if cfg.dtype == "bf16" else 4
         words = cfg.channels * es // 2
         # integer-coded grid: every 16-bit word of row g holds (g * 31 + c) mod 2^16
