@@ -88,6 +88,10 @@ def make_rank_layout(kind, ranks, shift=(0, 0, 0)):
 
 
 def _load():
+    # One HIP runtime per process: torch ships its own. Importing it before the library makes
+    # the library bind to that runtime; loaded first, the library would pull in the system
+    # runtime, and torch's copy, loaded later, then finds no device.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError("libswinattn.so is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
                           "or `python shifted_window_attention_amd/build_lib.py`")
