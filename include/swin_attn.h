@@ -224,6 +224,25 @@ swin_status swin_attn_bwd(const swin_attn_plan* plan, const void* dy, const void
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * swin_attn_bwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). The
+ * arguments, results and errors are those of swin_attn_bwd; the workspace is a device array
+ * of SWIN_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the process ends.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   - Plans whose backward workspace (swin_attn_sizes' bwd_ws) exceeds
+ *     SWIN_NOALLOC_SCRATCH_BYTES are refused with SWIN_ERR_WORKSPACE; use swin_attn_bwd there.
+ *   - The current device must be the plan's device (else SWIN_ERR_ARG).
+ *   - Every call on a GPU shares that GPU's scratch array: calls that overlap in time on one
+ *     GPU (different streams, or different threads) race on it and must be serialised by the
+ *     caller.
+ */
+#define SWIN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+swin_status swin_attn_bwd_noalloc(const swin_attn_plan* plan, const void* dy, const void* x, const void* w_qkv,
+                                  const void* w_proj, const float* bias_table, const void* saved, void* dx,
+                                  float* dw_qkv, float* db_qkv, float* dw_proj, float* db_proj, float* dbias_table,
+                                  void* stream);
+
+/*
  * Stand-alone cyclic shift + window partition (gather) and its inverse
  * (window reverse + un-shift scatter), on rows of C elements of desc.dtype:
  *   gather:  xw[t, :] = x[map[t], :]     (x on the grid, xw window-major)

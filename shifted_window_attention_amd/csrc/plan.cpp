@@ -256,6 +256,18 @@ static void build_work(const std::vector<ClassInfo>& classes, int heads, int64_t
   }
 }
 
+// Argument checks of the module backward, shared by swin_attn_bwd and swin_attn_bwd_noalloc.
+swin_status bwd_arg_checks(const swin_attn_plan* plan, const void* dy, const void* x, const void* w_qkv,
+                           const void* w_proj, const float* bias_table, const void* saved, const void* dx,
+                           const float* dw_qkv, const float* dw_proj, const float* dbias_table) {
+  if (!plan) return fail(SWIN_ERR_ARG, "plan is NULL");
+  if (plan->d.dtype != SWIN_BF16) return fail(SWIN_ERR_UNSUPPORTED, "backward is implemented for bf16 only");
+  if (!dy || !x || !w_qkv || !w_proj || !bias_table || !saved || !dx || !dw_qkv || !dw_proj || !dbias_table)
+    return fail(SWIN_ERR_ARG, "NULL input or output pointer");
+  if (dx == dy || dx == x) return fail(SWIN_ERR_ARG, "dx must not alias dy or x");
+  return SWIN_OK;
+}
+
 }  // namespace swin
 
 using namespace swin;
@@ -501,11 +513,9 @@ swin_status swin_attn_bwd(const swin_attn_plan* plan, const void* dy, const void
                           const void* w_proj, const float* bias_table, const void* saved, void* dx, float* dw_qkv,
                           float* db_qkv, float* dw_proj, float* db_proj, float* dbias_table, void* ws,
                           size_t ws_bytes, void* stream) {
-  if (!plan) return fail(SWIN_ERR_ARG, "plan is NULL");
-  if (plan->d.dtype != SWIN_BF16) return fail(SWIN_ERR_UNSUPPORTED, "backward is implemented for bf16 only");
-  if (!dy || !x || !w_qkv || !w_proj || !bias_table || !saved || !dx || !dw_qkv || !dw_proj || !dbias_table)
-    return fail(SWIN_ERR_ARG, "NULL input or output pointer");
-  if (dx == dy || dx == x) return fail(SWIN_ERR_ARG, "dx must not alias dy or x");
+  const swin_status st = bwd_arg_checks(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, dw_proj,
+                                        dbias_table);
+  if (st != SWIN_OK) return st;
   if (!ws || ws_bytes < plan->bwd_total) return fail(SWIN_ERR_WORKSPACE, "backward workspace too small");
   return hip_status(launch_bwd_bf16(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_qkv, dw_proj,
                                     db_proj, dbias_table, ws, (hipStream_t)stream),

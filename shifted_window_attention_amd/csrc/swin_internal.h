@@ -128,6 +128,11 @@ namespace swin {
 
 void set_error(const std::string& msg);
 
+// Argument checks of the module backward (status and last-error message as the ABI returns them).
+swin_status bwd_arg_checks(const swin_attn_plan* plan, const void* dy, const void* x, const void* w_qkv,
+                           const void* w_proj, const float* bias_table, const void* saved, const void* dx,
+                           const float* dw_qkv, const float* dw_proj, const float* dbias_table);
+
 // Records the next installed trace event (if any) on stream s; see swin_attn_trace_events.
 hipError_t trace_mark(hipStream_t s);
 

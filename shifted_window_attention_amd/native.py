@@ -108,6 +108,7 @@ def _load():
         "swin_attn_sizes": (st, [vp, P(sz), P(sz), P(sz)]),
         "swin_attn_fwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "swin_attn_bwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "swin_attn_bwd_noalloc": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "swin_window_gather": (st, [vp, vp, vp, vp]),
         "swin_window_scatter": (st, [vp, vp, vp, vp]),
         "swin_attn_trace_events": (st, [P(vp), st]),
@@ -334,6 +335,29 @@ def swin_attn_bwd(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_
     _check(lib.swin_attn_bwd(plan, _ptr(dy), _ptr(x), _ptr(w_qkv), _ptr(w_proj), _ptr(bias_table), _ptr(saved),
                              _ptr(dx), _ptr(dw_qkv), _ptr(db_qkv), _ptr(dw_proj), _ptr(db_proj), _ptr(dbias_table),
                              _ptr(ws), ws_bytes, _stream(stream)), "swin_attn_bwd")
+
+
+SWIN_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def swin_attn_bwd_noalloc(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_qkv, dw_proj, db_proj,
+                          dbias_table, stream=None):
+    """swin_attn_bwd on the library's own per-GPU scratch array (no workspace argument)."""
+    sh = _ATTN_SHAPES.get(_key(plan))
+    if sh is not None:
+        rows, dt, f32, C = sh.n_tok * sh.C * sh.elem, _torch_dtype(sh.dtype_code), _torch_dtype(SWIN_F32), sh.C
+        for t, what in ((dy, "dy"), (x, "x"), (dx, "dx")):
+            check_buffer(t, what, rows, dt)
+        _check_attn_weights(sh, w_qkv, None, w_proj, None, bias_table)
+        check_buffer(saved, "saved", sh.saved_bytes)
+        check_buffer(dw_qkv, "dw_qkv", 3 * C * C * 4, f32)
+        check_buffer(db_qkv, "db_qkv", 3 * C * 4, f32)
+        check_buffer(dw_proj, "dw_proj", C * C * 4, f32)
+        check_buffer(db_proj, "db_proj", C * 4, f32)
+        check_buffer(dbias_table, "dbias_table", sh.table * 4, f32)
+    _check(lib.swin_attn_bwd_noalloc(plan, _ptr(dy), _ptr(x), _ptr(w_qkv), _ptr(w_proj), _ptr(bias_table),
+                                     _ptr(saved), _ptr(dx), _ptr(dw_qkv), _ptr(db_qkv), _ptr(dw_proj), _ptr(db_proj),
+                                     _ptr(dbias_table), _stream(stream)), "swin_attn_bwd_noalloc")
 
 
 def swin_attn_trace_events(events):
