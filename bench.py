@@ -8,12 +8,20 @@ seeded synthetic data resident in HBM before the timed region. After the timed s
 window gather and scatter are also timed stand-alone against a device-to-device copy, and the
 chain is timed on one GPU's share of an 8-way latitude split (72x1080 tokens).
 
+Then the other workloads of the measurement plan, each on its own (180x360 batch 2, the ragged
+181x361 grid and the 8x180x360 level grid forward + backward; the 32x64 fp32 grid forward):
+median / min / max over 50 calls after 10 warm-ups, with the fp64 oracle timed on the same
+inputs (and the brute-force per-token loop on the fp32 grid).
+
 Prints one JSON line on stdout:
   value = token-blocks per second (tokens x modules per step / step time),
   tflops / mfma_peak_frac = algorithmic FLOPs per second and their fraction of the
-  dense bf16 MFMA peak, roofline = the dominant kernel against its bound (stage
-  durations from HIP events recorded on the library's stream inside the timed region),
-  cpu_baseline = the fp64 oracle on a bounded sample of the same workload.
+  dense bf16 MFMA peak, step_ms = median / min / max of the timed steps,
+  hbm_bytes_per_step = the algorithmic bytes of all stages of a step,
+  roofline = the dominant kernel against its bound (stage durations from HIP events
+  recorded on the library's stream inside the timed region),
+  configs = the other workloads, cpu_baseline = the fp64 oracle on a bounded sample of the
+  same workload (CPU model and BLAS threads recorded).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-seconds S]
 """
@@ -120,39 +128,73 @@ def traffic_for(stage, per_launch_ref):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, inp, seconds):
-    """The fp64 oracle, as it is, on whole windows of both modules until ~`seconds` of CPU work."""
-    import numpy as np
-    from oracle import swin_oracle as O
+def cpu_info():
+    """CPU model name, visible cores and the BLAS library's thread count."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    threads = os.cpu_count() or 1
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] or [os.cpu_count() or 1])
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            threads = max(int(i.get("num_threads", 1)) for i in info)
     except Exception:
-        threads = os.cpu_count() or 1
+        pass
+    return {"model": model, "cores_visible": os.cpu_count() or 0, "blas_threads": int(threads)}
+
+
+def cpu_baseline_sampled(cfg, params_f64, x_rows, dy_rows, lays, seconds, rng_seed=11):
+    """The fp64 oracle, as it is, on random whole windows of every module of `cfg`, forward and
+    forward + backward, until ~`seconds` of CPU work each. x_rows / dy_rows(mi) give the
+    window-major float64 rows of module mi's input / upstream gradient for a list of window ids."""
+    import numpy as np
+    from oracle import swin_oracle as O
+    rng = np.random.default_rng(rng_seed)
+    res = {}
+    for mode in ("fwd", "fwd_bwd"):
+        tokens = windows = 0
+        elapsed = 0.0
+        while elapsed < seconds:
+            for mi, lay in enumerate(lays):
+                ids = sorted(rng.choice(len(lay.windows), min(4, len(lay.windows)), replace=False).tolist())
+                xw = x_rows(mi, ids)
+                dyw = dy_rows(mi, ids) if mode == "fwd_bwd" else None
+                t0 = time.perf_counter()
+                O.windows_fwd(xw, params_f64[mi], lay, cfg.heads, window_ids=ids)
+                if mode == "fwd_bwd":
+                    O.windows_bwd(dyw, xw, params_f64[mi], lay, cfg.heads, window_ids=ids)
+                elapsed += time.perf_counter() - t0
+                tokens += sum(lay.windows[i].n for i in ids)
+                windows += len(ids)
+        res[mode] = {"tokens_per_s": round(tokens / elapsed, 1), "windows": windows, "seconds": round(elapsed, 2)}
+    return res
+
+
+def cpu_baseline(cfg, inp, seconds):
+    """The fp64 oracle, as it is, on whole windows of both modules of the headline workload."""
+    from oracle import swin_oracle as O
     lays = [O.window_layout(cfg.batch, cfg.grid, cfg.window, s, cfg.periodic) for s in cfg.shifts]
     ps = [O.Params(m.w_qkv, m.b_qkv, m.w_proj, m.b_proj, m.table) for m in inp.modules]
     xws = [O.gather(inp.x, lay) for lay in lays]
     dyws = [O.gather(inp.dy, lay) for lay in lays]
-    rng = np.random.default_rng(11)
-    tokens = 0
-    windows = 0
-    t0 = time.perf_counter()
-    elapsed = 0.0
-    while elapsed < seconds:
-        for mi, lay in enumerate(lays):
-            ids = sorted(rng.choice(len(lay.windows), 4, replace=False).tolist())
-            O.windows_fwd(xws[mi], ps[mi], lay, cfg.heads, window_ids=ids)
-            O.windows_bwd(dyws[mi], xws[mi], ps[mi], lay, cfg.heads, window_ids=ids)
-            tokens += sum(lay.windows[i].n for i in ids)
-            windows += len(ids)
-        elapsed = time.perf_counter() - t0
-    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    r = cpu_baseline_sampled(cfg, ps, lambda mi, ids: xws[mi], lambda mi, ids: dyws[mi], lays, seconds / 2)
+    ci = cpu_info()
+    fb = r["fwd_bwd"]
+    return {"value": fb["tokens_per_s"], "unit": "tokens/s", "cores": ci["blas_threads"], "kind": "oracle",
             "sample": "%d random whole windows (fwd+bwd, float64 oracle) split over the W-MSA and SW-MSA modules "
-                      "of the 540x1080 C=512 workload, %.1f s of CPU work; the full-grid gather is outside the "
-                      "timed part; CPU %s, %d cores visible" % (windows, elapsed, platform.processor() or
-                                                                 platform.machine(), os.cpu_count() or 0),
-            "seconds": round(elapsed, 2)}
+                      "of the 540x1080 C=512 workload, %.1f s of CPU work (the full-grid gather is outside the "
+                      "timed part); forward alone: %.1f tokens/s over %d windows; CPU %s, %d cores visible, "
+                      "BLAS threads %d" % (fb["windows"], fb["seconds"], r["fwd"]["tokens_per_s"],
+                                           r["fwd"]["windows"], ci["model"], ci["cores_visible"],
+                                           ci["blas_threads"]),
+            "seconds": fb["seconds"], "fwd_tokens_per_s": r["fwd"]["tokens_per_s"], "cpu": ci}
 
 
 def _device_inputs(cfg):
@@ -178,6 +220,119 @@ def _device_inputs(cfg):
     x = torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16)
     dy = torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16)
     return types.SimpleNamespace(modules=mods, x_t=x, dy_t=dy)
+
+
+PEAK_F32_TFLOPS = 157.3   # MI355X fp32 vector peak (the fp32 path runs on FMA, not MFMA)
+
+
+def time_config(hip, N, stream, name, calls=50, warmup=10, cpu_seconds=2.0, with_cpu=True):
+    """One workload of the measurement plan on its own: every module forward (and backward in
+    reverse, for the bf16 workloads), `warmup` untimed calls, then `calls` calls each bracketed
+    by HIP events on the library's stream; median / min / max per call. bf16 inputs are drawn on
+    the device (seeded, same shapes and scales as the host recipe); the fp32 tiny workload uses
+    the host recipe. The fp64 oracle is timed on random whole windows of the same inputs (and the
+    brute-force per-token loop on the tiny workload)."""
+    import numpy as np
+    import torch
+    from shifted_window_attention_amd.device import ModuleOnDevice, from_dev, to_dev
+    from workloads import bf16_bits_to_f64, get_config, make_inputs
+    cfg = get_config(name)
+    f32 = cfg.dtype == "f32"
+    if f32:
+        inp = make_inputs(cfg, bias_scale=0.0)
+        x = to_dev(inp.x_dev, "f32")
+        dy = None
+        params = inp.modules
+    else:
+        inp = _device_inputs(cfg)
+        x, dy = inp.x_t, inp.dy_t
+        params = inp.modules
+    mods = [ModuleOnDevice(cfg, i, p) for i, p in enumerate(params)]
+    C = cfg.channels
+    ys = [torch.empty_like(x) for _ in mods]
+    dxs = [torch.empty_like(x) for _ in mods] if cfg.backward else []
+    grads = [{"w_qkv": torch.empty(3 * C, C, dtype=torch.float32, device="cuda"),
+              "b_qkv": torch.empty(3 * C, dtype=torch.float32, device="cuda"),
+              "w_proj": torch.empty(C, C, dtype=torch.float32, device="cuda"),
+              "b_proj": torch.empty(C, dtype=torch.float32, device="cuda"),
+              "table": torch.empty_like(m.table)} for m in mods] if cfg.backward else []
+
+    def call():
+        xin = x
+        for m, y in zip(mods, ys):
+            N.swin_attn_fwd(m.plan.handle, xin, m.w_qkv, m.b_qkv, m.w_proj, m.b_proj, m.table, y, m.saved,
+                            stream=stream)
+            xin = y
+        if cfg.backward:
+            d = dy
+            for i in reversed(range(len(mods))):
+                m, g = mods[i], grads[i]
+                xin = x if i == 0 else ys[i - 1]
+                N.swin_attn_bwd(m.plan.handle, d, xin, m.w_qkv, m.w_proj, m.table, m.saved, dxs[i], g["w_qkv"],
+                                g["b_qkv"], g["w_proj"], g["b_proj"], g["table"], m.ws, stream=stream)
+                d = dxs[i]
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = hip.events(2 * calls)
+    for i in range(calls):
+        assert hip.l.hipEventRecord(ev[2 * i], stream.cuda_stream) == 0
+        call()
+        assert hip.l.hipEventRecord(ev[2 * i + 1], stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    ms = np.array([hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(calls)])
+    hip.destroy(ev)
+    flops = 0
+    for m in mods:
+        f, _ = stage_flops_bytes(cfg, m.plan.stats["allowed_pairs"])
+        flops += sum(f[s] for s in FWD_STAGES) + (sum(f[s] for s in BWD_STAGES) if cfg.backward else 0)
+    med = float(np.median(ms))
+    tfl = flops / (med * 1e-3) / 1e12
+    res = {"config": cfg.description, "pass": "fwd+bwd" if cfg.backward else "fwd", "dtype": cfg.dtype,
+           "tokens": cfg.n_tokens, "modules": cfg.modules, "calls": calls, "warmup": warmup,
+           "median_ms": round(med, 4), "min_ms": round(float(ms.min()), 4), "max_ms": round(float(ms.max()), 4),
+           "tokens_per_s": round(cfg.n_tokens * cfg.modules / (med * 1e-3), 1),
+           "algorithmic_gflop": round(flops / 1e9, 3), "tflops": round(tfl, 2),
+           "inputs": "host recipe (seed 0)" if f32 else "device-drawn (seeded torch generator, recipe's scales)"}
+    if f32:
+        res["fp32_peak_frac"] = round(tfl / PEAK_F32_TFLOPS, 5)
+    else:
+        res["mfma_peak_frac"] = round(tfl / PEAK_BF16_TFLOPS, 4)
+    if with_cpu:
+        from oracle import swin_oracle as O
+        lays = [O.window_layout(cfg.batch, cfg.grid, cfg.window, s, cfg.periodic) for s in cfg.shifts]
+        if f32:
+            ps = [O.Params(pm.w_qkv, pm.b_qkv, pm.w_proj, pm.b_proj, pm.table) for pm in params]
+            xh = inp.x
+            dyh = None
+        else:
+            def f64(bits):
+                return bf16_bits_to_f64(bits)
+            ps = [O.Params(f64(pm.w_qkv_dev), f64(pm.b_qkv_dev), f64(pm.w_proj_dev), f64(pm.b_proj_dev),
+                           np.asarray(pm.table_dev, dtype=np.float64)) for pm in params]
+            xh = from_dev(x)
+            dyh = from_dev(dy)
+        if cfg.modules == 1:
+            xw = O.gather(xh, lays[0])
+            dyw = O.gather(dyh, lays[0]) if dyh is not None else None
+            if cfg.backward:
+                r = cpu_baseline_sampled(cfg, ps, lambda mi, ids: xw, lambda mi, ids: dyw, lays, cpu_seconds)
+            else:
+                t0 = time.perf_counter()
+                O.module_fwd(xh, ps[0], lays[0], cfg.heads)
+                el = time.perf_counter() - t0
+                r = {"fwd": {"tokens_per_s": round(cfg.n_tokens / el, 1), "windows": len(lays[0].windows),
+                             "seconds": round(el, 3)}}
+            if name == "tiny":
+                t0 = time.perf_counter()
+                O.brute_force_fwd(xh, ps[0], cfg.grid, cfg.window, cfg.shifts[0], cfg.periodic, cfg.heads)
+                el = time.perf_counter() - t0
+                r["brute_force_fwd"] = {"tokens_per_s": round(cfg.n_tokens / el, 1), "seconds": round(el, 2)}
+            res["cpu_oracle"] = r
+    for m in mods:
+        m.plan.close()
+    return res
 
 
 def time_window_moves(hip, N, plan, x, stream, cfg, reps=20):
@@ -509,7 +664,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--device-inputs", action="store_true",
                     help="draw inputs on the GPU (torch generator, same shapes and scales) instead of the seeded "
@@ -591,14 +746,18 @@ def main():
     total_ms = hip.elapsed_ms(t_start, t_end)
     ms_step = total_ms / args.steps
 
-    # per-stage durations: each call's events bracket its stages
+    # per-stage durations: each call's events bracket its stages; a step runs from its first
+    # call's start event to its last call's final event
     durations = {s: [] for s in FWD_STAGES + BWD_STAGES}
+    step_ms = []
     k = 0
     for _ in range(args.steps):
+        k0 = k
         for stages in (FWD_STAGES, FWD_STAGES, BWD_STAGES, BWD_STAGES):
             for j, s in enumerate(stages):
                 durations[s].append(hip.elapsed_ms(ev[k + j], ev[k + j + 1]))
             k += len(stages) + 1
+        step_ms.append(hip.elapsed_ms(ev[k0], ev[k - 1]))
     hip.destroy(ev)
 
     pairs = [m.plan.stats["allowed_pairs"] for m in mods]
@@ -611,6 +770,7 @@ def main():
         bytes_mod.append(b)
         flops_step += sum(f.values())
     tflops = flops_step / (ms_step * 1e-3) / 1e12
+    hbm_bytes_step = sum(sum(b.values()) for b in bytes_mod)
     tokens_step = cfg.n_tokens * cfg.modules
     value = tokens_step / (ms_step * 1e-3)
 
@@ -658,6 +818,12 @@ def main():
     block = time_block_chain(hip, N, stream, cfg, max(1, args.steps // 5), max(1, args.warmup // 5))
     routes = time_routes(hip, N, stream, cfg)
     tiled = time_tiled(hip, N, stream, cfg)
+    configs = {}
+    for name in ("om4", "ragged", "levels3d", "tiny"):
+        log("bench: workload", name)
+        configs[name] = time_config(hip, N, stream, name, calls=max(args.steps, 50), warmup=max(args.warmup, 10),
+                                    with_cpu=not args.no_cpu_baseline)
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -674,11 +840,14 @@ def main():
                    "tokens": cfg.n_tokens, "modules": cfg.modules, "global_batch": cfg.batch, "seq_len": 144,
                    "parallelism": "single GPU"},
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "step_ms": {"median": round(float(np.median(step_ms)), 4), "min": round(float(np.min(step_ms)), 4),
+                    "max": round(float(np.max(step_ms)), 4)},
+        "hbm_bytes_per_step": int(hbm_bytes_step),
         "algorithmic_gflop_per_step": round(flops_step / 1e9, 2),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "roofline": roof, "kernels": kernels, "window_moves": moves, "shard_share_8way": shard,
         "swin_block_chain": block, "saved_offload": offload,
-        "token_routes_8_ranks": routes, "tiled_w32_hd128": tiled, "cpu_baseline": cpu,
+        "token_routes_8_ranks": routes, "tiled_w32_hd128": tiled, "configs": configs, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
