@@ -17,6 +17,13 @@ def layouts(cfg):
     return [O.window_layout(cfg.batch, cfg.grid, cfg.window, s, cfg.periodic) for s in cfg.shifts]
 
 
+def _grad_dict(g):
+    d = {"w_qkv": g.w_qkv, "b_qkv": g.b_qkv, "w_proj": g.w_proj, "b_proj": g.b_proj, "table": g.table}
+    if g.abs is not None:
+        d["abs"] = g.abs
+    return d
+
+
 def chain_full(cfg, inp, with_bwd=True, with_bias=True):
     lays = layouts(cfg)
     ps = [params_of(m) for m in inp.modules]
@@ -35,9 +42,8 @@ def chain_full(cfg, inp, with_bwd=True, with_bias=True):
         d = inp.dy
         grads = [None] * len(ps)
         for i in reversed(range(len(ps))):
-            d, g = O.module_bwd(d, xs[i], ps[i], lays[i], cfg.heads)
-            grads[i] = {"w_qkv": g.w_qkv, "b_qkv": g.b_qkv, "w_proj": g.w_proj, "b_proj": g.b_proj,
-                        "table": g.table}
+            d, g = O.module_bwd(d, xs[i], ps[i], lays[i], cfg.heads, with_abs=True)
+            grads[i] = _grad_dict(g)
         out["dx"] = d
         out["grads"] = grads
     return out
@@ -131,9 +137,8 @@ def chain_masked_dy(cfg, inp, last_windows, dy_masked):
     if len(lays) == 1:
         lay, p = lays[0], ps[0]
         g = O.windows_bwd(O.gather(dy_masked, lay), O.gather(inp.x, lay), p, lay, cfg.heads,
-                          window_ids=last_windows)
-        res["grads"][0] = {"w_qkv": g.w_qkv, "b_qkv": g.b_qkv, "w_proj": g.w_proj, "b_proj": g.b_proj,
-                           "table": g.table}
+                          window_ids=last_windows, with_abs=True)
+        res["grads"][0] = _grad_dict(g)
         toks = _tokens_of_windows(lay, last_windows)
         slots = np.concatenate([np.arange(lay.windows[i].tok_off, lay.windows[i].tok_off + lay.windows[i].n)
                                 for i in last_windows])
@@ -151,15 +156,13 @@ def chain_masked_dy(cfg, inp, last_windows, dy_masked):
                               for i in S1f])
     y1[_tokens_of_windows(l1, S1f)] = y1w[slots1f]
     g2 = O.windows_bwd(O.gather(dy_masked, l2), O.gather(y1.reshape(shape), l2), p2, l2, cfg.heads,
-                       window_ids=S2)
-    res["grads"][1] = {"w_qkv": g2.w_qkv, "b_qkv": g2.b_qkv, "w_proj": g2.w_proj, "b_proj": g2.b_proj,
-                       "table": g2.table}
+                       window_ids=S2, with_abs=True)
+    res["grads"][1] = _grad_dict(g2)
     dy1 = np.zeros_like(y1)
     slots2 = np.concatenate([np.arange(l2.windows[i].tok_off, l2.windows[i].tok_off + l2.windows[i].n) for i in S2])
     dy1[T2] = g2.dxw[slots2]
-    g1 = O.windows_bwd(O.gather(dy1.reshape(shape), l1), xw1, p1, l1, cfg.heads, window_ids=S1f)
-    res["grads"][0] = {"w_qkv": g1.w_qkv, "b_qkv": g1.b_qkv, "w_proj": g1.w_proj, "b_proj": g1.b_proj,
-                       "table": g1.table}
+    g1 = O.windows_bwd(O.gather(dy1.reshape(shape), l1), xw1, p1, l1, cfg.heads, window_ids=S1f, with_abs=True)
+    res["grads"][0] = _grad_dict(g1)
     res["dx_tokens"], res["dx"] = _tokens_of_windows(l1, S1f), g1.dxw[slots1f]
     return res
 

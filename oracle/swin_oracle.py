@@ -245,11 +245,16 @@ class Grads:
     w_proj: np.ndarray
     b_proj: np.ndarray
     table: np.ndarray
+    # with_abs: for every reduced gradient, the same sum taken over the absolute values of its
+    # terms (e.g. sum_t |d(qkv)_t|^T |x~_t| for dW_qkv, sum of |dS| per bin for dT). A
+    # diagnostic that leaves the gradients unchanged: it measures how much the terms cancel,
+    # which sets how far rounding in the terms can move the sum.
+    abs: Optional[Dict[str, np.ndarray]] = None
 
 
 def windows_bwd(dyw: np.ndarray, xw: np.ndarray, p: Params, layout: Layout, heads: int,
                 scale: Optional[float] = None, window_ids: Optional[Sequence[int]] = None,
-                max_batch: int = 64) -> Grads:
+                max_batch: int = 64, with_abs: bool = False) -> Grads:
     """Hand-derived backward of windows_fwd (forward recomputed per group).
 
     dW_proj = dy~^T o; db_proj = sum dy~; do = dy~ W_proj;
@@ -264,6 +269,9 @@ def windows_bwd(dyw: np.ndarray, xw: np.ndarray, p: Params, layout: Layout, head
               w_proj=np.zeros_like(p.w_proj), b_proj=np.zeros_like(p.b_proj), table=np.zeros_like(p.table))
     nbins = p.table[0].size
     dtab = g.table.reshape(heads, nbins)
+    if with_abs:
+        g.abs = {k: np.zeros_like(getattr(g, k)) for k in ("w_qkv", "b_qkv", "w_proj", "b_proj", "table")}
+        atab = g.abs["table"].reshape(heads, nbins)
     for ext, wids in _groups(layout, window_ids, max_batch):
         rows = _window_rows(layout, wids)
         G, n = rows.shape
@@ -282,6 +290,9 @@ def windows_bwd(dyw: np.ndarray, xw: np.ndarray, p: Params, layout: Layout, head
         dyt = dyw[rows]                                            # [G, n, C]
         g.w_proj += np.einsum("gnc,gnd->cd", dyt, o)
         g.b_proj += dyt.sum(axis=(0, 1))
+        if with_abs:
+            g.abs["w_proj"] += np.einsum("gnc,gnd->cd", np.abs(dyt), np.abs(o))
+            g.abs["b_proj"] += np.abs(dyt).sum(axis=(0, 1))
         do = (dyt @ p.w_proj).reshape(G, n, heads, hd).transpose(0, 2, 1, 3)
         dv = P.transpose(0, 1, 3, 2) @ do
         dP = do @ v.transpose(0, 1, 3, 2)
@@ -292,9 +303,16 @@ def windows_bwd(dyw: np.ndarray, xw: np.ndarray, p: Params, layout: Layout, head
         dsum = dS.sum(axis=0)                                      # [nh, n, n]
         for h in range(heads):
             np.add.at(dtab[h], bins.ravel(), dsum[h].ravel())
+        if with_abs:
+            asum = np.abs(dS).sum(axis=0)
+            for h in range(heads):
+                np.add.at(atab[h], bins.ravel(), asum[h].ravel())
         dqkv = np.concatenate([t.transpose(0, 2, 1, 3).reshape(G, n, C) for t in (dq, dk, dv)], axis=-1)
         g.w_qkv += np.einsum("gnc,gnd->cd", dqkv, xt)
         g.b_qkv += dqkv.sum(axis=(0, 1))
+        if with_abs:
+            g.abs["w_qkv"] += np.einsum("gnc,gnd->cd", np.abs(dqkv), np.abs(xt))
+            g.abs["b_qkv"] += np.abs(dqkv).sum(axis=(0, 1))
         g.dxw[rows] = dqkv @ p.w_qkv
     return g
 
@@ -312,9 +330,10 @@ def module_fwd(x: np.ndarray, p: Params, layout: Layout, heads: int, scale: Opti
 
 
 def module_bwd(dy: np.ndarray, x: np.ndarray, p: Params, layout: Layout, heads: int,
-               scale: Optional[float] = None, max_batch: int = 64):
+               scale: Optional[float] = None, max_batch: int = 64, with_abs: bool = False):
     """Returns (dx on the grid, Grads with dxw)."""
-    g = windows_bwd(gather(dy, layout), gather(x, layout), p, layout, heads, scale, max_batch=max_batch)
+    g = windows_bwd(gather(dy, layout), gather(x, layout), p, layout, heads, scale, max_batch=max_batch,
+                    with_abs=with_abs)
     return scatter(g.dxw, layout), g
 
 

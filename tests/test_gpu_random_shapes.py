@@ -2,10 +2,11 @@
 3-D grids, ragged edges, head_dim 32/64/128, batch 1-2, every periodic combination of the lat
 and lon axes, windows from 16 to over 1000 tokens (so both the one-tile and the tiled kernels,
 tables held in LDS and in global memory), one or two chained modules. Same bars as the other
-parity tests: per-token outputs max-abs <= 2e-2, reduced gradients 2e-2 * max(1, |ref|_inf)."""
+parity tests (tests/bars.py): per-token outputs 2e-2 + ulp_bf16(ref)/2, reduced gradients 2e-2 * max(1, |ref|_inf)."""
 import numpy as np
 import pytest
 
+from tests.bars import reduced_excess, token_excess
 from tests.gpu_util import log, run_chain
 from tests.oracle_runner import chain_full
 from workloads import make_inputs
@@ -13,7 +14,6 @@ from workloads.configs import SwinConfig
 
 pytestmark = pytest.mark.gpu
 
-TOL = 2e-2
 
 
 def random_configs(n=16, seed=11):
@@ -59,12 +59,10 @@ def test_random_shape_vs_oracle(c):
     inp = make_inputs(c)
     got = run_chain(c, inp)
     ref = chain_full(c, inp)
-    ey = float(np.abs(got["y"] - ref["y"]).max())
-    edx = float(np.abs(got["dx"] - ref["dx"]).max())
-    log("  y max-abs %.3e  dx max-abs %.3e" % (ey, edx))
-    assert ey <= TOL and edx <= TOL
+    (exy, ey), (exd, edx) = token_excess(got["y"], ref["y"]), token_excess(got["dx"], ref["dx"])
+    log("  y max-abs %.3e  dx max-abs %.3e (worst excess over the bar %.3e, %.3e)" % (ey, edx, exy, exd))
+    assert exy <= 0.0 and exd <= 0.0
     for i, (gm, rm) in enumerate(zip(got["grads"], ref["grads"])):
         for k in ("w_qkv", "b_qkv", "w_proj", "b_proj", "table"):
-            r, g = np.asarray(rm[k]).reshape(-1), np.asarray(gm[k]).reshape(-1)
-            err, bound = float(np.abs(g - r).max()), TOL * max(1.0, float(np.abs(r).max()))
-            assert err <= bound, (c.name, i, k, err, bound)
+            ex, err = reduced_excess(gm[k], rm[k], rm.get("abs", {}).get(k))
+            assert ex <= 0.0, (c.name, i, k, err, ex)

@@ -101,3 +101,18 @@ def test_torch_autograd_crosscheck(case):
     (y * torch.from_numpy(inp.dy)).sum().backward()
     for t, ref in zip(ts, (dx, g.w_qkv, g.b_qkv, g.w_proj, g.b_proj, g.table)):
         assert np.abs(t.grad.numpy() - ref).max() < 1e-11 * max(1.0, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("case", FD_CASES, ids=lambda c: c[0])
+def test_absolute_term_sums(case):
+    """The absolute-term sums (a diagnostic of how much a reduced gradient's terms cancel) leave
+    the gradients unchanged, bound them from above (|sum a| <= sum |a|), and for the proj bias
+    are the sum of |dy| over the tokens."""
+    cfg, inp, p, lay = setup(case)
+    _, g0 = O.module_bwd(inp.dy, inp.x, p, lay, cfg.heads)
+    _, g1 = O.module_bwd(inp.dy, inp.x, p, lay, cfg.heads, with_abs=True)
+    assert g0.abs is None
+    for k in ("w_qkv", "b_qkv", "w_proj", "b_proj", "table"):
+        assert np.array_equal(getattr(g0, k), getattr(g1, k)), k
+        assert np.all(g1.abs[k] >= np.abs(getattr(g1, k)) * (1 - 1e-12)), k
+    np.testing.assert_allclose(g1.abs["b_proj"], np.abs(inp.dy).reshape(-1, cfg.channels).sum(0), rtol=1e-12)

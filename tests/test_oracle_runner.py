@@ -38,5 +38,7 @@ def test_masked_dy_equals_full(name, grid):
     r = chain_masked_dy(cfg, inp, pick, inp.dy)
     assert np.abs(full["dx"].reshape(-1, C)[r["dx_tokens"]] - r["dx"]).max() < 1e-12
     for gf, gr in zip(full["grads"], r["grads"]):
-        for k in gf:
+        for k in ("w_qkv", "b_qkv", "w_proj", "b_proj", "table"):
             assert np.abs(gf[k] - gr[k]).max() < 1e-10 * max(1.0, np.abs(gf[k]).max()), k
+            # the absolute-term sums reduce over the same windows, so they agree too
+            assert np.abs(gf["abs"][k] - gr["abs"][k]).max() < 1e-10 * max(1.0, np.abs(gf["abs"][k]).max()), k
