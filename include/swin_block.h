@@ -18,6 +18,9 @@
  * forward/backward path (only swin_block_plan_create allocates). Activations are
  * [B, D, H, W, C] bf16; weights bf16 in [out, in] layout; layer-norm scales and shifts bf16
  * [C]; the relative-position table fp32; gradients fp32, overwritten (never accumulated).
+ * Inside the block the residual stream h and its gradient are kept in fp32 (only GEMM
+ * operands and the outputs y, dx are rounded to bf16), and y = h + W2 (.) + b2 and
+ * dx = dh + LN1'(.) are each rounded once.
  */
 #ifndef SWIN_BLOCK_H_
 #define SWIN_BLOCK_H_

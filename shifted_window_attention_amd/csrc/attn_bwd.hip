@@ -331,12 +331,12 @@ static const bwd_launcher kBwd[kMaxBwdTiles + 1] = {nullptr,           launch_bw
 hipError_t launch_dproj_bf16(const swin_attn_plan* p, const void* dy, const void* wprojT, void* dO, const void* o,
                              float* dd, hipStream_t s);
 hipError_t launch_dgrad_qkv_bf16(const swin_attn_plan* p, const void* dqkv, const void* wqkvT, void* dx,
-                                 hipStream_t s);
+                                 float* dx32, hipStream_t s);
 
 hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* x, const void* w_qkv,
                            const void* w_proj, const float* table, const void* saved, void* dx, float* dw_qkv,
                            float* db_qkv, float* dw_proj, float* db_proj, float* dtable, void* ws,
-                           hipStream_t s) {
+                           hipStream_t s, float* dx32) {
   const int C = p->C;
   const char* sv = (const char*)saved;
   const bf16* qkv = (const bf16*)sv;
@@ -407,7 +407,7 @@ hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* 
   }
   if (e != hipSuccess) return e;
   // QKV backward: dx = scatter(dqkv W_qkv), dW_qkv = dqkv^T gather(x), db_qkv
-  e = launch_dgrad_qkv_bf16(p, dqkv, wqkvT, dx, s);
+  e = launch_dgrad_qkv_bf16(p, dqkv, wqkvT, dx, dx32, s);
   if (e == hipSuccess) e = trace_mark(s);
   if (e == hipSuccess)
     e = launch_wgrad_bf16(dqkv, 3 * C, (const bf16*)x, C, p->n_tok, 3 * C, C, p->wgrad_splits_qkv,

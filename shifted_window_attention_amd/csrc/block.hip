@@ -18,11 +18,26 @@ __device__ __forceinline__ float wave_sum64(float v) {
   return v;
 }
 
+// Eight consecutive channels of a bf16 or fp32 row as fp32 (one 16-byte load, or two).
+__device__ __forceinline__ void load8(const bf16* p, float (&v)[8]) {
+  const bf16x8 t = *(const bf16x8*)p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = to_f32(t[e]);
+}
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = a[e];
+    v[4 + e] = b[e];
+  }
+}
+
 // y = (x - mean) rstd g + b per row of C channels (biased variance, fp32 statistics);
 // mean and rstd are saved for the backward. One wave per row, lane l holds the 8-channel
 // chunks l, l + 64, ... (CH of them).
-template <int CH>
-__global__ __launch_bounds__(256) void k_layernorm_fwd(const bf16* __restrict__ x, const bf16* __restrict__ g,
+template <int CH, typename TX>
+__global__ __launch_bounds__(256) void k_layernorm_fwd(const TX* __restrict__ x, const bf16* __restrict__ g,
                                                        const bf16* __restrict__ b, bf16* __restrict__ y,
                                                        float* __restrict__ mean_out, float* __restrict__ rstd_out,
                                                        int64_t rows, int C, float eps) {
@@ -35,12 +50,14 @@ __global__ __launch_bounds__(256) void k_layernorm_fwd(const bf16* __restrict__ 
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int ch = lane + 64 * c;
-    const bf16x8 t = ch < nch ? *(const bf16x8*)(x + row * C + 8 * ch) : bf16x8{};
+    if (ch < nch) {
+      load8(x + row * C + 8 * ch, v[c]);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v[c][e] = to_f32(t[e]);
-      sum += v[c][e];
+      for (int e = 0; e < 8; ++e) v[c][e] = 0.f;
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum += v[c][e];
   }
   const float mean = wave_sum64(sum) / C;
   float sq = 0.f;
@@ -67,8 +84,11 @@ __global__ __launch_bounds__(256) void k_layernorm_fwd(const bf16* __restrict__ 
   }
 }
 
-// Backward of k_layernorm_fwd plus a residual gradient:
+// Backward of k_layernorm_fwd (upstream gradient dy in fp32: the products that produce it write
+// fp32) plus a residual gradient:
 //   dx = dres + rstd (dxhat - mean(dxhat) - xhat mean(dxhat xhat)),  dxhat = dy g,
+// rounded once to bf16 (and also stored in fp32 when dx32 is given: the block's residual
+// gradient stream stays in fp32),
 // and, per workgroup (a contiguous range of `per` rows), partial sums of dg = sum dy xhat
 // and db = sum dy (part[group][0][:] and part[group][1][:]), combined over the 4 waves in a
 // fixed order. At most kLnMaxGroups workgroups, so that the final reduction stays short.
@@ -80,12 +100,12 @@ static int64_t ln_rows_per_group(int64_t rows) {
   return (per + 3) / 4 * 4;
 }
 
-template <int CH>
-__global__ __launch_bounds__(256) void k_layernorm_bwd(const bf16* __restrict__ dy, const bf16* __restrict__ x,
+template <int CH, typename TX, typename TR>
+__global__ __launch_bounds__(256) void k_layernorm_bwd(const float* __restrict__ dy, const TX* __restrict__ x,
                                                        const float* __restrict__ mean, const float* __restrict__ rstd,
-                                                       const bf16* __restrict__ g, const bf16* __restrict__ dres,
-                                                       bf16* __restrict__ dx, float* __restrict__ part, int64_t rows,
-                                                       int64_t per, int C) {
+                                                       const bf16* __restrict__ g, const TR* __restrict__ dres,
+                                                       bf16* __restrict__ dx, float* __restrict__ dx32,
+                                                       float* __restrict__ part, int64_t rows, int64_t per, int C) {
   __shared__ float red[4][2][64 * 8 * CH];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nch = C / 8;
@@ -110,12 +130,24 @@ __global__ __launch_bounds__(256) void k_layernorm_bwd(const bf16* __restrict__ 
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int ch = lane + 64 * c;
-      const bf16x8 tx = ch < nch ? *(const bf16x8*)(x + row * C + 8 * ch) : bf16x8{};
-      const bf16x8 ty = ch < nch ? *(const bf16x8*)(dy + row * C + 8 * ch) : bf16x8{};
+      float tx[8];
+      if (ch < nch) {
+        load8(x + row * C + 8 * ch, tx);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tx[e] = 0.f;
+      }
+      float ty[8];
+      if (ch < nch) {
+        load8(dy + row * C + 8 * ch, ty);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ty[e] = 0.f;
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float d = to_f32(ty[e]);
-        xh[c][e] = ch < nch ? (to_f32(tx[e]) - mu) * rs : 0.f;
+        const float d = ty[e];
+        xh[c][e] = ch < nch ? (tx[e] - mu) * rs : 0.f;
         dxh[c][e] = d * gv[c][e];
         s1 += dxh[c][e];
         s2 += dxh[c][e] * xh[c][e];
@@ -129,11 +161,20 @@ __global__ __launch_bounds__(256) void k_layernorm_bwd(const bf16* __restrict__ 
     for (int c = 0; c < CH; ++c) {
       const int ch = lane + 64 * c;
       if (ch < nch) {
-        const bf16x8 tr = *(const bf16x8*)(dres + row * C + 8 * ch);
+        float tr[8], r[8];
+        load8(dres + row * C + 8 * ch, tr);
         bf16x8 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = to_bf16(rs * (dxh[c][e] - s1 - xh[c][e] * s2) + to_f32(tr[e]));
+        for (int e = 0; e < 8; ++e) {
+          r[e] = rs * (dxh[c][e] - s1 - xh[c][e] * s2) + tr[e];
+          o[e] = to_bf16(r[e]);
+        }
         *(bf16x8*)(dx + row * C + 8 * ch) = o;
+        if (dx32) {
+          float* d32 = dx32 + row * C + 8 * ch;
+          *(f32x4*)d32 = f32x4{r[0], r[1], r[2], r[3]};
+          *(f32x4*)(d32 + 4) = f32x4{r[4], r[5], r[6], r[7]};
+        }
       }
     }
   }
@@ -177,34 +218,47 @@ __global__ __launch_bounds__(256) void k_reduce_groups(const float* __restrict__
   }
 }
 
-hipError_t launch_layernorm_fwd(const bf16* x, const bf16* g, const bf16* b, bf16* y, float* mean, float* rstd,
+template <typename TX>
+hipError_t launch_layernorm_fwd(const TX* x, const bf16* g, const bf16* b, bf16* y, float* mean, float* rstd,
                                 int64_t rows, int C, float eps, hipStream_t s) {
   const unsigned blocks = (unsigned)((rows + 3) / 4);
   if (C <= 512)
-    k_layernorm_fwd<1><<<blocks, 256, 0, s>>>(x, g, b, y, mean, rstd, rows, C, eps);
+    k_layernorm_fwd<1, TX><<<blocks, 256, 0, s>>>(x, g, b, y, mean, rstd, rows, C, eps);
   else
-    k_layernorm_fwd<2><<<blocks, 256, 0, s>>>(x, g, b, y, mean, rstd, rows, C, eps);
+    k_layernorm_fwd<2, TX><<<blocks, 256, 0, s>>>(x, g, b, y, mean, rstd, rows, C, eps);
   return hipGetLastError();
 }
+template hipError_t launch_layernorm_fwd<bf16>(const bf16*, const bf16*, const bf16*, bf16*, float*, float*, int64_t,
+                                               int, float, hipStream_t);
+template hipError_t launch_layernorm_fwd<float>(const float*, const bf16*, const bf16*, bf16*, float*, float*, int64_t,
+                                                int, float, hipStream_t);
 
 int layernorm_groups(int64_t rows) {
   const int64_t per = ln_rows_per_group(rows);
   return (int)((rows + per - 1) / per);
 }
 
-hipError_t launch_layernorm_bwd(const bf16* dy, const bf16* x, const float* mean, const float* rstd, const bf16* g,
-                                const bf16* dres, bf16* dx, float* part, float* dg, float* db, int64_t rows, int C,
-                                hipStream_t s) {
+template <typename TX, typename TR>
+hipError_t launch_layernorm_bwd(const float* dy, const TX* x, const float* mean, const float* rstd, const bf16* g,
+                                const TR* dres, bf16* dx, float* dx32, float* part, float* dg, float* db, int64_t rows,
+                                int C, hipStream_t s) {
   const int groups = layernorm_groups(rows);
   const int64_t per = ln_rows_per_group(rows);
   if (C <= 512)
-    k_layernorm_bwd<1><<<groups, 256, 0, s>>>(dy, x, mean, rstd, g, dres, dx, part, rows, per, C);
+    k_layernorm_bwd<1, TX, TR><<<groups, 256, 0, s>>>(dy, x, mean, rstd, g, dres, dx, dx32, part, rows, per, C);
   else
-    k_layernorm_bwd<2><<<groups, 256, 0, s>>>(dy, x, mean, rstd, g, dres, dx, part, rows, per, C);
+    k_layernorm_bwd<2, TX, TR><<<groups, 256, 0, s>>>(dy, x, mean, rstd, g, dres, dx, dx32, part, rows, per, C);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   k_reduce_groups<<<(unsigned)((2 * C + 63) / 64), 256, 0, s>>>(part, groups, 2 * C, dg, db);
   return hipGetLastError();
 }
+// LN2 of the block: fp32 h, bf16 dy; LN1: bf16 x, fp32 residual gradient
+template hipError_t launch_layernorm_bwd<float, bf16>(const float*, const float*, const float*, const float*,
+                                                      const bf16*, const bf16*, bf16*, float*, float*, float*, float*,
+                                                      int64_t, int, hipStream_t);
+template hipError_t launch_layernorm_bwd<bf16, float>(const float*, const bf16*, const float*, const float*,
+                                                      const bf16*, const float*, bf16*, float*, float*, float*, float*,
+                                                      int64_t, int, hipStream_t);
 
 }  // namespace swin

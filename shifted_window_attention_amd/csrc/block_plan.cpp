@@ -17,7 +17,7 @@ struct swin_block_plan {
   // saved state (byte offsets)
   size_t s_xn1 = 0, s_h = 0, s_xn2 = 0, s_a1 = 0, s_g1 = 0, s_st1 = 0, s_st2 = 0, s_total = 0;
   // backward workspace (byte offsets; the attention module's workspace comes first)
-  size_t w_dh = 0, w_dxn = 0, w_da1 = 0, w_w1t = 0, w_w2t = 0, w_ln = 0, w_part = 0, w_total = 0;
+  size_t w_dh = 0, w_dh32 = 0, w_dxn32 = 0, w_da1 = 0, w_w1t = 0, w_w2t = 0, w_ln = 0, w_part = 0, w_total = 0;
   int split_w1 = 1, split_w2 = 1;
   int64_t chunk_w1 = 0, chunk_w2 = 0;
 };
@@ -64,10 +64,12 @@ swin_status swin_block_plan_create(const swin_block_desc* desc, swin_block_plan*
   p->eps = desc->ln_eps > 0.f ? desc->ln_eps : 1e-5f;
   const int64_t T = ap->n_tok;
   p->T = T;
-  const size_t act = align256((size_t)T * p->C * 2), hid = align256((size_t)T * H * 2), sts = align256((size_t)T * 8);
+  // the residual stream h and its gradient stay in fp32 (act32); GEMM operands are bf16 (act)
+  const size_t act = align256((size_t)T * p->C * 2), act32 = align256((size_t)T * p->C * 4),
+               hid = align256((size_t)T * H * 2), sts = align256((size_t)T * 8);
   size_t o = align256(ap->saved_total);
   p->s_xn1 = o; o += act;
-  p->s_h = o; o += act;
+  p->s_h = o; o += act32;
   p->s_xn2 = o; o += act;
   p->s_a1 = o; o += hid;
   p->s_g1 = o; o += hid;
@@ -78,7 +80,8 @@ swin_status swin_block_plan_create(const swin_block_desc* desc, swin_block_plan*
   swin::wgrad_split(T, p->C, H, &p->split_w2, &p->chunk_w2);
   o = align256(ap->bwd_total);
   p->w_dh = o; o += act;
-  p->w_dxn = o; o += act;
+  p->w_dh32 = o; o += act32;
+  p->w_dxn32 = o; o += act32;
   p->w_da1 = o; o += hid;
   p->w_w1t = o; o += align256((size_t)H * p->C * 2);
   p->w_w2t = o; o += align256((size_t)H * p->C * 2);
@@ -121,7 +124,7 @@ swin_status swin_block_fwd(const swin_block_plan* plan, const void* x, const swi
   const int C = plan->C, H = plan->H;
   const int64_t T = plan->T;
   bf16_t* xn1 = (bf16_t*)(sv + plan->s_xn1);
-  bf16_t* h = (bf16_t*)(sv + plan->s_h);
+  float* h = (float*)(sv + plan->s_h);
   bf16_t* xn2 = (bf16_t*)(sv + plan->s_xn2);
   bf16_t* a1 = (bf16_t*)(sv + plan->s_a1);
   bf16_t* g1 = (bf16_t*)(sv + plan->s_g1);
@@ -132,20 +135,22 @@ swin_status swin_block_fwd(const swin_block_plan* plan, const void* x, const swi
   void* o = sv + ap->saved_qkv;
   float* lse = (float*)(sv + ap->saved_qkv + ap->saved_o);
 
-  hipError_t e = swin::launch_layernorm_fwd((const bf16_t*)x, (const bf16_t*)prm->ln1_g, (const bf16_t*)prm->ln1_b,
-                                            xn1, st1, st1 + T, T, C, plan->eps, s);
+  hipError_t e = swin::launch_layernorm_fwd<bf16_t>((const bf16_t*)x, (const bf16_t*)prm->ln1_g,
+                                                    (const bf16_t*)prm->ln1_b, xn1, st1, st1 + T, T, C, plan->eps, s);
   if (e == hipSuccess) e = swin::launch_qkv_fwd_bf16(ap, xn1, prm->w_qkv, prm->b_qkv, qkv, s);
   if (e == hipSuccess) e = swin::launch_attn_fwd_bf16(ap, qkv, prm->bias_table, o, lse, s);
-  if (e == hipSuccess) e = swin::launch_proj_fwd_res_bf16(ap, o, prm->w_proj, prm->b_proj, x, h, s);
+  // h = x + proj(o), kept in fp32
+  if (e == hipSuccess) e = swin::launch_proj_fwd_res_f32(ap, o, prm->w_proj, prm->b_proj, x, h, s);
   if (e == hipSuccess)
-    e = swin::launch_layernorm_fwd(h, (const bf16_t*)prm->ln2_g, (const bf16_t*)prm->ln2_b, xn2, st2, st2 + T, T, C,
-                                   plan->eps, s);
+    e = swin::launch_layernorm_fwd<float>(h, (const bf16_t*)prm->ln2_g, (const bf16_t*)prm->ln2_b, xn2, st2, st2 + T,
+                                          T, C, plan->eps, s);
   if (e == hipSuccess)
     e = swin::launch_rows_gemm_bf16(xn2, C, (const bf16_t*)prm->w1, C, T, H, C, (const bf16_t*)prm->b1, 2, g1, a1,
-                                    nullptr, nullptr, s);
+                                    nullptr, nullptr, nullptr, nullptr, s);
+  // y = h + W2 g1 + b2, one rounding
   if (e == hipSuccess)
     e = swin::launch_rows_gemm_bf16(g1, H, (const bf16_t*)prm->w2, H, T, C, H, (const bf16_t*)prm->b2, 0, (bf16_t*)y,
-                                    nullptr, nullptr, h, s);
+                                    nullptr, nullptr, nullptr, h, nullptr, s);
   return hip_status(e, "block forward");
 }
 
@@ -167,7 +172,7 @@ swin_status swin_block_bwd(const swin_block_plan* plan, const void* dy, const vo
   const int64_t T = plan->T;
   const char* sv = (const char*)saved;
   const bf16_t* xn1 = (const bf16_t*)(sv + plan->s_xn1);
-  const bf16_t* h = (const bf16_t*)(sv + plan->s_h);
+  const float* h = (const float*)(sv + plan->s_h);
   const bf16_t* xn2 = (const bf16_t*)(sv + plan->s_xn2);
   const bf16_t* a1 = (const bf16_t*)(sv + plan->s_a1);
   const bf16_t* g1 = (const bf16_t*)(sv + plan->s_g1);
@@ -175,7 +180,8 @@ swin_status swin_block_bwd(const swin_block_plan* plan, const void* dy, const vo
   const float* st2 = (const float*)(sv + plan->s_st2);
   char* w = (char*)ws;
   bf16_t* dh = (bf16_t*)(w + plan->w_dh);
-  bf16_t* dxn = (bf16_t*)(w + plan->w_dxn);
+  float* dh32 = (float*)(w + plan->w_dh32);
+  float* dxn = (float*)(w + plan->w_dxn32);  // dLN2-out, then dLN1-out, in fp32
   bf16_t* da1 = (bf16_t*)(w + plan->w_da1);
   bf16_t* w1t = (bf16_t*)(w + plan->w_w1t);
   bf16_t* w2t = (bf16_t*)(w + plan->w_w2t);
@@ -187,26 +193,29 @@ swin_status swin_block_bwd(const swin_block_plan* plan, const void* dy, const vo
   hipError_t e = swin::launch_transpose_bf16(prm->w1, w1t, H, C, s);
   if (e == hipSuccess) e = swin::launch_transpose_bf16(prm->w2, w2t, C, H, s);
   if (e == hipSuccess)
-    e = swin::launch_rows_gemm_bf16((const bf16_t*)dy, C, w2t, C, T, H, C, nullptr, 3, da1, nullptr, a1, nullptr, s);
+    e = swin::launch_rows_gemm_bf16((const bf16_t*)dy, C, w2t, C, T, H, C, nullptr, 3, da1, nullptr, a1, nullptr,
+                                    nullptr, nullptr, s);
   if (e == hipSuccess)
     e = swin::launch_wgrad_bf16((const bf16_t*)dy, C, g1, H, T, C, H, plan->split_w2, plan->chunk_w2, part, gr->w2,
                                 gr->b2, s);
   if (e == hipSuccess)
     e = swin::launch_wgrad_bf16(da1, H, xn2, C, T, H, C, plan->split_w1, plan->chunk_w1, part, gr->w1, gr->b1, s);
   if (e == hipSuccess)
-    e = swin::launch_rows_gemm_bf16(da1, H, w1t, H, T, C, H, nullptr, 0, dxn, nullptr, nullptr, nullptr, s);
-  // LN2: dh = dy + LN2'(dxn2)
+    e = swin::launch_rows_gemm_bf16(da1, H, w1t, H, T, C, H, nullptr, 0, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                    dxn, s);
+  // LN2: dh = dy + LN2'(dxn2), in bf16 for the attention module's products and in fp32 for
+  // the residual add of LN1's backward
   if (e == hipSuccess)
-    e = swin::launch_layernorm_bwd(dxn, h, st2, st2 + T, (const bf16_t*)prm->ln2_g, (const bf16_t*)dy, dh, lnpart,
-                                   gr->ln2_g, gr->ln2_b, T, C, s);
+    e = swin::launch_layernorm_bwd<float, bf16_t>(dxn, h, st2, st2 + T, (const bf16_t*)prm->ln2_g, (const bf16_t*)dy,
+                                                  dh, dh32, lnpart, gr->ln2_g, gr->ln2_b, T, C, s);
   if (e != hipSuccess) return hip_status(e, "block backward (MLP)");
   // attention module with dy = dh on its input LN1(x); dxn1 reuses the dxn buffer
-  e = swin::launch_bwd_bf16(ap, dh, xn1, prm->w_qkv, prm->w_proj, prm->bias_table, sv, dxn, gr->w_qkv, gr->b_qkv,
-                            gr->w_proj, gr->b_proj, gr->bias_table, w, s);
-  // LN1: dx = dh + LN1'(dxn1)
+  e = swin::launch_bwd_bf16(ap, dh, xn1, prm->w_qkv, prm->w_proj, prm->bias_table, sv, nullptr, gr->w_qkv,
+                            gr->b_qkv, gr->w_proj, gr->b_proj, gr->bias_table, w, s, dxn);
+  // LN1: dx = dh + LN1'(dxn1), one rounding
   if (e == hipSuccess)
-    e = swin::launch_layernorm_bwd(dxn, (const bf16_t*)x, st1, st1 + T, (const bf16_t*)prm->ln1_g, dh, (bf16_t*)dx,
-                                   lnpart, gr->ln1_g, gr->ln1_b, T, C, s);
+    e = swin::launch_layernorm_bwd<bf16_t, float>(dxn, (const bf16_t*)x, st1, st1 + T, (const bf16_t*)prm->ln1_g, dh32,
+                                                  (bf16_t*)dx, nullptr, lnpart, gr->ln1_g, gr->ln1_b, T, C, s);
   return hip_status(e, "block backward");
 }
 

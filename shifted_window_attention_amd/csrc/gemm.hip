@@ -28,6 +28,8 @@ struct EpiParams {
   bf16* out2;                // mode 2: pre-activation rows [M][N]
   const bf16* aux;           // mode 3: the pre-activation the GELU derivative is taken at
   const bf16* res;           // mode 0: if set, residual rows added before rounding (same layout as out)
+  const float* res_f32;      // mode 0: if set, fp32 residual rows added before rounding (pitch ldc)
+  float* out_f32;            // mode 0: if set, the rows are written here in fp32 (pitch ldc) instead of to out
   const int32_t* out_rows;   // mode 0: destination row of each C row (NULL: identity)
   int64_t ldc;               // mode 0: row pitch of out (elements)
   const bf16* bias;          // [N] or NULL
@@ -96,7 +98,7 @@ __device__ __forceinline__ float gelu_grad_f(float a) {
   return fmaf(a * 0.39894228040143268f, g, cdf);
 }
 
-// Epilogue of the element-wise modes (2, 3, and 0 with a residual): the accumulator tile
+// Epilogue of the element-wise modes (2, 3, and 0 with a residual or an fp32 output): the accumulator tile
 // plus bias goes through LDS as fp32 in two halves of BM/2 rows, so the residual add or the
 // activation is applied before the single rounding to bf16; 16-byte row stores. The rows a
 // thread reads (GELU pre-activation or residual) are loaded for the whole half before the
@@ -154,6 +156,29 @@ __device__ __forceinline__ void epilogue_f32(const f32x16 (&acc)[NtCfg<BM, BN>::
       const f32x4 lo = *(const f32x4*)(Cs + row * FP + cc), hi = *(const f32x4*)(Cs + row * FP + cc + 4);
       float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       const int64_t orow = (ep.mode == 0 && ep.out_rows) ? (int64_t)ep.out_rows[m] : m;
+      if (ep.mode == 0) {
+        // residual rows (bf16 or fp32) join the fp32 value before its one rounding, or before
+        // an fp32 store
+        if (ep.res) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += to_f32(pre[it][e]);
+        }
+        if (ep.res_f32) {
+          const float* r = ep.res_f32 + orow * ep.ldc + n;
+          const f32x4 r0 = *(const f32x4*)r, r1 = *(const f32x4*)(r + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] += r0[e];
+            v[4 + e] += r1[e];
+          }
+        }
+        if (ep.out_f32) {
+          float* dst = ep.out_f32 + orow * ep.ldc + n;
+          *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
+          *(f32x4*)(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+          continue;
+        }
+      }
       bf16x8 o;
       if (ep.mode == 2) {
         bf16x8 pa;
@@ -168,7 +193,7 @@ __device__ __forceinline__ void epilogue_f32(const f32x16 (&acc)[NtCfg<BM, BN>::
         for (int e = 0; e < 8; ++e) o[e] = to_bf16(v[e] * gelu_grad_f(to_f32(pre[it][e])));
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = to_bf16(v[e] + to_f32(pre[it][e]));
+        for (int e = 0; e < 8; ++e) o[e] = to_bf16(v[e]);
       }
       *(bf16x8*)(ep.out + orow * ep.ldc + n) = o;
     }
@@ -265,7 +290,7 @@ __global__ __launch_bounds__(256, BM == 128 ? 3 : 2) void k_gemm_nt(const bf16* 
     }
   }
 
-  if (ep.mode >= 2 || ep.res) {
+  if (ep.mode >= 2 || ep.res || ep.res_f32 || ep.out_f32) {
     epilogue_f32<BM, BN>(acc, smem, tid, lane, wm, wn, m0, n0, M, N, ep);
     return;
   }
@@ -702,10 +727,11 @@ hipError_t launch_dproj_bf16(const swin_attn_plan* p, const void* dy, const void
 }
 
 hipError_t launch_dgrad_qkv_bf16(const swin_attn_plan* p, const void* dqkv, const void* wqkvT, void* dx,
-                                 hipStream_t s) {
+                                 float* dx32, hipStream_t s) {
   EpiParams ep{};
   ep.mode = 0;
   ep.out = (bf16*)dx;  // dqkv is in grid order already
+  ep.out_f32 = dx32;   // if set, dx goes there in fp32 instead
   ep.ldc = p->C;
   ep.qscale = 1.f;
   ep.C = p->C;
@@ -713,12 +739,13 @@ hipError_t launch_dgrad_qkv_bf16(const swin_attn_plan* p, const void* dqkv, cons
                  s);
 }
 
-// Output projection whose epilogue also adds a residual (the block's h = x + proj(o)).
-hipError_t launch_proj_fwd_res_bf16(const swin_attn_plan* p, const void* o, const void* w, const void* b,
-                                    const void* res, void* y, hipStream_t s) {
+// The block's h = x + proj(o) in fp32: the projection's rows plus the bf16 residual x, stored
+// without rounding (the block keeps its residual stream in fp32).
+hipError_t launch_proj_fwd_res_f32(const swin_attn_plan* p, const void* o, const void* w, const void* b,
+                                   const void* res, float* h, hipStream_t s) {
   EpiParams ep{};
   ep.mode = 0;
-  ep.out = (bf16*)y;
+  ep.out_f32 = h;
   ep.res = (const bf16*)res;
   ep.ldc = p->C;
   ep.bias = (const bf16*)b;
@@ -732,13 +759,15 @@ hipError_t launch_proj_fwd_res_bf16(const swin_attn_plan* p, const void* o, cons
 // GELU'(aux)). All row-major with pitch N.
 hipError_t launch_rows_gemm_bf16(const bf16* A, int64_t lda, const bf16* B, int64_t ldb, int64_t M, int N, int K,
                                  const bf16* bias, int mode, bf16* out, bf16* out2, const bf16* aux, const bf16* res,
-                                 hipStream_t s) {
+                                 const float* res_f32, float* out_f32, hipStream_t s) {
   EpiParams ep{};
   ep.mode = mode;
   ep.out = out;
+  ep.out_f32 = out_f32;
   ep.out2 = out2;
   ep.aux = aux;
   ep.res = res;
+  ep.res_f32 = res_f32;
   ep.ldc = N;
   ep.bias = bias;
   ep.qscale = 1.f;

@@ -148,26 +148,32 @@ hipError_t launch_attn_fwd_bf16(const swin_attn_plan* p, const void* qkv, const 
                                 float* lse, hipStream_t s);
 hipError_t launch_proj_fwd_bf16(const swin_attn_plan* p, const void* o, const void* w, const void* b, void* y,
                                 hipStream_t s);
+// Module backward; with dx32 set, dx is written there in fp32 instead of to dx (the block's use).
 hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* x, const void* w_qkv,
                            const void* w_proj, const float* table, const void* saved, void* dx, float* dw_qkv,
                            float* db_qkv, float* dw_proj, float* db_proj, float* dtable, void* ws,
-                           hipStream_t s);
+                           hipStream_t s, float* dx32 = nullptr);
 
 // Swin block pieces
 typedef __bf16 bf16_t;
-hipError_t launch_proj_fwd_res_bf16(const swin_attn_plan* p, const void* o, const void* w, const void* b,
-                                    const void* res, void* y, hipStream_t s);
+hipError_t launch_proj_fwd_res_f32(const swin_attn_plan* p, const void* o, const void* w, const void* b,
+                                   const void* res, float* h, hipStream_t s);
 hipError_t launch_rows_gemm_bf16(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb, int64_t M, int N, int K,
                                  const bf16_t* bias, int mode, bf16_t* out, bf16_t* out2, const bf16_t* aux,
-                                 const bf16_t* res, hipStream_t s);
+                                 const bf16_t* res, const float* res_f32, float* out_f32, hipStream_t s);
 hipError_t launch_wgrad_bf16(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb, int64_t T, int M, int N,
                              int splits, int64_t chunk, float* part, float* dw, float* db, hipStream_t s);
 hipError_t launch_transpose_bf16(const void* in, void* out, int R, int Cn, hipStream_t s);
-hipError_t launch_layernorm_fwd(const bf16_t* x, const bf16_t* g, const bf16_t* b, bf16_t* y, float* mean, float* rstd,
+// Layer normalisation of bf16 or fp32 rows (the block's input x, or its fp32 residual stream h).
+template <typename TX>
+hipError_t launch_layernorm_fwd(const TX* x, const bf16_t* g, const bf16_t* b, bf16_t* y, float* mean, float* rstd,
                                 int64_t rows, int C, float eps, hipStream_t s);
-hipError_t launch_layernorm_bwd(const bf16_t* dy, const bf16_t* x, const float* mean, const float* rstd,
-                                const bf16_t* g, const bf16_t* dres, bf16_t* dx, float* part, float* dg, float* db,
-                                int64_t rows, int C, hipStream_t s);
+// Backward of the layer norm for an fp32 upstream gradient dy plus a residual gradient dres (bf16
+// or fp32) over bf16 or fp32 rows x; dx in bf16 and, if dx32 is set, also in fp32.
+template <typename TX, typename TR>
+hipError_t launch_layernorm_bwd(const float* dy, const TX* x, const float* mean, const float* rstd,
+                                const bf16_t* g, const TR* dres, bf16_t* dx, float* dx32, float* part, float* dg,
+                                float* db, int64_t rows, int C, hipStream_t s);
 int layernorm_groups(int64_t rows);
 // split-K count and chunk for a token contraction with an M x N output (plan helper)
 void wgrad_split(int64_t n_tok, int64_t M, int64_t N, int* splits, int64_t* chunk);

@@ -1,22 +1,21 @@
 """Parity of the Swin block (layer norms, attention module, GELU MLP, residuals) with the
 fp64 block oracle, through the C ABI of include/swin_block.h.
 
-Bars: per-token outputs (y, dx) |got - ref| <= 2e-2 + 2e-2 |ref| element-wise (the block
-rounds h, LN outputs, the MLP activation and y to bf16, so the error grows with the value);
-reduced gradients 2e-2 * max(1, |ref|_inf), as for the attention module."""
+Bars (tests/bars.py), as for the attention module: per-token outputs (y, dx) |got - ref| <=
+2e-2 + ulp_bf16(ref)/2 element-wise; reduced gradients 2e-2 * max(1, |ref|_inf). The block keeps
+its residual stream h (and its gradient) in fp32; tests/test_block_rounding.py shows on the CPU
+that this is what brings the block's bf16 storage within the per-token bar."""
 import numpy as np
 import pytest
 
+from tests.bars import reduced_excess, token_excess
 from tests.gpu_util import log, run_block_chain
 from tests.oracle_runner import block_chain_full
-from workloads import get_config, make_block_extras, make_inputs
+from workloads import BLOCK_BIAS_SCALE, get_config, make_block_extras, make_inputs
 from workloads.configs import small_variant
 
 pytestmark = pytest.mark.gpu
 
-ATOL = 2e-2
-RTOL = 2e-2
-TOL_RED = 2e-2
 GRAD_KEYS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_proj", "b_proj", "table", "ln2_g", "ln2_b", "w1", "b1", "w2",
              "b2")
 
@@ -30,22 +29,18 @@ def _gpu():
 
 
 def _check_tokens(got, ref, label):
-    got, ref = np.asarray(got), np.asarray(ref)
-    excess = np.abs(got - ref) - (ATOL + RTOL * np.abs(ref))
-    log("  %s max-abs %.3e (|ref| %.3e), worst excess over the bound %.3e" %
-        (label, np.abs(got - ref).max(), np.abs(ref).max(), excess.max()))
-    assert excess.max() <= 0, label
+    ex, err = token_excess(got, ref)
+    log("  %s max-abs %.3e (|ref| %.3e), worst excess over the bar %.3e" %
+        (label, err, float(np.abs(np.asarray(ref)).max()), ex))
+    assert ex <= 0, label
 
 
 def _check_grads(got, ref, label):
     for i, (gm, rm) in enumerate(zip(got, ref)):
         for k in GRAD_KEYS:
-            r = np.asarray(rm[k]).reshape(-1)
-            g = np.asarray(gm[k]).reshape(-1)
-            err = float(np.abs(g - r).max())
-            bound = TOL_RED * max(1.0, float(np.abs(r).max()))
-            log("  %s block %d d%s max-abs %.3e (bound %.3e)" % (label, i, k, err, bound))
-            assert err <= bound, (label, i, k, err, bound)
+            ex, err = reduced_excess(gm[k], rm[k])
+            log("  %s block %d d%s max-abs %.3e, worst excess over the bar %.3e" % (label, i, k, err, ex))
+            assert ex <= 0, (label, i, k, err, ex)
 
 
 BLOCK_CASES = [
@@ -76,7 +71,7 @@ def test_block_with_large_windows():
     cfg = SwinConfig(name="block_w16", batch=1, grid=(1, 32, 48), channels=128, heads=4, window=(1, 16, 16),
                      shifts=((0, 0, 0), (0, 8, 8)), dtype="bf16", backward=True, periodic=4, description="block_w16")
     log("block fwd+bwd with 256-token windows", cfg.grid)
-    inp = make_inputs(cfg)
+    inp = make_inputs(cfg, bias_scale=BLOCK_BIAS_SCALE)
     extras = make_block_extras(cfg)
     got = run_block_chain(cfg, inp, extras)
     ref = block_chain_full(cfg, inp, extras)
@@ -89,7 +84,7 @@ def test_block_with_large_windows():
 def test_block_chain_vs_oracle(name, kw, hidden):
     cfg = small_variant(get_config(name), **kw)
     log("block fwd+bwd", name, cfg.grid, "batch", cfg.batch, "C", cfg.channels, "hidden", hidden or 4 * cfg.channels)
-    inp = make_inputs(cfg)
+    inp = make_inputs(cfg, bias_scale=BLOCK_BIAS_SCALE)
     extras = make_block_extras(cfg, hidden=hidden)
     got = run_block_chain(cfg, inp, extras)
     ref = block_chain_full(cfg, inp, extras)
@@ -101,7 +96,7 @@ def test_block_chain_vs_oracle(name, kw, hidden):
 def test_block_backward_is_deterministic():
     import torch
     cfg = small_variant(get_config("ragged"), grid=(1, 41, 57))
-    inp = make_inputs(cfg)
+    inp = make_inputs(cfg, bias_scale=BLOCK_BIAS_SCALE)
     extras = make_block_extras(cfg)
     got = run_block_chain(cfg, inp, extras)
     b = got["blocks"][0]
@@ -121,7 +116,7 @@ def test_block_rejects_bad_calls():
     import torch
     from shifted_window_attention_amd import native as N
     cfg = small_variant(get_config("om4"), grid=(1, 12, 24), batch=1, channels=64, heads=2)
-    inp = make_inputs(cfg)
+    inp = make_inputs(cfg, bias_scale=BLOCK_BIAS_SCALE)
     extras = make_block_extras(cfg)
     got = run_block_chain(cfg, inp, extras, with_bwd=False)
     b = got["blocks"][0]
@@ -152,7 +147,7 @@ def test_block_inference_call_matches_training_forward():
     import torch
     from shifted_window_attention_amd import native as N
     cfg = small_variant(get_config("highres"), grid=(1, 24, 36))
-    inp = make_inputs(cfg)
+    inp = make_inputs(cfg, bias_scale=BLOCK_BIAS_SCALE)
     extras = make_block_extras(cfg)
     got = run_block_chain(cfg, inp, extras, with_bwd=False)
     b = got["blocks"][0]

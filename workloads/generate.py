@@ -126,8 +126,13 @@ class BlockExtras:
     dev: dict = None
 
 
+# Scale of every bias inside a Swin block (b1, b2 here, and the attention module's b_qkv, b_proj,
+# which the block tests draw with make_inputs(cfg, bias_scale=BLOCK_BIAS_SCALE)).
+BLOCK_BIAS_SCALE = 0.1
+
+
 def make_block_extras(cfg: SwinConfig, hidden: Optional[int] = None, seed: int = 0,
-                      bias_scale: float = 0.1, norm_scale: float = 0.1) -> List[BlockExtras]:
+                      bias_scale: float = BLOCK_BIAS_SCALE, norm_scale: float = 0.1) -> List[BlockExtras]:
     """Per chained block, drawn from numpy default_rng([seed, 1]) (a stream separate from
     make_inputs, whose draws stay unchanged) in float64, in the order ln1 scale, ln1 shift,
     ln2 scale, ln2 shift, W1, b1, W2, b2. Scales are 1 + norm_scale N(0,1) and shifts
