@@ -92,14 +92,6 @@ __global__ __launch_bounds__(256) void k_layernorm_fwd(const TX* __restrict__ x,
 // and, per workgroup (a contiguous range of `per` rows), partial sums of dg = sum dy xhat
 // and db = sum dy (part[group][0][:] and part[group][1][:]), combined over the 4 waves in a
 // fixed order. At most kLnMaxGroups workgroups, so that the final reduction stays short.
-constexpr int kLnMaxGroups = 1024;
-
-static int64_t ln_rows_per_group(int64_t rows) {
-  int64_t per = (rows + kLnMaxGroups - 1) / kLnMaxGroups;
-  per = per < 64 ? 64 : per;
-  return (per + 3) / 4 * 4;
-}
-
 template <int CH, typename TX, typename TR>
 __global__ __launch_bounds__(256) void k_layernorm_bwd(const float* __restrict__ dy, const TX* __restrict__ x,
                                                        const float* __restrict__ mean, const float* __restrict__ rstd,
@@ -232,11 +224,6 @@ template hipError_t launch_layernorm_fwd<bf16>(const bf16*, const bf16*, const b
                                                int, float, hipStream_t);
 template hipError_t launch_layernorm_fwd<float>(const float*, const bf16*, const bf16*, bf16*, float*, float*, int64_t,
                                                 int, float, hipStream_t);
-
-int layernorm_groups(int64_t rows) {
-  const int64_t per = ln_rows_per_group(rows);
-  return (int)((rows + per - 1) / per);
-}
 
 template <typename TX, typename TR>
 hipError_t launch_layernorm_bwd(const float* dy, const TX* x, const float* mean, const float* rstd, const bf16* g,

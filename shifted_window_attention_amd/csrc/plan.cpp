@@ -522,4 +522,27 @@ swin_status swin_attn_bwd(const swin_attn_plan* plan, const void* dy, const void
                     "bf16 backward");
 }
 
+swin_status swin_attn_bwd_noalloc(const swin_attn_plan* plan, const void* dy, const void* x, const void* w_qkv,
+                                  const void* w_proj, const float* bias_table, const void* saved, void* dx,
+                                  float* dw_qkv, float* db_qkv, float* dw_proj, float* db_proj, float* dbias_table,
+                                  void* stream) {
+  const swin_status st = bwd_arg_checks(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, dw_proj,
+                                        dbias_table);
+  if (st != SWIN_OK) return st;
+  if (plan->bwd_total > SWIN_NOALLOC_SCRATCH_BYTES)
+    return fail(SWIN_ERR_WORKSPACE, "backward workspace of " + std::to_string(plan->bwd_total) +
+                                        " bytes exceeds the " + std::to_string(SWIN_NOALLOC_SCRATCH_BYTES) +
+                                        "-byte scratch of swin_attn_bwd_noalloc; use swin_attn_bwd");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev != plan->device) return fail(SWIN_ERR_ARG, "the current device is not the plan's device");
+  void* ws = nullptr;
+  e = noalloc_scratch(dev, &ws);
+  if (e == hipSuccess)
+    e = launch_bwd_bf16(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_qkv, dw_proj, db_proj,
+                        dbias_table, ws, (hipStream_t)stream);
+  return hip_status(e, "bf16 backward (no allocation)");
+}
+
 }  // extern "C"

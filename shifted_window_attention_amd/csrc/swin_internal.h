@@ -133,6 +133,10 @@ swin_status bwd_arg_checks(const swin_attn_plan* plan, const void* dy, const voi
                            const void* w_proj, const float* bias_table, const void* saved, const void* dx,
                            const float* dw_qkv, const float* dw_proj, const float* dbias_table);
 
+// Device address of the no-allocation scratch array on device dev (the current device), looked
+// up on the first call per device and kept; hipErrorInvalidDevice beyond the per-device table.
+hipError_t noalloc_scratch(int dev, void** out);
+
 // Records the next installed trace event (if any) on stream s; see swin_attn_trace_events.
 hipError_t trace_mark(hipStream_t s);
 
@@ -174,7 +178,18 @@ template <typename TX, typename TR>
 hipError_t launch_layernorm_bwd(const float* dy, const TX* x, const float* mean, const float* rstd,
                                 const bf16_t* g, const TR* dres, bf16_t* dx, float* dx32, float* part, float* dg,
                                 float* db, int64_t rows, int C, hipStream_t s);
-int layernorm_groups(int64_t rows);
+// Layer-norm backward partial sums: at most kLnMaxGroups workgroups, each over a contiguous range
+// of rows (a multiple of 4, at least 64), so that the final fixed-order reduction stays short.
+constexpr int kLnMaxGroups = 1024;
+inline int64_t ln_rows_per_group(int64_t rows) {
+  int64_t per = (rows + kLnMaxGroups - 1) / kLnMaxGroups;
+  per = per < 64 ? 64 : per;
+  return (per + 3) / 4 * 4;
+}
+inline int layernorm_groups(int64_t rows) {
+  const int64_t per = ln_rows_per_group(rows);
+  return (int)((rows + per - 1) / per);
+}
 // split-K count and chunk for a token contraction with an M x N output (plan helper)
 void wgrad_split(int64_t n_tok, int64_t M, int64_t N, int* splits, int64_t* chunk);
 

@@ -19,7 +19,9 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libswinattn.so")
+# SWIN_ATTN_LIB names another build of the same library (the host-only sanitizer build of the
+# host tests); unset, the in-tree libswinattn.so is loaded.
+LIB_PATH = os.environ.get("SWIN_ATTN_LIB") or os.path.join(_PKG, "libswinattn.so")
 
 SWIN_OK = 0
 SWIN_F32 = 0
@@ -93,7 +95,7 @@ def _load():
     # runtime, and torch's copy, loaded later, then finds no device.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libswinattn.so is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+        raise ImportError(LIB_PATH + " is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
                           "or `python shifted_window_attention_amd/build_lib.py`")
     L = ctypes.CDLL(LIB_PATH)
     vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
