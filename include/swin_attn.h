@@ -173,6 +173,20 @@ swin_status swin_attn_index_map(const swin_attn_plan* plan, int64_t* host_map, u
 swin_status swin_attn_sizes(const swin_attn_plan* plan, size_t* fwd_ws, size_t* bwd_ws, size_t* saved_bytes);
 
 /*
+ * Sticky condition flags of a plan: bits that calls on this plan raise on the
+ * device and that stay set until cleared, like a floating-point exception flag.
+ *   SWIN_FLAG_DT_SATURATED  a backward call's relative-position-bias gradient
+ *                           did not fit its fixed-point accumulator (see
+ *                           swin_attn_bwd); that call's dbias_table holds NaN.
+ * Waits for all work on the plan's device (hipDeviceSynchronize), then writes
+ * the flags to *flags (host memory) and, if clear is non-zero, resets them to 0.
+ * Not meant for a hot loop; the calls that raise a flag never wait.
+ * Errors: SWIN_ERR_ARG for NULL arguments, SWIN_ERR_HIP if the device fails.
+ */
+#define SWIN_FLAG_DT_SATURATED 0x1u
+swin_status swin_attn_plan_flags(const swin_attn_plan* plan, uint32_t* flags, int clear);
+
+/*
  * Forward. Attention reading (the pages name W-MSA/SW-MSA [TERRA IV-A] and
  * give its structure [BEAST "Domain-Tensor Parallelism"] but never its
  * formula): inside each window, for head h,
@@ -211,8 +225,12 @@ swin_status swin_attn_fwd(const swin_attn_plan* plan, const void* x, const void*
  * dT[h, bin] sums dS over every window and allowed pair (the inverse routes
  * carry gradients back to their sources [TERRA IV-D]); all reductions run in
  * a fixed order (on the tiled kernels every dS term of dT is rounded to an
- * integer multiple of 2^-20, saturating at magnitude 2^11, and the integers are
- * summed exactly, in any order), so repeated calls are bitwise identical.
+ * integer multiple of 2^-20 and the integers are summed exactly, in any order),
+ * so repeated calls are bitwise identical. On the tiled kernels a dS term of
+ * magnitude 2^11 or more (or NaN) does not fit that fixed point: the call then
+ * writes NaN over the whole dbias_table and raises SWIN_FLAG_DT_SATURATED in
+ * the plan's sticky flags (swin_attn_plan_flags); no status is returned at once,
+ * since the call does not wait for its kernels.
  * Tables of more than 8192 bins per head (windows of thousands of tokens) are
  * accumulated with global 64-bit integer atomics instead of workgroup LDS bins:
  * slower, equally exact. Only SWIN_BF16 is supported (SWIN_ERR_UNSUPPORTED for

@@ -85,6 +85,11 @@ void swin_block_plan_destroy(swin_block_plan* plan);
  * LN1(x), h, LN2(h), the MLP pre-activation and activation, and the layer-norm statistics). */
 swin_status swin_block_sizes(const swin_block_plan* plan, size_t* fwd_ws, size_t* bwd_ws, size_t* saved_bytes);
 
+/* The sticky flags of the block's attention module (swin_attn_plan_flags: waits for the device,
+ * writes *flags, clears them if clear is non-zero). SWIN_FLAG_DT_SATURATED after a block backward
+ * means its bias_table gradient did not fit the fixed-point accumulator and holds NaN. */
+swin_status swin_block_plan_flags(const swin_block_plan* plan, uint32_t* flags, int clear);
+
 /* y = block(x). saved receives saved_bytes of state for swin_block_bwd; for an inference call
  * pass saved = NULL and a workspace of at least saved_bytes. y must not alias x.
  * Errors: SWIN_ERR_ARG (NULL plan, params or required pointer; aliasing), SWIN_ERR_WORKSPACE,

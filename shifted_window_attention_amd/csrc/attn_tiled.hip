@@ -361,9 +361,13 @@ __global__ __launch_bounds__(256, (FAST || HD < 128) ? 2 : 1) void k_tiled_fwd_p
 // backward
 // ---------------------------------------------------------------------------------------
 // dT is summed in fixed point: every dS term is rounded to a 32-bit integer in units of 2^-20
-// (terms of magnitude 2^11 and beyond saturate) and added into 64-bit integer bins, so the
-// sums are exact and do not depend on the order of the additions.
-constexpr float kFix = 1048576.f;  // 2^20
+// and added into 64-bit integer bins, so the sums are exact and do not depend on the order of
+// the additions. A term of magnitude 2^11 or more (or not a number) does not fit: it is clamped
+// to +-kFixLim before the conversion, and the call's saturation word (the u64 after the
+// accumulator) is set; the conversion to fp32 then writes NaN over the whole table and raises
+// SWIN_FLAG_DT_SATURATED in the plan's sticky flags.
+constexpr float kFix = 1048576.f;         // 2^20
+constexpr float kFixLim = 2147483520.f;   // the largest float below 2^31
 
 template <int HD>
 struct TiledQBuf {
@@ -611,6 +615,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
     dkacc[d] = f32x4{};
     dvacc[d] = f32x4{};
   }
+  float sat = 0.f;  // the lane's largest clamped |dS| 2^20 (kFixLim once a term saturated)
 
   for (int qb = 0; qb < nqb; ++qb) {
     vm_wait(0);
@@ -679,7 +684,9 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
     for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int v = (int)rintf(ds[qt][i] * kFix);
+        const float t = fminf(fmaxf(ds[qt][i] * kFix, -kFixLim), kFixLim);  // NaN -> -kFixLim
+        sat = fmaxf(sat, fabsf(t));
+        const int v = (int)rintf(t);
         if constexpr (FAST) {
           // the clamped offset is even (both encodings are even and the odd padding query code
           // always clamps to 2 nbins), so bin * 8 = offset * 4; masked pairs: bin nbins, v = 0
@@ -739,6 +746,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
       *(bf16x4*)(row + 2 * a.C + 32 * sc + 16 + 4 * g) = v1;
     }
   }
+  if (sat >= kFixLim) a.dbias_acc[(int64_t)a.nh * a.nbins] = 1ull;  // saturation word (same value from any lane)
   if (global_bins) return;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the bin additions above are inline assembly
   __syncthreads();
@@ -753,9 +761,14 @@ __global__ __launch_bounds__(256) void k_fixed_zero(unsigned long long* p, int64
   if (i < n) p[i] = 0ull;
 }
 
-__global__ __launch_bounds__(256) void k_fixed_to_f32(const unsigned long long* p, float* out, int64_t n) {
+// p[n] is the call's saturation word: when set, every entry becomes NaN and the plan's sticky
+// flags get SWIN_FLAG_DT_SATURATED.
+__global__ __launch_bounds__(256) void k_fixed_to_f32(const unsigned long long* p, float* out, int64_t n,
+                                                      unsigned int* flags) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) out[i] = (float)((double)(long long)p[i] * (1.0 / kFix));
+  const bool saturated = p[n] != 0ull;
+  if (i < n) out[i] = saturated ? __builtin_nanf("") : (float)((double)(long long)p[i] * (1.0 / kFix));
+  if (saturated && i == 0) atomicOr(flags, SWIN_FLAG_DT_SATURATED);
 }
 
 static TiledArgs tiled_args(const swin_attn_plan* p) {
@@ -822,7 +835,7 @@ hipError_t launch_tiled_bwd_bf16(const swin_attn_plan* p, const void* qkv, const
   a.dqkv = (bf16*)dqkv;
   a.dbias_acc = acc;
   const int64_t nacc = (int64_t)p->nh * p->nbins;
-  k_fixed_zero<<<(unsigned)((nacc + 255) / 256), 256, 0, s>>>(acc, nacc);
+  k_fixed_zero<<<(unsigned)((nacc + 1 + 255) / 256), 256, 0, s>>>(acc, nacc + 1);  // and the saturation word
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned items = (unsigned)p->tiled_work.size(), kv_items = (unsigned)p->tiled_kv_work.size();
@@ -833,7 +846,7 @@ hipError_t launch_tiled_bwd_bf16(const swin_attn_plan* p, const void* qkv, const
   else
     e = tiled_bwd_launch<128>(a, items, kv_items, p->nh, s);
   if (e != hipSuccess) return e;
-  k_fixed_to_f32<<<(unsigned)((nacc + 255) / 256), 256, 0, s>>>(acc, dtable, nacc);
+  k_fixed_to_f32<<<(unsigned)((nacc + 255) / 256), 256, 0, s>>>(acc, dtable, nacc, p->dev.flags);
   return hipGetLastError();
 }
 

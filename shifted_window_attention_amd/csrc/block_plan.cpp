@@ -99,6 +99,11 @@ void swin_block_plan_destroy(swin_block_plan* plan) {
   delete plan;
 }
 
+swin_status swin_block_plan_flags(const swin_block_plan* plan, uint32_t* flags, int clear) {
+  if (!plan) return fail(SWIN_ERR_ARG, "plan is NULL");
+  return swin_attn_plan_flags(plan->attn, flags, clear);
+}
+
 swin_status swin_block_sizes(const swin_block_plan* plan, size_t* fwd_ws, size_t* bwd_ws, size_t* saved_bytes) {
   if (!plan) return fail(SWIN_ERR_ARG, "plan is NULL");
   if (fwd_ws) *fwd_ws = 0;

@@ -222,6 +222,7 @@ static void free_dev(swin_attn_plan* p) {
     hipFree(p->dev.tiled_work);
     hipFree(p->dev.tiled_kv_work);
     hipFree(p->dev.tiled_codes);
+    hipFree(p->dev.flags);
     if (cur >= 0) (void)hipSetDevice(cur);
   }
   p->dev = DevTables{};
@@ -416,7 +417,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
     const size_t part_proj = (size_t)p->wgrad_splits_proj * (C * C + C);
     p->bwd_part = align256(std::max(part_qkv, part_proj) * 4);
     // dT: per-work-item partials (one-tile path) or one fixed-point accumulator (tiled path)
-    p->bwd_dbias_part = p->tiled_bwd ? align256((size_t)p->nh * (size_t)p->nbins * 8)
+    p->bwd_dbias_part = p->tiled_bwd ? align256((size_t)p->nh * (size_t)p->nbins * 8 + 8)  // + saturation word
                                  : align256(p->bwd_work.size() * (size_t)p->nh * (size_t)p->nbins * 4);
     p->bwd_dd = align256(nt * (size_t)p->nh * 4);
     p->bwd_total = p->bwd_do + p->bwd_dqkv + p->bwd_wt + p->bwd_part + p->bwd_dbias_part + p->bwd_dd;
@@ -432,6 +433,7 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
   if (e == hipSuccess && !p->tiled_work.empty()) e = upload(&p->dev.tiled_work, p->tiled_work);
   if (e == hipSuccess && !p->tiled_kv_work.empty()) e = upload(&p->dev.tiled_kv_work, p->tiled_kv_work);
   if (e == hipSuccess && !p->tiled_codes.empty()) e = upload(&p->dev.tiled_codes, p->tiled_codes);
+  if (e == hipSuccess) e = upload(&p->dev.flags, std::vector<unsigned int>{0u});
   if (e != hipSuccess) {
     set_error(std::string("plan upload failed: ") + hipGetErrorString(e));
     free_dev(p);
@@ -451,6 +453,26 @@ void swin_attn_plan_destroy(swin_attn_plan* plan) {
 swin_status swin_attn_plan_stats(const swin_attn_plan* plan, swin_attn_stats* out) {
   if (!plan || !out) return fail(SWIN_ERR_ARG, "plan or output is NULL");
   *out = plan->stats;
+  return SWIN_OK;
+}
+
+swin_status swin_attn_plan_flags(const swin_attn_plan* plan, uint32_t* flags, int clear) {
+  if (!plan || !flags) return fail(SWIN_ERR_ARG, "plan or flags is NULL");
+  if (!plan->dev.flags) return fail(SWIN_ERR_ARG, "plan has no device state (host-only plan)");
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e == hipSuccess) e = hipSetDevice(plan->device);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  unsigned int v = 0u;
+  if (e == hipSuccess) e = hipMemcpy(&v, plan->dev.flags, sizeof(v), hipMemcpyDeviceToHost);
+  const unsigned int zero = 0u;
+  if (e == hipSuccess && clear) e = hipMemcpy(plan->dev.flags, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (cur >= 0) (void)hipSetDevice(cur);
+  if (e != hipSuccess) {
+    set_error(std::string("reading the plan flags: ") + hipGetErrorString(e));
+    return SWIN_ERR_HIP;
+  }
+  *flags = v;
   return SWIN_OK;
 }
 

@@ -95,6 +95,7 @@ struct DevTables {
   WorkItem* tiled_work = nullptr;  // [n_tiled_work] (class, window, 64-token block): the tiled dQ kernel
   WorkItem* tiled_kv_work = nullptr;  // (class, window, 128-token block): the tiled forward and dK/dV kernels
   int32_t* tiled_codes = nullptr;     // per class: key codes, then query codes (tiled path)
+  unsigned int* flags = nullptr;      // sticky SWIN_FLAG_* bits (swin_attn_plan_flags)
 };
 
 }  // namespace swin

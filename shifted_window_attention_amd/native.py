@@ -29,6 +29,7 @@ SWIN_BF16 = 1
 SWIN_PERIODIC_LEVEL = 0x1
 SWIN_PERIODIC_LAT = 0x2
 SWIN_PERIODIC_LON = 0x4
+SWIN_FLAG_DT_SATURATED = 0x1
 
 
 class SwinError(RuntimeError):
@@ -108,6 +109,7 @@ def _load():
         "swin_attn_plan_stats": (st, [vp, P(SwinAttnStats)]),
         "swin_attn_index_map": (st, [vp, P(ctypes.c_int64), P(ctypes.c_uint8)]),
         "swin_attn_sizes": (st, [vp, P(sz), P(sz), P(sz)]),
+        "swin_attn_plan_flags": (st, [vp, P(ctypes.c_uint32), st]),
         "swin_attn_fwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "swin_attn_bwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "swin_attn_bwd_noalloc": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
@@ -118,6 +120,7 @@ def _load():
         "swin_block_plan_create": (st, [P(SwinBlockDesc), P(vp)]),
         "swin_block_plan_destroy": (None, [vp]),
         "swin_block_sizes": (st, [vp, P(sz), P(sz), P(sz)]),
+        "swin_block_plan_flags": (st, [vp, P(ctypes.c_uint32), st]),
         "swin_block_fwd": (st, [vp, vp, P(SwinBlockParams), vp, vp, vp, sz, vp]),
         "swin_block_bwd": (st, [vp, vp, vp, P(SwinBlockParams), vp, vp, P(SwinBlockGrads), vp, sz, vp]),
         "swin_offload_create": (st, [ctypes.c_int32, P(vp)]),
@@ -282,6 +285,13 @@ def swin_attn_sizes(plan):
     a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     _check(lib.swin_attn_sizes(plan, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "swin_attn_sizes")
     return a.value, b.value, c.value
+
+
+def swin_attn_plan_flags(plan, clear=False):
+    """Sticky SWIN_FLAG_* bits of the plan (waits for the device); clear=True resets them."""
+    f = ctypes.c_uint32()
+    _check(lib.swin_attn_plan_flags(plan, ctypes.byref(f), 1 if clear else 0), "swin_attn_plan_flags")
+    return f.value
 
 
 def _ptr(t):
@@ -456,6 +466,13 @@ def swin_block_sizes(plan):
     a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     _check(lib.swin_block_sizes(plan, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "swin_block_sizes")
     return a.value, b.value, c.value
+
+
+def swin_block_plan_flags(plan, clear=False):
+    """Sticky SWIN_FLAG_* bits of the block's attention module (waits for the device)."""
+    f = ctypes.c_uint32()
+    _check(lib.swin_block_plan_flags(plan, ctypes.byref(f), 1 if clear else 0), "swin_block_plan_flags")
+    return f.value
 
 
 def swin_block_fwd(plan, x, params, y, saved, ws=None, stream=None):

@@ -89,6 +89,9 @@ def test_tiled_backward_vs_oracle(c):
     log("  y max-abs %.3e  dx max-abs %.3e (worst excess over the bar %.3e, %.3e)" % (ey, edx, exy, exd))
     assert exy <= 0.0 and exd <= 0.0
     _check_grads(got["grads"], ref["grads"], c.name)
+    from shifted_window_attention_amd import native as N
+    for m in got["mods"]:
+        assert N.swin_attn_plan_flags(m.plan.handle) == 0   # no dT term left the fixed-point range
 
 
 def test_tiled_backward_is_deterministic():
@@ -116,3 +119,38 @@ def test_tiled_forward_vs_oracle(c):
     ex, err = token_excess(got["y"], ref["y"])
     log("  y max-abs %.3e (worst excess over the bar %.3e)" % (err, ex))
     assert ex <= 0.0
+
+
+def test_tiled_dT_saturation_is_flagged():
+    """A dS term of magnitude 2^11 or more does not fit the fixed-point dT accumulator: the call
+    writes NaN over dbias_table and raises SWIN_FLAG_DT_SATURATED in the plan's sticky flags,
+    which swin_attn_plan_flags reads and clears; the other gradients are still computed, and a
+    later call in range gives the in-range result again, bit for bit."""
+    import torch
+    from shifted_window_attention_amd import native as N
+    c = BWD_CASES[-3]          # w16x16: 256-token windows, tiled backward, table in LDS
+    inp = make_inputs(c)
+    got = run_chain(c, inp)
+    m = got["mods"][-1]
+    x = got["xs"][-2]
+    dy = torch.randn(x.shape, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).cuda()
+    assert N.swin_attn_plan_flags(m.plan.handle, clear=True) == 0
+    dx1, g1 = m.bwd(dy, x)
+    assert N.swin_attn_plan_flags(m.plan.handle) == 0
+    assert bool(torch.isfinite(g1["table"]).all())
+    log("  in range: max |dT| %.3e" % float(g1["table"].abs().max()))
+    big = dy * (2.0 ** 20)     # dS ~ P (dP - D) grows with dy: far beyond 2^11
+    dx2, g2 = m.bwd(big, x)
+    flags = N.swin_attn_plan_flags(m.plan.handle)
+    log("  saturating call: flags %#x" % flags)
+    assert flags & N.SWIN_FLAG_DT_SATURATED
+    assert bool(torch.isnan(g2["table"]).all())
+    for k in ("w_qkv", "b_qkv", "w_proj", "b_proj"):
+        assert bool(torch.isfinite(g2[k]).all()), k
+    assert bool(torch.isfinite(dx2.float()).all())
+    # the flag is sticky until cleared
+    dx3, g3 = m.bwd(dy, x)
+    assert N.swin_attn_plan_flags(m.plan.handle, clear=True) & N.SWIN_FLAG_DT_SATURATED
+    assert N.swin_attn_plan_flags(m.plan.handle) == 0
+    assert torch.equal(g3["table"], g1["table"])
+    assert torch.equal(dx3.view(torch.int16), dx1.view(torch.int16))
