@@ -23,6 +23,8 @@
 // read from the row-major V tile with gfx950's transposing LDS read. A window has at most
 // 256 tokens, so a query's whole key row lives in registers and the softmax is exact in a
 // single pass (no online rescaling).
+#include <type_traits>
+
 #include "device_common.h"
 #include "swin_internal.h"
 
@@ -56,9 +58,10 @@ struct FwdBuf {
 template <int NKT>
 struct FwdSmem {
   static constexpr int B = sizeof(FwdBuf<NKT>), T = 4 * (kMaxBins + kMaxChunk + 16 * NKT);
-  // two workgroups per CU when the register budget allows it (up to 10 query tiles), with as
-  // many buffers as then fit; otherwise three buffers if one workgroup fits them
-  static constexpr int MIN_BLOCKS = NKT <= 10 ? 2 : 1;
+  // two workgroups per CU when the register budget allows it (up to 8 query tiles, with the
+  // bias in fp32), with as many buffers as then fit; otherwise three buffers if one workgroup
+  // fits them
+  static constexpr int MIN_BLOCKS = NKT <= 8 ? 2 : 1;
   static constexpr int LDS_CAP = 160 * 1024 / MIN_BLOCKS;
   static constexpr int NBUF = 3 * B + T <= LDS_CAP ? 3 : (2 * B + T <= LDS_CAP ? 2 : (3 * B + T <= 160 * 1024 ? 3 : 2));
   FwdBuf<NKT> buf[NBUF];
@@ -125,9 +128,13 @@ __global__ __launch_bounds__(64 * NKT, FwdSmem<NKT>::MIN_BLOCKS) void k_attn_fwd
   for (int w = 0; w < NBUF - 1 && w < wk.count; ++w) stage(w);
 
   // bias + mask of this lane's query against every key; keys past n are masked, and
-  // queries past n (whose outputs are dropped) get finite zeros. Held as fp16 (|error| <=
-  // 2^-11 |bias|, -inf exact) to leave registers for a second workgroup per CU.
-  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  // queries past n (whose outputs are dropped) get finite zeros. The values are rounded to
+  // fp16 (|error| <= 2^-11 |bias|, -inf exact) as in the backward, which recomputes P from the
+  // saved LSE with the same rounded logits. Held in fp32 up to 10 query tiles (an fp16 copy
+  // would cost a conversion per pair and window); beyond that as fp16, which leaves registers
+  // for the logits.
+  typedef typename std::conditional<NKT <= 10, float, _Float16>::type bias_t;
+  typedef bias_t h4 __attribute__((ext_vector_type(4)));
   const int code0 = code0_of(a.win);
   const int cq = sm.codes[q];
   h4 bias[NKT];
@@ -138,7 +145,7 @@ __global__ __launch_bounds__(64 * NKT, FwdSmem<NKT>::MIN_BLOCKS) void k_attn_fwd
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = 16 * kt + 4 * g + i;
-      bias[kt][i] = (_Float16)(!qv ? 0.f : (k >= n ? -INFINITY : pair_bias_codes(cq, kk[i], code0, sm.tab)));
+      bias[kt][i] = (bias_t)(_Float16)(!qv ? 0.f : (k >= n ? -INFINITY : pair_bias_codes(cq, kk[i], code0, sm.tab)));
     }
   }
 
@@ -160,12 +167,12 @@ __global__ __launch_bounds__(64 * NKT, FwdSmem<NKT>::MIN_BLOCKS) void k_attn_fwd
     const FwdBuf<NKT>& cur = sm.buf[w % NBUF];
     // Issue order: the first NBUF-1 windows' copies, then per window w: the stores of window
     // w-1, then the copies of window w+NBUF-1. Operations complete in issue order, so the
-    // copies of window w are done once at most the copies issued after them (those of
-    // windows w+1 .. w+NBUF-2) are outstanding.
-    if (NBUF == 3 && w + 1 < wk.count)
-      vm_wait(COPIES);
-    else
-      vm_wait(0);
+    // copies of window w are done once at most the copies of windows w+1 .. w+NBUF-2 are
+    // outstanding (stores issued in between only make that wait stricter).
+    {
+      const int later = wk.count - 1 - w < NBUF - 2 ? wk.count - 1 - w : NBUF - 2;  // windows staged after w
+      vm_wait(COPIES * later);
+    }
     // every wave's copies into `cur` have landed, and every wave is done with window w-1
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (prev_off >= 0 && qv) {

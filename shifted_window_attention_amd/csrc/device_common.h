@@ -35,10 +35,17 @@ __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Maximum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane rows at one position),
+// with gfx950's row-swapping permutes instead of LDS round trips. Each swap of v with itself
+// leaves, in its two results, a lane's own value and its partner's (across the 32-lane halves,
+// then across adjacent rows), so the maximum of the two results is the pairwise maximum.
 __device__ __forceinline__ float wave_max_xor16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const auto h = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                  false, false);
+  v = fmaxf(__builtin_bit_cast(float, (unsigned)h[0]), __builtin_bit_cast(float, (unsigned)h[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 __device__ __forceinline__ float wave_sum_xor16_32(float v) {
   v += __shfl_xor(v, 16);
