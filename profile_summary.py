@@ -2,6 +2,10 @@
 
   python profile_summary.py trace DIR OUT.md --cmd "<rocprofv3 command>"
       per-kernel table from the --kernel-trace --stats CSV (kernel_stats.csv) under DIR
+  python profile_summary.py counters DIR [DIR ...] --cmd "<rocprofv3 command, {counters} for the list>"
+      per-stage SQ counters from --pmc runs (each DIR one pass of at most 8 SQ counters plus
+      GRBM_GUI_ACTIVE), with the derived MFMA, VALU, LDS and wait figures, written to
+      profiles/counters_540x1080_c512.md
   python profile_summary.py traffic FETCH_DIR WRITE_DIR --cmd-fetch "..." --cmd-write "..."
       HBM bytes per dispatch from two --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per
       dispatch), each scaled by what the same counter reads for the window gather, a copy of
@@ -230,6 +234,100 @@ def cmd_traffic(a):
     print("\n".join(lines))
 
 
+# FLOP per MFMA instruction: the GEMMs run v_mfma_f32_32x32x16_bf16, the attention kernels
+# v_mfma_f32_16x16x32_bf16
+MFMA_FLOP = {"k_gemm_nt": 2 * 32 * 32 * 16, "k_gemm_tn": 2 * 32 * 32 * 16, "k_attn_fwd": 2 * 16 * 16 * 32,
+             "k_attn_bwd": 2 * 16 * 16 * 32}
+N_CU, N_SIMD, N_XCD = 256, 1024, 8
+
+
+def per_dispatch_rows(path):
+    """{counter: {(kernel, role): [(value, ns)]}} for the attention chain, as per_dispatch."""
+    rows = list(csv.DictReader(open(path)))
+    out = {}
+    for c in sorted({r["Counter_Name"] for r in rows}):
+        vals = per_dispatch(path, c)
+        durs = per_dispatch_durations(path, c)
+        out[c] = {k: list(zip(v, durs[k])) for k, v in vals.items()}
+    return out
+
+
+def per_dispatch_durations(path, counter):
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    # same selection and labelling as per_dispatch, with the dispatch duration as the value
+    tmp = path + ".dur.csv"
+    with open(tmp, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=list(rows[0].keys()))
+        w.writeheader()
+        for r in rows:
+            r = dict(r)
+            r["Counter_Value"] = str(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            w.writerow(r)
+    try:
+        return per_dispatch(tmp, counter)
+    finally:
+        os.remove(tmp)
+
+
+def cmd_counters(a):
+    from bench import stage_flops_bytes
+    from shifted_window_attention_amd import native as N
+    from workloads import get_config
+    cfg = get_config("highres")
+    pairs = [N.swin_attn_host_stats(N.make_desc(cfg.batch, cfg.grid, cfg.channels, cfg.heads, cfg.window, sh,
+                                                cfg.periodic, N.SWIN_BF16))["allowed_pairs"] for sh in cfg.shifts]
+    alg = [stage_flops_bytes(cfg, p)[0] for p in pairs]
+    data = defaultdict(dict)   # (kernel, role) -> counter -> mean value
+    dur = defaultdict(list)
+    for d in a.dirs:
+        for c, per in per_dispatch_rows(find(d, "counter_collection.csv")).items():
+            for k, v in per.items():
+                if k[1] == "copy":
+                    continue
+                data[k][c] = sum(x for x, _ in v) / len(v)
+                dur[k] += [ns for _, ns in v]
+    mean = lambda v: sum(v) / len(v)
+    lines = ["# SQ counters per dispatch: 540x1080 tokens, C=512, 16 heads, 12x12 windows (W-MSA -> SW-MSA fwd+bwd)",
+             "", "Counter runs (from the repository root on the GPU host), one per counter set:", ""]
+    lines += ["    " + c for c in a.cmd]
+    lines += ["", "Every value is the mean over the chain's dispatches of that stage (both modules, warmup and",
+              "timed steps), summed over the chip by rocprofv3. Derived figures (cycles = GRBM_GUI_ACTIVE / %d," % N_XCD,
+              "the busy cycles of one XCD's command processor over the dispatch):",
+              "- MFMA GFLOP = SQ_INSTS_MFMA x FLOP per instruction (32x32x16: 32768, 16x16x32: 16384), against the",
+              "  algorithmic GFLOP of the stage (mean of the two modules; the attention kernels also multiply padding",
+              "  rows of the last 32-key chunk and form the softmax row sums on the matrix cores);",
+              "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs x cycles);" % N_SIMD,
+              "- VALU busy = 4 x SQ_ACTIVE_INST_VALU / (%d SIMDs x cycles) (a wave64 VALU instruction holds a" % N_SIMD,
+              "  16-lane SIMD for 4 cycles; MFMA issue included);",
+              "- LDS active = SQ_ACTIVE_INST_LDS / (%d CUs x cycles); bank conflicts = SQ_LDS_BANK_CONFLICT /" % N_CU,
+              "  SQ_ACTIVE_INST_LDS;",
+              "- waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES (share of resident wave time spent in s_waitcnt).", "",
+              "| stage | kernel | us | clock GHz | MFMA GFLOP | alg. GFLOP | MFMA busy | VALU busy | LDS active | "
+              "bank confl. | waiting |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    order = ["qkv_gemm", "attn_fwd", "proj_gemm", "dproj_gemm", "wgrad_proj", "attn_bwd", "dgrad_qkv", "wgrad_qkv"]
+    for (kname, role) in sorted(data, key=lambda k: order.index(k[1]) if k[1] in order else 99):
+        c = data[(kname, role)]
+        us = mean(dur[(kname, role)]) / 1e3
+        cyc = c.get("GRBM_GUI_ACTIVE", float("nan")) / N_XCD
+        f = lambda n: c.get(n, float("nan"))
+        mf = f("SQ_INSTS_MFMA") * MFMA_FLOP.get(base(kname), float("nan")) / 1e9
+        ag = mean([x.get(role, 0) for x in alg]) / 1e9
+        lines.append("| %s | %s | %.0f | %.2f | %.1f | %.1f | %.1f%% | %.1f%% | %.1f%% | %.2f | %.1f%% |" % (
+            role, kname, us, cyc / (us * 1e3), mf, ag, 100 * f("SQ_VALU_MFMA_BUSY_CYCLES") / (N_SIMD * cyc),
+            100 * 4 * f("SQ_ACTIVE_INST_VALU") / (N_SIMD * cyc), 100 * f("SQ_ACTIVE_INST_LDS") / (N_CU * cyc),
+            f("SQ_LDS_BANK_CONFLICT") / f("SQ_ACTIVE_INST_LDS"), 100 * f("SQ_WAIT_ANY") / f("SQ_WAVE_CYCLES")))
+    lines += ["", "Raw means per dispatch:", "", "| stage | " + " | ".join(sorted({n for v in data.values() for n in v}))
+              + " |", "|---|" + "---|" * len({n for v in data.values() for n in v})]
+    names = sorted({n for v in data.values() for n in v})
+    for (kname, role) in sorted(data, key=lambda k: order.index(k[1]) if k[1] in order else 99):
+        lines.append("| %s | " % role + " | ".join("%.4g" % data[(kname, role)].get(n, float("nan")) for n in names)
+                     + " |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    out = os.path.join(ROOT, "profiles", "counters_540x1080_c512.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -244,8 +342,11 @@ def main():
     f.add_argument("write_dir")
     f.add_argument("--cmd-fetch", required=True)
     f.add_argument("--cmd-write", required=True)
+    k = sub.add_parser("counters")
+    k.add_argument("dirs", nargs="+")
+    k.add_argument("--cmd", action="append", required=True)
     a = ap.parse_args()
-    (cmd_trace if a.what == "trace" else cmd_traffic)(a)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters}[a.what](a)
 
 
 if __name__ == "__main__":
