@@ -6,7 +6,9 @@ workload (a 2160x4320 field after 4x4 patch embedding): W-MSA forward, SW-MSA
 QKV GEMM + window attention + proj GEMM + scatter and their backward. Inputs are
 seeded synthetic data resident in HBM before the timed region. After the timed steps the
 window gather and scatter are also timed stand-alone against a device-to-device copy, and the
-chain is timed on one GPU's share of an 8-way latitude split (72x1080 tokens).
+chain is timed on one GPU's share of an 8-way latitude split (72x1080 tokens), with the saved
+state sent to host memory and back, and on the recomputing calls (o + LSE saved, q/k/v rebuilt
+in each backward).
 
 Then the other workloads of the measurement plan, each on its own (180x360 batch 2, the ragged
 181x361 grid and the 8x180x360 level grid forward + backward; the 32x64 fp32 grid forward):
@@ -480,6 +482,43 @@ def time_offload(hip, N, stream, mods, x, dy, outs, grads, steps):
     return res
 
 
+def time_recompute(hip, N, stream, mods, x, dy, outs, grads, steps):
+    """The chain step on the recomputing calls (saved state o + LSE; each backward rebuilds q/k/v
+    from its input with the QKV GEMM): ms per step and the device memory that stays saved from the
+    forwards to the backwards, against the saved-q/k/v calls."""
+    import torch
+    m1, m2 = mods
+    y1, y2, dx2, dx1 = outs
+    sizes = [N.swin_attn_sizes_recompute(m.plan.handle) for m in mods]
+    saved = [torch.empty(sz[2], dtype=torch.uint8, device="cuda") for sz in sizes]
+    ws = torch.empty(max(max(sz[0], sz[1]) for sz in sizes), dtype=torch.uint8, device="cuda")
+
+    def step():
+        N.swin_attn_fwd_recompute(m1.plan.handle, x, m1.w_qkv, m1.b_qkv, m1.w_proj, m1.b_proj, m1.table, y1,
+                                  saved[0], ws, stream=stream)
+        N.swin_attn_fwd_recompute(m2.plan.handle, y1, m2.w_qkv, m2.b_qkv, m2.w_proj, m2.b_proj, m2.table, y2,
+                                  saved[1], ws, stream=stream)
+        for m, d, xin, dxo, g, sv in ((m2, dy, y1, dx2, grads[1], saved[1]), (m1, dx2, x, dx1, grads[0], saved[0])):
+            N.swin_attn_bwd_recompute(m.plan.handle, d, xin, m.w_qkv, m.b_qkv, m.w_proj, m.table, sv, dxo,
+                                      g["w_qkv"], g["b_qkv"], g["w_proj"], g["b_proj"], g["table"], ws,
+                                      stream=stream)
+
+    ev = hip.events(2)
+    step()
+    torch.cuda.synchronize()
+    assert hip.l.hipEventRecord(ev[0], stream.cuda_stream) == 0
+    for _ in range(steps):
+        step()
+    assert hip.l.hipEventRecord(ev[1], stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    res = {"steps": steps, "chain_ms_per_step": round(hip.elapsed_ms(ev[0], ev[1]) / steps, 3),
+           "saved_bytes_per_module": sizes[0][2], "saved_bytes_per_module_with_qkv": m1.plan.saved_bytes,
+           "transient_workspace_bytes": ws.numel()}
+    hip.destroy(ev)
+    del saved, ws
+    return res
+
+
 def time_routes(hip, N, stream, cfg, ranks=8, reps=10):
     """TERRA's DMP route (8 latitude stripes -> 8 Eq. 4 window ranks) and shift route (unshifted
     -> shifted window ranks) on the full grid, all ranks on this GPU: per-rank pack, the
@@ -812,6 +851,7 @@ def main():
     shard = time_shard_share(hip, N, stream, cfg, max(1, args.steps // 2), max(1, args.warmup // 2))
     offload = time_offload(hip, N, stream, mods, x, dy, (y1, y2, dx2, dx1), grads, 3)
     offload["chain_ms_per_step"] = round(ms_step, 4)
+    recompute = time_recompute(hip, N, stream, mods, x, dy, (y1, y2, dx2, dx1), grads, max(1, args.steps // 5))
     # the activations of the attention chain are no longer needed: free them before the blocks
     del mods, grads, y1, y2, dx2, dx1
     torch.cuda.empty_cache()
@@ -846,7 +886,7 @@ def main():
         "algorithmic_gflop_per_step": round(flops_step / 1e9, 2),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "roofline": roof, "kernels": kernels, "window_moves": moves, "shard_share_8way": shard,
-        "swin_block_chain": block, "saved_offload": offload,
+        "swin_block_chain": block, "saved_offload": offload, "recompute_qkv": recompute,
         "token_routes_8_ranks": routes, "tiled_w32_hd128": tiled, "configs": configs, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

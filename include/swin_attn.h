@@ -242,6 +242,34 @@ swin_status swin_attn_bwd(const swin_attn_plan* plan, const void* dy, const void
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The module with the smaller saved-state contract: the forward keeps only o and the LSE, and
+ * the backward recomputes q, k, v from x with the forward's own QKV GEMM before the usual
+ * backward. This trades one QKV product (2 n_tok 3C C FLOPs, not counted as algorithmic) per
+ * backward for the q/k/v planes (3 n_tok C elements) that would otherwise stay in device memory
+ * from the forward to the backward: activation recomputation, as TERRA section VI's memory
+ * orchestration and the Samudra page's activation checkpointing use it to fit deeper models.
+ *   swin_attn_sizes_recompute: fwd_ws = the q/k/v planes (the forward's scratch, free after the
+ *     call), bwd_ws = the q/k/v planes + swin_attn_sizes' bwd_ws, saved_bytes = o + LSE.
+ *   swin_attn_fwd_recompute: as swin_attn_fwd, with saved (saved_bytes, required) holding
+ *     [o | LSE] and ws (fwd_ws) the q/k/v planes.
+ *   swin_attn_bwd_recompute: as swin_attn_bwd, plus b_qkv (the forward's, NULL for none) to
+ *     rebuild q/k/v; saved is the forward's [o | LSE]; ws (bwd_ws) holds the rebuilt planes and
+ *     the backward's workspace.
+ * Results are bitwise those of swin_attn_fwd / swin_attn_bwd on the same inputs. bf16 only
+ * (SWIN_ERR_UNSUPPORTED otherwise); SWIN_ERR_WORKSPACE for a short workspace, SWIN_ERR_ARG for
+ * NULL pointers or the aliasing swin_attn_fwd / swin_attn_bwd refuse.
+ */
+swin_status swin_attn_sizes_recompute(const swin_attn_plan* plan, size_t* fwd_ws, size_t* bwd_ws,
+                                      size_t* saved_bytes);
+swin_status swin_attn_fwd_recompute(const swin_attn_plan* plan, const void* x, const void* w_qkv, const void* b_qkv,
+                                    const void* w_proj, const void* b_proj, const float* bias_table, void* y,
+                                    void* saved, void* ws, size_t ws_bytes, void* stream);
+swin_status swin_attn_bwd_recompute(const swin_attn_plan* plan, const void* dy, const void* x, const void* w_qkv,
+                                    const void* b_qkv, const void* w_proj, const float* bias_table, const void* saved,
+                                    void* dx, float* dw_qkv, float* db_qkv, float* dw_proj, float* db_proj,
+                                    float* dbias_table, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * swin_attn_bwd without a workspace argument, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). The
  * arguments, results and errors are those of swin_attn_bwd; the workspace is a device array
@@ -280,6 +308,8 @@ swin_status swin_window_scatter(const swin_attn_plan* plan, const void* yw, void
  *   forward  (bf16): start | QKV GEMM | attention | proj GEMM                 -> 4 events
  *   backward (bf16): start | weight transposes | dO GEMM | dW_proj GEMM | attention backward
  *                    | dT reduction | dx GEMM | dW_qkv GEMM                   -> 8 events
+ * (the recomputing calls record the same; the recomputing backward launches its QKV GEMM before
+ * its first event, so that GEMM falls outside the recorded stages)
  * The elapsed time between consecutive events is the duration of that stage. events = NULL
  * uninstalls. swin_attn_trace_cursor returns how many events have been recorded since the
  * last install. Recording failures are reported as SWIN_ERR_HIP by the fwd/bwd call.

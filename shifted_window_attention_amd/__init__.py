@@ -15,6 +15,7 @@ from .native import (  # noqa: F401
     SwinAttnStats, SwinError, lib, make_desc, swin_attn_bwd, swin_attn_bwd_noalloc, swin_attn_fwd, swin_attn_host_index_map,
     swin_attn_host_stats, swin_attn_index_map, swin_attn_plan_create, swin_attn_plan_destroy, swin_attn_plan_stats, swin_attn_sizes,
     swin_attn_plan_flags, swin_block_plan_flags, SWIN_FLAG_DT_SATURATED,
+    swin_attn_sizes_recompute, swin_attn_fwd_recompute, swin_attn_bwd_recompute,
     swin_status_string, swin_window_gather, swin_window_scatter, swin_attn_trace_events, swin_attn_trace_cursor, Plan,
     SwinBlockDesc, SwinBlockParams, SwinBlockGrads, make_block_desc, swin_block_plan_create, swin_block_plan_destroy,
     swin_block_sizes, swin_block_fwd, swin_block_bwd, BlockPlan,

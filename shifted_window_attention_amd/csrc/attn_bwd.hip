@@ -337,11 +337,19 @@ hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* 
                            const void* w_proj, const float* table, const void* saved, void* dx, float* dw_qkv,
                            float* db_qkv, float* dw_proj, float* db_proj, float* dtable, void* ws,
                            hipStream_t s, float* dx32) {
-  const int C = p->C;
   const char* sv = (const char*)saved;
-  const bf16* qkv = (const bf16*)sv;
-  const bf16* o = (const bf16*)(sv + p->saved_qkv);
-  const float* lse = (const float*)(sv + p->saved_qkv + p->saved_o);
+  return launch_bwd_bf16_parts(p, dy, x, w_qkv, w_proj, table, sv, sv + p->saved_qkv,
+                               (const float*)(sv + p->saved_qkv + p->saved_o), dx, dw_qkv, db_qkv, dw_proj, db_proj,
+                               dtable, ws, s, dx32);
+}
+
+hipError_t launch_bwd_bf16_parts(const swin_attn_plan* p, const void* dy, const void* x, const void* w_qkv,
+                                 const void* w_proj, const float* table, const void* qkv_v, const void* o_v,
+                                 const float* lse, void* dx, float* dw_qkv, float* db_qkv, float* dw_proj,
+                                 float* db_proj, float* dtable, void* ws, hipStream_t s, float* dx32) {
+  const int C = p->C;
+  const bf16* qkv = (const bf16*)qkv_v;
+  const bf16* o = (const bf16*)o_v;
   char* w = (char*)ws;
   bf16* dO = (bf16*)w;
   bf16* dqkv = (bf16*)(w + p->bwd_do);

@@ -24,6 +24,11 @@ hipError_t launch_bwd_bf16(const swin_attn_plan*, const void*, const void*, cons
                            const void*, void*, float*, float*, float*, float*, float*, void*, hipStream_t, float*) {
   return hipErrorNotSupported;
 }
+hipError_t launch_bwd_bf16_parts(const swin_attn_plan*, const void*, const void*, const void*, const void*,
+                                 const float*, const void*, const void*, const float*, void*, float*, float*, float*,
+                                 float*, float*, void*, hipStream_t, float*) {
+  return hipErrorNotSupported;
+}
 hipError_t launch_proj_fwd_res_f32(const swin_attn_plan*, const void*, const void*, const void*, const void*, float*,
                                    hipStream_t) {
   return hipErrorNotSupported;

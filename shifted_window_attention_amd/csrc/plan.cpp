@@ -544,6 +544,58 @@ swin_status swin_attn_bwd(const swin_attn_plan* plan, const void* dy, const void
                     "bf16 backward");
 }
 
+swin_status swin_attn_sizes_recompute(const swin_attn_plan* plan, size_t* fwd_ws, size_t* bwd_ws,
+                                      size_t* saved_bytes) {
+  if (!plan) return fail(SWIN_ERR_ARG, "plan is NULL");
+  if (plan->d.dtype != SWIN_BF16) return fail(SWIN_ERR_UNSUPPORTED, "the recomputing calls are implemented for bf16 only");
+  if (fwd_ws) *fwd_ws = plan->saved_qkv;
+  if (bwd_ws) *bwd_ws = plan->saved_qkv + plan->bwd_total;
+  if (saved_bytes) *saved_bytes = plan->saved_o + plan->saved_lse;
+  return SWIN_OK;
+}
+
+swin_status swin_attn_fwd_recompute(const swin_attn_plan* plan, const void* x, const void* w_qkv, const void* b_qkv,
+                                    const void* w_proj, const void* b_proj, const float* bias_table, void* y,
+                                    void* saved, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan) return fail(SWIN_ERR_ARG, "plan is NULL");
+  if (plan->d.dtype != SWIN_BF16) return fail(SWIN_ERR_UNSUPPORTED, "the recomputing calls are implemented for bf16 only");
+  if (!x || !w_qkv || !w_proj || !bias_table || !y || !saved) return fail(SWIN_ERR_ARG, "NULL input or output pointer");
+  if (x == y) return fail(SWIN_ERR_ARG, "y must not alias x");
+  if (!ws || ws_bytes < plan->saved_qkv) return fail(SWIN_ERR_WORKSPACE, "forward workspace too small (q/k/v planes)");
+  hipStream_t s = (hipStream_t)stream;
+  void* qkv = ws;
+  void* o = saved;
+  float* lse = (float*)((char*)saved + plan->saved_o);
+  hipError_t e = trace_mark(s);
+  if (e == hipSuccess) e = launch_qkv_fwd_bf16(plan, x, w_qkv, b_qkv, qkv, s);
+  if (e == hipSuccess) e = trace_mark(s);
+  if (e == hipSuccess) e = launch_attn_fwd_bf16(plan, qkv, bias_table, o, lse, s);
+  if (e == hipSuccess) e = trace_mark(s);
+  if (e == hipSuccess) e = launch_proj_fwd_bf16(plan, o, w_proj, b_proj, y, s);
+  if (e == hipSuccess) e = trace_mark(s);
+  return hip_status(e, "bf16 forward (recomputing)");
+}
+
+swin_status swin_attn_bwd_recompute(const swin_attn_plan* plan, const void* dy, const void* x, const void* w_qkv,
+                                    const void* b_qkv, const void* w_proj, const float* bias_table, const void* saved,
+                                    void* dx, float* dw_qkv, float* db_qkv, float* dw_proj, float* db_proj,
+                                    float* dbias_table, void* ws, size_t ws_bytes, void* stream) {
+  const swin_status st = bwd_arg_checks(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, dw_proj,
+                                        dbias_table);
+  if (st != SWIN_OK) return st;
+  if (!ws || ws_bytes < plan->saved_qkv + plan->bwd_total)
+    return fail(SWIN_ERR_WORKSPACE, "backward workspace too small (q/k/v planes + backward workspace)");
+  hipStream_t s = (hipStream_t)stream;
+  void* qkv = ws;
+  const char* sv = (const char*)saved;
+  // q/k/v again from x, by the forward's own GEMM (bitwise the planes the forward attended over)
+  hipError_t e = launch_qkv_fwd_bf16(plan, x, w_qkv, b_qkv, qkv, s);
+  if (e == hipSuccess)
+    e = launch_bwd_bf16_parts(plan, dy, x, w_qkv, w_proj, bias_table, qkv, sv, (const float*)(sv + plan->saved_o), dx,
+                              dw_qkv, db_qkv, dw_proj, db_proj, dbias_table, (char*)ws + plan->saved_qkv, s);
+  return hip_status(e, "bf16 backward (recomputing q/k/v)");
+}
+
 swin_status swin_attn_bwd_noalloc(const swin_attn_plan* plan, const void* dy, const void* x, const void* w_qkv,
                                   const void* w_proj, const float* bias_table, const void* saved, void* dx,
                                   float* dw_qkv, float* db_qkv, float* dw_proj, float* db_proj, float* dbias_table,

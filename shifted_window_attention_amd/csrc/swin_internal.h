@@ -158,6 +158,12 @@ hipError_t launch_bwd_bf16(const swin_attn_plan* p, const void* dy, const void* 
                            const void* w_proj, const float* table, const void* saved, void* dx, float* dw_qkv,
                            float* db_qkv, float* dw_proj, float* db_proj, float* dtable, void* ws,
                            hipStream_t s, float* dx32 = nullptr);
+// launch_bwd_bf16 with the saved q/k/v planes, o rows and LSE given separately (saved is laid out
+// [q/k/v | o | LSE]; the recomputing backward rebuilds q/k/v in its workspace instead).
+hipError_t launch_bwd_bf16_parts(const swin_attn_plan* p, const void* dy, const void* x, const void* w_qkv,
+                                 const void* w_proj, const float* table, const void* qkv, const void* o,
+                                 const float* lse, void* dx, float* dw_qkv, float* db_qkv, float* dw_proj,
+                                 float* db_proj, float* dtable, void* ws, hipStream_t s, float* dx32 = nullptr);
 
 // Swin block pieces
 typedef __bf16 bf16_t;

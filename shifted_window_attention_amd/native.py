@@ -113,6 +113,9 @@ def _load():
         "swin_attn_fwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "swin_attn_bwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "swin_attn_bwd_noalloc": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "swin_attn_sizes_recompute": (st, [vp, P(sz), P(sz), P(sz)]),
+        "swin_attn_fwd_recompute": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "swin_attn_bwd_recompute": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "swin_window_gather": (st, [vp, vp, vp, vp]),
         "swin_window_scatter": (st, [vp, vp, vp, vp]),
         "swin_attn_trace_events": (st, [P(vp), st]),
@@ -347,6 +350,55 @@ def swin_attn_bwd(plan, dy, x, w_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_
     _check(lib.swin_attn_bwd(plan, _ptr(dy), _ptr(x), _ptr(w_qkv), _ptr(w_proj), _ptr(bias_table), _ptr(saved),
                              _ptr(dx), _ptr(dw_qkv), _ptr(db_qkv), _ptr(dw_proj), _ptr(db_proj), _ptr(dbias_table),
                              _ptr(ws), ws_bytes, _stream(stream)), "swin_attn_bwd")
+
+
+def swin_attn_sizes_recompute(plan):
+    """(fwd_ws, bwd_ws, saved_bytes) of the recomputing forward/backward pair."""
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.swin_attn_sizes_recompute(plan, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
+           "swin_attn_sizes_recompute")
+    return a.value, b.value, c.value
+
+
+def swin_attn_fwd_recompute(plan, x, w_qkv, b_qkv, w_proj, b_proj, bias_table, y, saved, ws, stream=None):
+    """swin_attn_fwd keeping only [o | LSE] in saved; ws (fwd_ws bytes) takes the q/k/v planes."""
+    sh = _ATTN_SHAPES.get(_key(plan))
+    if sh is not None:
+        _, _, saved_bytes = swin_attn_sizes_recompute(plan)
+        rows = sh.n_tok * sh.C * sh.elem
+        check_buffer(x, "x", rows, _torch_dtype(sh.dtype_code))
+        check_buffer(y, "y", rows, _torch_dtype(sh.dtype_code))
+        _check_attn_weights(sh, w_qkv, b_qkv, w_proj, b_proj, bias_table)
+        check_buffer(saved, "saved", saved_bytes)
+        check_buffer(ws, "ws", 0)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.swin_attn_fwd_recompute(plan, _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_proj), _ptr(b_proj),
+                                       _ptr(bias_table), _ptr(y), _ptr(saved), _ptr(ws), ws_bytes, _stream(stream)),
+           "swin_attn_fwd_recompute")
+
+
+def swin_attn_bwd_recompute(plan, dy, x, w_qkv, b_qkv, w_proj, bias_table, saved, dx, dw_qkv, db_qkv, dw_proj,
+                            db_proj, dbias_table, ws, stream=None):
+    """swin_attn_bwd that rebuilds q/k/v from x (and b_qkv) into ws before the backward."""
+    sh = _ATTN_SHAPES.get(_key(plan))
+    if sh is not None:
+        _, _, saved_bytes = swin_attn_sizes_recompute(plan)
+        rows, dt, f32, C = sh.n_tok * sh.C * sh.elem, _torch_dtype(sh.dtype_code), _torch_dtype(SWIN_F32), sh.C
+        for t, what in ((dy, "dy"), (x, "x"), (dx, "dx")):
+            check_buffer(t, what, rows, dt)
+        _check_attn_weights(sh, w_qkv, b_qkv, w_proj, None, bias_table)
+        check_buffer(saved, "saved", saved_bytes)
+        check_buffer(dw_qkv, "dw_qkv", 3 * C * C * 4, f32)
+        check_buffer(db_qkv, "db_qkv", 3 * C * 4, f32)
+        check_buffer(dw_proj, "dw_proj", C * C * 4, f32)
+        check_buffer(db_proj, "db_proj", C * 4, f32)
+        check_buffer(dbias_table, "dbias_table", sh.table * 4, f32)
+        check_buffer(ws, "ws", 0)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.swin_attn_bwd_recompute(plan, _ptr(dy), _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_proj),
+                                       _ptr(bias_table), _ptr(saved), _ptr(dx), _ptr(dw_qkv), _ptr(db_qkv),
+                                       _ptr(dw_proj), _ptr(db_proj), _ptr(dbias_table), _ptr(ws), ws_bytes,
+                                       _stream(stream)), "swin_attn_bwd_recompute")
 
 
 SWIN_NOALLOC_SCRATCH_BYTES = 64 << 20
