@@ -212,14 +212,15 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
           }
           *(bf16x4*)(dSt + key * SPT + 16 * qt + 4 * g) = bf16x4{sb[4 * u], sb[4 * u + 1], sb[4 * u + 2], sb[4 * u + 3]};
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         dvacc[dt] = mfma16(tile_frag_tr(cur.dO, 32 * c, 16 * dt, g, li), pb, dvacc[dt]);
         dkacc[dt] = mfma16(tile_frag_tr(cur.q, 32 * c, 16 * dt, g, li), sb, dkacc[dt]);
       }
-      __builtin_amdgcn_sched_barrier(0);  // bound live ranges to one query chunk
+      // bound live ranges to one query chunk (the two tiles inside a chunk may interleave: the
+      // second tile's S and dP products overlap the first tile's exp and conversions)
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();  // dS complete; the next window's copies have landed
     if (key < n) {
