@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, os.path.join(ROOT, "shifted_window_attention_amd"))
 
-HOST_TESTS = ["tests/test_abi_host.py", "tests/test_route_host.py"]
+HOST_TESTS = ["tests/test_abi_host.py", "tests/test_route_host.py", "tests/test_host_fuzz.py"]
 
 
 def test_host_code_is_clean_under_asan_and_ubsan():
