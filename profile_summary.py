@@ -30,16 +30,17 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# launch order of the two GEMM kernels within one bench step (W fwd, SW fwd, SW bwd, W bwd)
-NT_ROLES = ["qkv_gemm", "proj_gemm", "qkv_gemm", "proj_gemm", "dproj_gemm", "dgrad_qkv", "dproj_gemm", "dgrad_qkv"]
+# launch order of the GEMM kernels within one bench step (W fwd, SW fwd, SW bwd, W bwd); the
+# QKV product runs on its own kernel (k_gemm_nt_wide)
+NT_ROLES = ["proj_gemm", "proj_gemm", "dproj_gemm", "dgrad_qkv", "dproj_gemm", "dgrad_qkv"]
 TN_ROLES = ["wgrad_proj", "wgrad_qkv", "wgrad_proj", "wgrad_qkv"]
-SINGLE = {"k_attn_fwd": "attn_fwd", "k_attn_bwd": "attn_bwd"}
+SINGLE = {"k_attn_fwd": "attn_fwd", "k_attn_bwd": "attn_bwd", "k_gemm_nt_wide": "qkv_gemm"}
 # the same for one step of the two-block chain (block 0 fwd, block 1 fwd, block 1 bwd, block 0 bwd)
-NT_BLOCK_ROLES = (["qkv_gemm", "proj_res_gemm", "mlp_w1_gelu", "mlp_w2_res"] * 2 +
+NT_BLOCK_ROLES = (["proj_res_gemm", "mlp_w1_gelu", "mlp_w2_res"] * 2 +
                   ["mlp_dgelu", "mlp_dxn", "dproj_gemm", "dgrad_qkv"] * 2)
 TN_BLOCK_ROLES = ["wgrad_w2", "wgrad_w1", "wgrad_proj", "wgrad_qkv"] * 2
 BLOCK_START = "k_layernorm_fwd"
-SOURCES = {"k_gemm_nt": "gemm.hip", "k_gemm_tn": "gemm.hip", "k_attn_fwd": "attn_fwd.hip",
+SOURCES = {"k_gemm_nt": "gemm.hip", "k_gemm_nt_wide": "gemm.hip", "k_gemm_tn": "gemm.hip", "k_attn_fwd": "attn_fwd.hip",
            "k_attn_bwd": "attn_bwd.hip"}
 COPY = "k_window_move<true>"
 
@@ -236,7 +237,7 @@ def cmd_traffic(a):
 
 # FLOP per MFMA instruction: the GEMMs run v_mfma_f32_32x32x16_bf16, the attention kernels
 # v_mfma_f32_16x16x32_bf16
-MFMA_FLOP = {"k_gemm_nt": 2 * 32 * 32 * 16, "k_gemm_tn": 2 * 32 * 32 * 16, "k_attn_fwd": 2 * 16 * 16 * 32,
+MFMA_FLOP = {"k_gemm_nt": 2 * 32 * 32 * 16, "k_gemm_nt_wide": 2 * 32 * 32 * 16, "k_gemm_tn": 2 * 32 * 32 * 16, "k_attn_fwd": 2 * 16 * 16 * 32,
              "k_attn_bwd": 2 * 16 * 16 * 32}
 N_CU, N_SIMD, N_XCD = 256, 1024, 8
 

@@ -376,6 +376,212 @@ __global__ __launch_bounds__(256, BM == 128 ? 3 : 2) void k_gemm_nt(const bf16* 
 }
 
 // ---------------------------------------------------------------------------
+// Wide NT GEMM for the QKV projection: C = A B^T with 256 x 256 output tiles, 8 waves of
+// 128 x 64 (v_mfma_f32_32x32x16_bf16), one workgroup per CU.
+//
+// Operands are copied straight into LDS (global_load_lds, 16 bytes per lane, gathered A rows
+// allowed) through a ring of three 32-deep K stages of 32 KB, each 64-byte tile row holding
+// its four 16-byte chunks at slot chunk ^ swz(row). The loop is software-pipelined across K
+// steps: a step's first fragments are read before the step starts, and the barrier that makes
+// the next stage visible sits after the step's last MFMAs are issued, so it overlaps their
+// execution; right after that barrier the stage the step used takes the copies of the stage
+// three ahead. The accumulators hold transposed 32 x 32 blocks (the MFMA's operands swapped),
+// so a lane owns one output row and 4 consecutive columns per register group; the epilogue
+// (bias, q scale, bf16) stages the tile in LDS and stores 16-byte row chunks, as plain rows
+// (mode 0) or head-split planes (mode 1). Results are bitwise those of k_gemm_nt: the same
+// products summed over K in the same order.
+// ---------------------------------------------------------------------------
+namespace wide {
+constexpr int BM = 256, BN = 256, BK = 32, ST = 3;
+constexpr int NW = 8, NT = 64 * NW, WN = 4;   // waves: 2 along M, 4 along N
+constexpr int WTM = 128, WTN = 64, TM = WTM / 32, TN = WTN / 32;
+constexpr int A_BYTES = BM * 64, STAGE = (BM + BN) * 64;  // one 32-deep K step of A and B
+constexpr int CP = BM / 16 / NW + BN / 16 / NW;           // 1 KB copies per wave per stage
+constexpr int CPITCH = BN + 8;                            // bf16 per row of the staged output tile
+constexpr int LDS = ST * STAGE > BM * CPITCH * 2 ? ST * STAGE : BM * CPITCH * 2;
+
+__device__ __forceinline__ bf16x8 frag(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return __builtin_bit_cast(bf16x8, v);
+}
+template <int NA, int NB>
+__device__ __forceinline__ void wait_frags(bf16x8 (&fa)[NA], bf16x8 (&fb)[NB]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < NA; ++i) asm volatile("" : "+v"(fa[i]));
+#pragma unroll
+  for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(fb[j]));
+}
+// this wave's copies of a stage have landed once at most `newer` later stages' are in flight
+__device__ __forceinline__ void wait_stage(int newer) {
+  if (newer >= 2)
+    vm_wait(2 * CP);
+  else if (newer == 1)
+    vm_wait(CP);
+  else
+    vm_wait(0);
+}
+}  // namespace wide
+
+__global__ __launch_bounds__(wide::NT, 1) void k_gemm_nt_wide(const bf16* __restrict__ A, int64_t lda,
+                                                             const int32_t* __restrict__ a_rows,
+                                                             const bf16* __restrict__ B, int64_t ldb, int64_t M,
+                                                             int N, int K, EpiParams ep) {
+  using namespace wide;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w / WN, wn = w % WN;
+  int64_t mt;
+  int ntile;
+  const int n_nt = (N + BN - 1) / BN;
+  if (!xcd_tile(((M + BM - 1) / BM) * n_nt, n_nt, mt, ntile)) return;
+  const int64_t m0 = mt * BM;
+  const int n0 = ntile * BN;
+
+  // copy q of this wave fills tile rows 16 (w + NW q) + lane/4 at slot lane%4, i.e. logical
+  // chunk (lane%4) ^ swz(row); rows past M or N repeat the last row (computed, never stored)
+  const unsigned char* a_src[BM / 16 / NW];
+  const unsigned char* b_src[BN / 16 / NW];
+#pragma unroll
+  for (int q = 0; q < BM / 16 / NW; ++q) {
+    const int r = 16 * (w + NW * q) + (lane >> 2);
+    int64_t gr = m0 + r;
+    gr = gr < M ? gr : M - 1;
+    if (a_rows) gr = a_rows[gr];
+    a_src[q] = (const unsigned char*)(A + gr * lda) + 16 * ((lane & 3) ^ swz(r));
+  }
+#pragma unroll
+  for (int q = 0; q < BN / 16 / NW; ++q) {
+    const int r = 16 * (w + NW * q) + (lane >> 2);
+    int64_t gr = n0 + r;
+    gr = gr < N ? gr : N - 1;
+    b_src[q] = (const unsigned char*)(B + gr * ldb) + 16 * ((lane & 3) ^ swz(r));
+  }
+  auto issue = [&](int kt) {
+    unsigned char* st = smem + (kt % ST) * STAGE;
+    const int kb = kt * 64;
+#pragma unroll
+    for (int q = 0; q < BM / 16 / NW; ++q) lds_copy16(a_src[q] + kb, st + 1024 * (w + NW * q));
+#pragma unroll
+    for (int q = 0; q < BN / 16 / NW; ++q) lds_copy16(b_src[q] + kb, st + A_BYTES + 1024 * (w + NW * q));
+  };
+
+  // fragment offsets: A rows wm WTM + 32 i + lane%32, B rows wn WTN + 32 j + lane%32, chunk
+  // lane/32 (K slice 0) or 2 + lane/32 (slice 1); rows 32 apart share their swizzle
+  const int fr = lane & 31;
+  const uint32_t l0 = (uint32_t)(fr * 64 + 16 * ((lane >> 5) ^ swz(fr)));
+  const uint32_t l1 = (uint32_t)(fr * 64 + 16 * (((lane >> 5) | 2) ^ swz(fr)));
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t a_w = (uint32_t)(wm * WTM * 64), b_w = (uint32_t)(A_BYTES + wn * WTN * 64);
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+  const int KT = K / BK;
+#pragma unroll
+  for (int s = 0; s < ST; ++s)
+    if (s < KT) issue(s);
+  wait_stage((ST - 1 < KT - 1 ? ST - 1 : KT - 1));  // stage 0 (the stages issued after it may fly)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) fa0[i] = frag(lds0 + a_w + l0 + 2048 * i);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) fb0[j] = frag(lds0 + b_w + l0 + 2048 * j);
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint32_t sb = lds0 + (uint32_t)((kt % ST) * STAGE);
+    wait_frags(fa0, fb0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa1[i] = frag(sb + a_w + l1 + 2048 * i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb1[j] = frag(sb + b_w + l1 + 2048 * j);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fb0[j], fa0[i], acc[i][j]);
+    wait_frags(fa1, fb1);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fb1[j], fa1[i], acc[i][j]);
+    if (kt + 1 < KT) {
+      // the newest stage issued so far is kt - 1 + ST (or KT - 1)
+      const int last = kt - 1 + ST < KT - 1 ? kt - 1 + ST : KT - 1;
+      wait_stage(last - (kt + 1));
+      // every wave's copies of stage kt+1 have landed and every wave has read stage kt
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (kt + ST < KT) issue(kt + ST);  // into the buffer step kt used
+      const uint32_t sn = lds0 + (uint32_t)(((kt + 1) % ST) * STAGE);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa0[i] = frag(sn + a_w + l0 + 2048 * i);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb0[j] = frag(sn + b_w + l0 + 2048 * j);
+    }
+  }
+
+  // epilogue: bias and q scale on the transposed blocks (a lane's 4 consecutive columns per
+  // register group), bf16 tile through LDS, 16-byte row chunks out
+  bf16* Cs = (bf16*)smem;
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const int half = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int nl = wn * WTN + 32 * j + 8 * g + 4 * half;
+      const int n = n0 + nl;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (ep.bias && n < N) {
+        const bf16x4 b4 = *(const bf16x4*)(ep.bias + n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[e] = to_f32(b4[e]);
+      }
+      const float scv = (ep.mode == 1 && n < ep.C) ? ep.qscale : 1.f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int ml = wm * WTM + 32 * i + fr;
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = to_bf16((acc[i][j][4 * g + e] + bv[e]) * scv);
+        *(bf16x4*)(Cs + ml * CPITCH + nl) = o;
+      }
+    }
+  __syncthreads();
+  constexpr int CH_PER_ROW = BN / 8;
+  constexpr int ROW_STEP = NT / CH_PER_ROW;
+  constexpr int ITERS = BM / ROW_STEP;
+  static_assert(NT % CH_PER_ROW == 0 && BM % ROW_STEP == 0, "uniform copy-out loop");
+  const int cc = (tid % CH_PER_ROW) * 8;
+  const int n = n0 + cc;
+  const int row0 = tid / CH_PER_ROW;
+  int64_t col_off, row_pitch;
+  if (ep.mode == 1) {
+    const int plane = n / ep.C;
+    const int rem = n - plane * ep.C;
+    const int head = rem / ep.hd;
+    col_off = ((int64_t)plane * ep.nh + head) * ep.n_tok * ep.hd + (rem - head * ep.hd);
+    row_pitch = ep.hd;
+  } else {
+    col_off = n;
+    row_pitch = ep.ldc;
+  }
+#pragma unroll 4
+  for (int it = 0; it < ITERS; ++it) {
+    const int row = row0 + ROW_STEP * it;
+    const int64_t m = m0 + row;
+    if (m < M && n < N) {
+      const int64_t orow = (ep.mode == 0 && ep.out_rows) ? (int64_t)ep.out_rows[m] : m;
+      *(bf16x8*)(ep.out + col_off + orow * row_pitch) = *(const bf16x8*)(Cs + row * CPITCH + cc);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Weight-gradient GEMM: P[s] = sum over the tokens t of chunk s of A[t, m0:m0+256]^T B[t, n0:n0+256]
 // (both operands token-major: a contraction over tokens), stored per split as
 // P[s][m/4][n][m%4] so that each lane's four consecutive MFMA rows are one 16-byte store.
@@ -693,7 +899,11 @@ hipError_t launch_qkv_fwd_bf16(const swin_attn_plan* p, const void* x, const voi
   ep.nh = p->nh;
   ep.hd = p->hd;
   ep.n_tok = p->n_tok;
-  return gemm_nt((const bf16*)x, p->C, p->dev.perm, (const bf16*)w, p->C, p->n_tok, 3 * p->C, p->C, ep, s);
+  // the wide kernel (K in 32-deep steps; C is a multiple of 64)
+  const int64_t tiles = ((p->n_tok + wide::BM - 1) / wide::BM) * ((3 * p->C + wide::BN - 1) / wide::BN);
+  k_gemm_nt_wide<<<xcd_grid(tiles), wide::NT, 0, s>>>((const bf16*)x, p->C, p->dev.perm, (const bf16*)w, p->C,
+                                                       p->n_tok, 3 * p->C, p->C, ep);
+  return hipGetLastError();
 }
 
 hipError_t launch_proj_fwd_bf16(const swin_attn_plan* p, const void* o, const void* w, const void* b, void* y,
