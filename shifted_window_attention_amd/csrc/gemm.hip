@@ -5,11 +5,13 @@
 //                partition fused into the operand load), and the epilogue writes
 //                head-split q/k/v planes or plain rows (optionally through a row map)
 //                and can also form per-head row dot products with a second matrix.
+//   k_gemm_nt_wide: the same product for the QKV projection (gathered A rows, head-split
+//                epilogue) on 256 x 256 tiles fed by direct global->LDS copies.
 //   k_gemm_tn:   P[s, m, n] = sum_{t in chunk s} A[t, m] * B[t, n]   (contraction over
 //                tokens for the weight gradients; deterministic split-K partials)
 //   k_reduce_splits: fixed-order sum of the split-K partials (weights and biases).
 //
-// Both GEMMs run on v_mfma_f32_32x32x16_bf16. k_gemm_nt: 256 threads (4 waves of 64),
+// All run on v_mfma_f32_32x32x16_bf16. k_gemm_nt: 256 threads (4 waves of 64),
 // 64-deep K steps staged through LDS via registers, rows padded by 16 bytes so that both
 // the row-wise 16-byte stores and the MFMA fragment reads are bank-conflict free.
 // k_gemm_tn: operand tiles copied straight into swizzled LDS tiles, double-buffered.
