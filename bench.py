@@ -33,6 +33,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -107,8 +108,15 @@ def stage_flops_bytes(cfg, pairs):
 
 
 def source_sha(fname):
-    with open(os.path.join(ROOT, "shifted_window_attention_amd", "csrc", fname), "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """Hash of a kernel source file's code: comments and blank lines are left out, so that a
+    change of comments alone does not mark counters taken on the file as stale. (bench.py and
+    profile_summary.py compute it the same way.)"""
+    with open(os.path.join(ROOT, "shifted_window_attention_amd", "csrc", fname)) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_for(stage, per_launch_ref):

@@ -24,6 +24,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 from collections import defaultdict
 
@@ -62,8 +63,15 @@ def find(dirname, suffix):
 
 
 def source_sha(fname):
-    with open(os.path.join(ROOT, "shifted_window_attention_amd", "csrc", fname), "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """Hash of a kernel source file's code: comments and blank lines are left out, so that a
+    change of comments alone does not mark counters taken on the file as stale. (bench.py and
+    profile_summary.py compute it the same way.)"""
+    with open(os.path.join(ROOT, "shifted_window_attention_amd", "csrc", fname)) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def cmd_trace(a):
