@@ -309,11 +309,23 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
 }
 
 // dT[h][b] = sum over work items (in order) of the partial tables.
+// The partials are loaded 16 at a time before they are added (in item order), so that the
+// loads of a thread overlap instead of each waiting for the previous add.
 __global__ void k_dbias_reduce(const float* __restrict__ part, int n_items, int per_item, float* __restrict__ out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= per_item) return;
+  constexpr int U = 16;
+  const float* src = part + i;
   float acc = 0.f;
-  for (int it = 0; it < n_items; ++it) acc += part[(int64_t)it * per_item + i];
+  int it = 0;
+  for (; it + U <= n_items; it += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[(int64_t)(it + u) * per_item];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += v[u];
+  }
+  for (; it < n_items; ++it) acc += src[(int64_t)it * per_item];
   out[i] = acc;
 }
 

@@ -825,6 +825,24 @@ __global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ 
 // Split-K reduction of the weight gradients, in order of s:
 //   dw[m][n] = sum_s P[s][m/4][n][m%4]   (threads 0 .. M N / 4 - 1: 4 rows of one column)
 //   db[m]    = sum_s dbpart[s][m]        (the next M / 4 threads: 4 consecutive entries)
+// sum over k < S of rows[k * stride + t] (f32x4 units) in order of k; the loads are issued
+// eight at a time ahead of their adds, so that they overlap
+__device__ __forceinline__ f32x4 sum_rows(const float* rows, int64_t t, int64_t stride, int S) {
+  constexpr int U = 8;
+  const f32x4* src = (const f32x4*)rows + t;
+  f32x4 acc = src[0];
+  int k = 1;
+  for (; k + U <= S; k += U) {
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[(k + u) * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += v[u];
+  }
+  for (; k < S; ++k) acc += src[k * stride];
+  return acc;
+}
+
 __global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__ part, int S, int M, int N,
                                                        float* __restrict__ dw, const float* __restrict__ dbpart,
                                                        float* __restrict__ db) {
@@ -833,10 +851,7 @@ __global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__
   if (t < n_w) {
     const int64_t mq = t / N;
     const int n = (int)(t - mq * N);
-    const f32x4* src = (const f32x4*)part + t;
-    const int64_t stride = n_w;  // one split, in f32x4
-    f32x4 acc = src[0];
-    for (int k = 1; k < S; ++k) acc += src[k * stride];
+    const f32x4 acc = sum_rows(part, t, n_w, S);  // one split is n_w f32x4
     float* o = dw + (4 * mq) * N + n;
     o[0] = acc[0];
     o[N] = acc[1];
@@ -844,9 +859,7 @@ __global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__
     o[3 * N] = acc[3];
   } else if (db && t < n_w + M / 4) {
     const int64_t i = t - n_w;
-    const f32x4* src = (const f32x4*)dbpart + i;
-    f32x4 acc = src[0];
-    for (int k = 1; k < S; ++k) acc += src[k * (M / 4)];
+    const f32x4 acc = sum_rows(dbpart, i, M / 4, S);
     float* o = db + 4 * i;  // the caller's pointer: no alignment beyond 4 bytes assumed
     o[0] = acc[0];
     o[1] = acc[1];
