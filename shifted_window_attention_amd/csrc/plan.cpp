@@ -397,8 +397,9 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
       for (int b = 0; b * 128 < n; ++b) p->tiled_kv_work.push_back(WorkItem{c, (int32_t)w, b, code_off[c]});
     }
   }
-  // the backward bins its bias gradient once per work item: fewer, longer items (1 WG per CU)
-  build_work(p->classes, p->nh, 1024, kMaxChunk, p->bwd_work, p->bwd_ranges);
+  // the backward ends every workgroup with a pass that bins its bias-gradient sums: half the
+  // forward's workgroup count (twice the windows each) measured faster on small grids
+  build_work(p->classes, p->nh, 512, kMaxChunk, p->bwd_work, p->bwd_ranges);
 
   // saved state and workspace layout
   const size_t es = desc->dtype == SWIN_BF16 ? 2 : 4;
