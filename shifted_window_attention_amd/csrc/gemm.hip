@@ -822,9 +822,6 @@ __global__ __launch_bounds__(tn::NT, 1) void k_gemm_tn(const bf16* __restrict__ 
   }
 }
 
-// Split-K reduction of the weight gradients, in order of s:
-//   dw[m][n] = sum_s P[s][m/4][n][m%4]   (threads 0 .. M N / 4 - 1: 4 rows of one column)
-//   db[m]    = sum_s dbpart[s][m]        (the next M / 4 threads: 4 consecutive entries)
 // sum over k < S of rows[k * stride + t] (f32x4 units) in order of k; the loads are issued
 // eight at a time ahead of their adds, so that they overlap
 __device__ __forceinline__ f32x4 sum_rows(const float* rows, int64_t t, int64_t stride, int S) {
@@ -843,6 +840,9 @@ __device__ __forceinline__ f32x4 sum_rows(const float* rows, int64_t t, int64_t 
   return acc;
 }
 
+// Split-K reduction of the weight gradients, in order of s:
+//   dw[m][n] = sum_s P[s][m/4][n][m%4]   (threads 0 .. M N / 4 - 1: 4 rows of one column)
+//   db[m]    = sum_s dbpart[s][m]        (the next M / 4 threads: 4 consecutive entries)
 __global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__ part, int S, int M, int N,
                                                        float* __restrict__ dw, const float* __restrict__ dbpart,
                                                        float* __restrict__ db) {
