@@ -168,11 +168,8 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
   auto flush = [&]() {
     if (prev_off < 0) return;
     const int q = 16 * kt + li;
-    if (q < n) {
-      bf16* row = a.dqkv + (int64_t)prev_row * (3 * C) + h * 32;
-      *(bf16x4*)(row + 4 * g) = pq[0];
-      *(bf16x4*)(row + 16 + 4 * g) = pq[1];
-    }
+    const bf16x8 dq8 = pair_cols(pq[0], pq[1], g);
+    if (q < n) *(bf16x8*)(a.dqkv + (int64_t)prev_row * (3 * C) + h * 32 + pair_col(g)) = dq8;
   };
 
   auto window = [&](int w, const BwdBuf<NKT>& cur, BwdBuf<NKT>& nxt) {
@@ -223,18 +220,20 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();  // dS complete; the next window's copies have landed
-    if (key < n) {
-      bf16* row = a.dqkv + (int64_t)cur.grow[key] * (3 * C) + h * 32;
+    {
+      bf16x4 k4[2], v4[2];
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        bf16x4 k4, v4;
+      for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          k4[i] = to_bf16(dkacc[dt][i] * inv_log2e);
-          v4[i] = to_bf16(dvacc[dt][i]);
+          k4[dt][i] = to_bf16(dkacc[dt][i] * inv_log2e);
+          v4[dt][i] = to_bf16(dvacc[dt][i]);
         }
-        *(bf16x4*)(row + C + 16 * dt + 4 * g) = k4;
-        *(bf16x4*)(row + 2 * C + 16 * dt + 4 * g) = v4;
+      const bf16x8 k8 = pair_cols(k4[0], k4[1], g), v8 = pair_cols(v4[0], v4[1], g);
+      if (key < n) {
+        bf16* row = a.dqkv + (int64_t)cur.grow[key] * (3 * C) + h * 32 + pair_col(g);
+        *(bf16x8*)(row + C) = k8;
+        *(bf16x8*)(row + 2 * C) = v8;
       }
     }
     // dQ^T for query tile kt: K^T (transposed read of K) times dS^T, whose columns (8 keys

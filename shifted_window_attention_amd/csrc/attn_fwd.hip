@@ -175,11 +175,12 @@ __global__ __launch_bounds__(64 * NKT, FwdSmem<NKT>::MIN_BLOCKS) void k_attn_fwd
     }
     // every wave's copies into `cur` have landed, and every wave is done with window w-1
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (prev_off >= 0 && qv) {
-      bf16* orow = a.o + (int64_t)prev_row * a.C + h * 32;
-      *(bf16x4*)(orow + 4 * g) = ov[0];
-      *(bf16x4*)(orow + 16 + 4 * g) = ov[1];
-      if (g == 0) a.lse[(int64_t)h * a.n_tok + prev_off + q] = lse_v;
+    if (prev_off >= 0) {
+      const bf16x8 o8 = pair_cols(ov[0], ov[1], g);
+      if (qv) {
+        *(bf16x8*)(a.o + (int64_t)prev_row * a.C + h * 32 + pair_col(g)) = o8;
+        if (g == 0) a.lse[(int64_t)h * a.n_tok + prev_off + q] = lse_v;
+      }
     }
     if (w + NBUF - 1 < wk.count) stage(w + NBUF - 1);  // into the buffer window w-1 used
     const bf16x8 bq = *(const bf16x8*)(cur.q + kq_off + 1024 * qt);
@@ -230,11 +231,12 @@ __global__ __launch_bounds__(64 * NKT, FwdSmem<NKT>::MIN_BLOCKS) void k_attn_fwd
     prev_off = sm.offs[w];
     prev_row = cur.grow[64 * qt + li];
   }
-  if (prev_off >= 0 && qv) {
-    bf16* orow = a.o + (int64_t)prev_row * a.C + h * 32;
-    *(bf16x4*)(orow + 4 * g) = ov[0];
-    *(bf16x4*)(orow + 16 + 4 * g) = ov[1];
-    if (g == 0) a.lse[(int64_t)h * a.n_tok + prev_off + q] = lse_v;
+  if (prev_off >= 0) {
+    const bf16x8 o8 = pair_cols(ov[0], ov[1], g);
+    if (qv) {
+      *(bf16x8*)(a.o + (int64_t)prev_row * a.C + h * 32 + pair_col(g)) = o8;
+      if (g == 0) a.lse[(int64_t)h * a.n_tok + prev_off + q] = lse_v;
+    }
   }
 }
 

@@ -65,6 +65,23 @@ __device__ __forceinline__ float pair_bias_codes(int cq, int ck, int code0, cons
 // one logical chunk touch distinct banks.
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
+// Lanes l and l ^ 16 (g = l / 16 and g ^ 1, same l % 16) hold columns 4 g .. 4 g + 3 of one
+// row in v0 and columns 16 + 4 g .. 16 + 4 g + 3 in v1. After one exchange an even-g lane
+// holds columns 4 g .. 4 g + 7 and an odd-g lane columns 4 g + 12 .. 4 g + 19 (both start at
+// pair_col(g)), so each lane writes one 16-byte piece and four lanes a whole 64-byte row piece.
+// Every lane of the wave must take part.
+__device__ __forceinline__ bf16x8 pair_cols(bf16x4 v0, bf16x4 v1, int g) {
+  const bool even = (g & 1) == 0;
+  const u32x2 send = __builtin_bit_cast(u32x2, even ? v1 : v0);
+  u32x2 recv;
+  recv[0] = (uint32_t)__shfl_xor((int)send[0], 16);
+  recv[1] = (uint32_t)__shfl_xor((int)send[1], 16);
+  const bf16x4 r = __builtin_bit_cast(bf16x4, recv);
+  return even ? bf16x8{v0[0], v0[1], v0[2], v0[3], r[0], r[1], r[2], r[3]}
+              : bf16x8{r[0], r[1], r[2], r[3], v1[0], v1[1], v1[2], v1[3]};
+}
+__device__ __forceinline__ int pair_col(int g) { return (g & 1) == 0 ? 4 * g : 4 * g + 12; }
+
 // Byte offset of element `col` (multiple of 4) of row r in a swizzled tile.
 __device__ __forceinline__ int swz_off(int r, int col) {
   return r * 64 + 16 * ((col >> 3) ^ swz(r)) + 2 * (col & 7);
