@@ -505,9 +505,10 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
       }
     }
   }
-  if (qv) {
-    const int64_t grow = a.perm[off + q];
-    bf16* row = a.dqkv + grow * 3 * a.C + (int64_t)h * HD;
+  {
+    // 16-byte pieces: lanes 16 apart (same query) swap halves (every lane takes part)
+    const int64_t grow = qv ? a.perm[off + q] : 0;
+    bf16* row = a.dqkv + grow * 3 * a.C + (int64_t)h * HD + pair_col(g);
 #pragma unroll
     for (int sc = 0; sc < NSUB; ++sc) {
       bf16x4 o0, o1;
@@ -516,8 +517,8 @@ __global__ __launch_bounds__(256, 2) void k_tiled_bwd_dq(TiledArgs a) {
         o0[i] = to_bf16(dqacc[2 * sc][i] * a.tau);
         o1[i] = to_bf16(dqacc[2 * sc + 1][i] * a.tau);
       }
-      *(bf16x4*)(row + 32 * sc + 4 * g) = o0;
-      *(bf16x4*)(row + 32 * sc + 16 + 4 * g) = o1;
+      const bf16x8 o8 = pair_cols(o0, o1, g);
+      if (qv) *(bf16x8*)(row + 32 * sc) = o8;
     }
   }
 }
@@ -726,9 +727,10 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
       }
     }
   }
-  if (kv) {
-    const int64_t grow = a.perm[off + k];
-    bf16* row = a.dqkv + grow * 3 * a.C + (int64_t)h * HD;
+  {
+    // 16-byte pieces: lanes 16 apart (same key) swap halves (every lane takes part)
+    const int64_t grow = kv ? a.perm[off + k] : 0;
+    bf16* row = a.dqkv + grow * 3 * a.C + (int64_t)h * HD + pair_col(g);
     const float kscale = 1.f / kLog2e;  // q' = tau log2(e) q
 #pragma unroll
     for (int sc = 0; sc < NSUB; ++sc) {
@@ -740,10 +742,11 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_tiled_bwd_dkv(TiledArgs a)
         v0[i] = to_bf16(dvacc[2 * sc][i]);
         v1[i] = to_bf16(dvacc[2 * sc + 1][i]);
       }
-      *(bf16x4*)(row + a.C + 32 * sc + 4 * g) = k0;
-      *(bf16x4*)(row + a.C + 32 * sc + 16 + 4 * g) = k1;
-      *(bf16x4*)(row + 2 * a.C + 32 * sc + 4 * g) = v0;
-      *(bf16x4*)(row + 2 * a.C + 32 * sc + 16 + 4 * g) = v1;
+      const bf16x8 k8 = pair_cols(k0, k1, g), v8 = pair_cols(v0, v1, g);
+      if (kv) {
+        *(bf16x8*)(row + a.C + 32 * sc) = k8;
+        *(bf16x8*)(row + 2 * a.C + 32 * sc) = v8;
+      }
     }
   }
   if (sat >= kFixLim) a.dbias_acc[(int64_t)a.nh * a.nbins] = 1ull;  // saturation word (same value from any lane)
