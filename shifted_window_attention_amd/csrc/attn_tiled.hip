@@ -340,20 +340,33 @@ __global__ __launch_bounds__(256, (FAST || HD < 128) ? 2 : 1) void k_tiled_fwd_p
     if (kb + 1 < nkb) step(kb + 1, Sb, Sa);
   }
   l += __shfl_xor(l, 32);
-  if (qv) {
+  {
+    // lanes l and l ^ 32 (same query) hold columns 8 j + 4 hh .. + 3 of every 32-column block;
+    // they swap halves so that each writes two 16-byte pieces: columns 8 hh + 16 p .. + 7
+    // (every lane takes part)
     const float inv = __builtin_amdgcn_rcpf(l);
-    const int64_t grow = a.perm[off + q];
-    bf16* orow = a.o + grow * a.C + (int64_t)h * HD;
+    const int64_t grow = qv ? a.perm[off + q] : 0;
+    bf16* orow = a.o + grow * a.C + (int64_t)h * HD + 8 * hh;
 #pragma unroll
-    for (int sc = 0; sc < NSUB; ++sc)
+    for (int sc = 0; sc < NSUB; ++sc) {
+      bf16x4 v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x4 o4;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] = to_bf16(oacc[sc][4 * j + i] * inv);
-        *(bf16x4*)(orow + 32 * sc + 8 * j + 4 * hh) = o4;
+        for (int i = 0; i < 4; ++i) v[j][i] = to_bf16(oacc[sc][4 * j + i] * inv);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const u32x2 send = __builtin_bit_cast(u32x2, hh ? v[2 * p] : v[2 * p + 1]);
+        u32x2 recv;
+        recv[0] = (uint32_t)__shfl_xor((int)send[0], 32);
+        recv[1] = (uint32_t)__shfl_xor((int)send[1], 32);
+        const bf16x4 r = __builtin_bit_cast(bf16x4, recv);
+        const bf16x4 lo = hh ? r : v[2 * p], hi = hh ? v[2 * p + 1] : r;
+        const bf16x8 o8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if (qv) *(bf16x8*)(orow + 32 * sc + 16 * p) = o8;
       }
-    if (hh == 0) a.lse[(int64_t)h * a.n_tok + off + q] = m_run + fast_log2(l);
+    }
+    if (qv && hh == 0) a.lse[(int64_t)h * a.n_tok + off + q] = m_run + fast_log2(l);
   }
 }
 
