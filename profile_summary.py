@@ -47,6 +47,32 @@ COPY = "k_window_move<true>"
 
 
 def short(name):
+    """Kernel name without return type, namespace and arguments. rocprofv3 leaves some template
+    instances mangled (_ZN4swin15k_layernorm_fwdILi1E...): those become the plain name plus
+    "<...>", so that base() gives the kernel's name for both spellings."""
+    m = re.match(r"_ZN4swin(\d+)", name)
+    if m:
+        ln = int(m.group(1))
+        ident = name[m.end():m.end() + ln]
+        rest = name[m.end() + ln:]
+        if not rest.startswith("I"):
+            return ident
+        args, i = [], 1
+        while i < len(rest) and rest[i] != "E":  # integer literals and the two element types used here
+            lit = re.match(r"Li(\d+)E", rest[i:])
+            if lit:
+                args.append(lit.group(1))
+                i += lit.end()
+            elif rest.startswith("DF16b", i):
+                args.append("bf16")
+                i += 5
+            elif rest[i] == "f":
+                args.append("float")
+                i += 1
+            else:
+                args.append("?")
+                break
+        return "%s<%s>" % (ident, ", ".join(args))
     n = name.split("(")[0].replace("void ", "").replace("swin::", "")
     return n.strip()
 
