@@ -58,10 +58,10 @@ struct FwdBuf {
 template <int NKT>
 struct FwdSmem {
   static constexpr int B = sizeof(FwdBuf<NKT>), T = 4 * (kMaxBins + kMaxChunk + 16 * NKT);
-  // two workgroups per CU when the register budget allows it (up to 8 query tiles, with the
-  // bias in fp32), with as many buffers as then fit; otherwise three buffers if one workgroup
-  // fits them
-  static constexpr int MIN_BLOCKS = NKT <= 8 ? 2 : 1;
+  // several workgroups per CU when registers and LDS allow it (four up to 4 query tiles, three
+  // up to 6, two up to 8, with the bias in fp32), with as many buffers as then fit; otherwise
+  // three buffers if one workgroup fits them
+  static constexpr int MIN_BLOCKS = NKT <= 4 ? 4 : (NKT <= 6 ? 3 : (NKT <= 8 ? 2 : 1));
   static constexpr int LDS_CAP = 160 * 1024 / MIN_BLOCKS;
   static constexpr int NBUF = 3 * B + T <= LDS_CAP ? 3 : (2 * B + T <= LDS_CAP ? 2 : (3 * B + T <= 160 * 1024 ? 3 : 2));
   FwdBuf<NKT> buf[NBUF];
