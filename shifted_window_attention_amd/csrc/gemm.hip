@@ -889,9 +889,11 @@ __global__ void k_transpose_bf16(const bf16* __restrict__ in, bf16* __restrict__
 // ---------------------------------------------------------------------------
 static hipError_t gemm_nt(const bf16* A, int64_t lda, const int32_t* a_rows, const bf16* B, int64_t ldb, int64_t M,
                           int N, int K, const EpiParams& ep, hipStream_t s) {
-  if (ep.dot_o) {
+  if (ep.dot_o || K < 256) {
     // the row-dot epilogue holds a whole column of dot_o chunks per thread: 128-row tiles keep
-    // three workgroups per CU (measured faster than 256 x 128 for this epilogue only)
+    // three workgroups per CU (measured faster than 256 x 128 for this epilogue); so do
+    // products of fewer than four 64-deep K steps, whose tiles are mostly set-up and epilogue
+    // (C = 192: 5-6% faster; at K = 256 the larger tile is faster)
     constexpr int BM = 128, BN = 128;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     k_gemm_nt<BM, BN><<<xcd_grid(tiles), 256, 0, s>>>(A, lda, a_rows, B, ldb, M, N, K, ep);
