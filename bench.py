@@ -20,8 +20,9 @@ Prints one JSON line on stdout:
   tflops / mfma_peak_frac = algorithmic FLOPs per second and their fraction of the
   dense bf16 MFMA peak, step_ms = median / min / max of the timed steps,
   hbm_bytes_per_step = the algorithmic bytes of all stages of a step,
-  roofline = the dominant kernel against its bound (stage durations from HIP events
-  recorded on the library's stream inside the timed region),
+  roofline = the dominant kernel against its bound (stage durations from HIP events the
+  library records between stages, in a second pass of the same number of steps after the
+  timed one, which records events only at step boundaries),
   configs = the other workloads, cpu_baseline = the fp64 oracle on a bounded sample of the
   same workload (CPU model and BLAS threads recorded).
 
@@ -775,36 +776,40 @@ def main():
     torch.cuda.synchronize()
 
     hip = Hip()
-    per_step = 2 * (len(FWD_STAGES) + 1) + 2 * (len(BWD_STAGES) + 1)
-    ev = hip.events(per_step * args.steps)
-    t_start, t_end = hip.events(2)
-    N.swin_attn_trace_events(ev)
+    # the timed steps: one event at each step boundary and nothing recorded inside a step
+    bounds = hip.events(args.steps + 1)
     torch.cuda.synchronize()
-    assert hip.l.hipEventRecord(t_start, stream.cuda_stream) == 0
     wall0 = time.perf_counter()
-    for _ in range(args.steps):
+    assert hip.l.hipEventRecord(bounds[0], stream.cuda_stream) == 0
+    for i in range(args.steps):
         step()
-    assert hip.l.hipEventRecord(t_end, stream.cuda_stream) == 0
+        assert hip.l.hipEventRecord(bounds[i + 1], stream.cuda_stream) == 0
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    step_ms = [hip.elapsed_ms(bounds[i], bounds[i + 1]) for i in range(args.steps)]
+    total_ms = hip.elapsed_ms(bounds[0], bounds[args.steps])
+    ms_step = total_ms / args.steps
+    hip.destroy(bounds)
+
+    # per-stage durations from the same number of steps run again with the library's trace
+    # events (recorded between stages on the library's stream; each call's events bracket its
+    # stages)
+    per_step = 2 * (len(FWD_STAGES) + 1) + 2 * (len(BWD_STAGES) + 1)
+    ev = hip.events(per_step * args.steps)
+    N.swin_attn_trace_events(ev)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     recorded = N.swin_attn_trace_cursor()
     N.swin_attn_trace_events(None)
     assert recorded == per_step * args.steps, (recorded, per_step * args.steps)
-    total_ms = hip.elapsed_ms(t_start, t_end)
-    ms_step = total_ms / args.steps
-
-    # per-stage durations: each call's events bracket its stages; a step runs from its first
-    # call's start event to its last call's final event
     durations = {s: [] for s in FWD_STAGES + BWD_STAGES}
-    step_ms = []
     k = 0
     for _ in range(args.steps):
-        k0 = k
         for stages in (FWD_STAGES, FWD_STAGES, BWD_STAGES, BWD_STAGES):
             for j, s in enumerate(stages):
                 durations[s].append(hip.elapsed_ms(ev[k + j], ev[k + j + 1]))
             k += len(stages) + 1
-        step_ms.append(hip.elapsed_ms(ev[k0], ev[k - 1]))
     hip.destroy(ev)
 
     pairs = [m.plan.stats["allowed_pairs"] for m in mods]
