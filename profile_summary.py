@@ -137,7 +137,7 @@ def cmd_trace(a):
         b = bj
         lines += ["", "bench.py line of the same run: %.3f ms/step, %.1f TFLOP/s (%.1f%% of bf16 MFMA peak)" % (
             b["ms_per_step"], b["tflops"], 100 * b["mfma_peak_frac"]), "",
-            "| stage | avg ms per launch (HIP events, timed steps) | avg ms per dispatch (trace, all chain steps) |",
+            "| stage | avg ms per launch (bench.py stage events) | avg ms per dispatch (trace, all chain steps) |",
             "|---|---|---|"]
         for k, v in b["kernels"].items():
             t = chain_avg.get(k)
