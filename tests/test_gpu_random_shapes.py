@@ -1,7 +1,8 @@
 """A seeded sweep of random module shapes against the fp64 oracle, through the C ABI: 2-D and
 3-D grids, ragged edges, head_dim 32/64/128, batch 1-2, every periodic combination of the lat
 and lon axes, windows from 16 to over 1000 tokens (so both the one-tile and the tiled kernels,
-tables held in LDS and in global memory), one or two chained modules. Same bars as the other
+tables held in LDS and in global memory), one or two chained modules; a second set with channels
+256-1024 (the wide-tile QKV GEMM, whose output width 3C is a multiple of 256). Same bars as the other
 parity tests (tests/bars.py): per-token outputs 2e-2 + ulp_bf16(ref)/2, reduced gradients 2e-2 * max(1, |ref|_inf)."""
 import numpy as np
 import pytest
@@ -50,7 +51,33 @@ def random_configs(n=16, seed=11):
     return out
 
 
-CASES = random_configs()
+def wide_configs(n=8, seed=5):
+    """Channels 256-1024 with head_dim 32/64/128 (up to 32 heads), windows up to 16 x 16, grids of a
+    few hundred to ~2400 tokens."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        hd = int(rng.choice([32, 64, 128]))
+        C = int(rng.choice([256, 512, 768, 1024]))
+        three_d = rng.random() < 0.25
+        D = int(rng.integers(2, 4)) if three_d else 1
+        H, W = int(rng.integers(6, 40)), int(rng.integers(6, 48))
+        wd = int(rng.integers(1, D + 1))
+        wh, ww = int(rng.integers(3, min(H, 16) + 1)), int(rng.integers(3, min(W, 16) + 1))
+        batch = int(rng.integers(1, 3))
+        n_tok = batch * D * H * W
+        if n_tok > 3000 or n_tok * C > 1_500_000:
+            continue
+        shift = tuple(int(rng.integers(0, w)) if g > w else 0 for g, w in zip((D, H, W), (wd, wh, ww)))
+        shifts = ((0, 0, 0), shift) if rng.random() < 0.3 else (shift,)
+        periodic = int(rng.choice([0, 2, 4, 6]))
+        name = "w%d_C%d_hd%d_g%dx%dx%d_w%dx%dx%d" % (len(out), C, hd, D, H, W, wd, wh, ww)
+        out.append(SwinConfig(name=name, batch=batch, grid=(D, H, W), channels=C, heads=C // hd, window=(wd, wh, ww),
+                              shifts=shifts, dtype="bf16", backward=True, periodic=periodic, description=name))
+    return out
+
+
+CASES = random_configs() + wide_configs()
 
 
 @pytest.mark.parametrize("c", CASES, ids=lambda c: c.name)
