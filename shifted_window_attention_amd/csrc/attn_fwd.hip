@@ -62,6 +62,8 @@ struct FwdSmem {
   // up to 6, two up to 8, with the bias in fp32), with as many buffers as then fit; otherwise
   // three buffers if one workgroup fits them
   static constexpr int MIN_BLOCKS = NKT <= 4 ? 4 : (NKT <= 6 ? 3 : (NKT <= 8 ? 2 : 1));
+  // the launch bound counts waves per SIMD: MIN_BLOCKS workgroups of NKT waves over the four SIMDs
+  static constexpr int WAVES_PER_SIMD = (MIN_BLOCKS * NKT + 3) / 4;
   static constexpr int LDS_CAP = 160 * 1024 / MIN_BLOCKS;
   static constexpr int NBUF = 3 * B + T <= LDS_CAP ? 3 : (2 * B + T <= LDS_CAP ? 2 : (3 * B + T <= 160 * 1024 ? 3 : 2));
   FwdBuf<NKT> buf[NBUF];
@@ -71,7 +73,7 @@ struct FwdSmem {
 };
 
 template <int NKT>
-__global__ __launch_bounds__(64 * NKT, FwdSmem<NKT>::MIN_BLOCKS) void k_attn_fwd(AttnArgs a) {
+__global__ __launch_bounds__(64 * NKT, FwdSmem<NKT>::WAVES_PER_SIMD) void k_attn_fwd(AttnArgs a) {
   constexpr int NKC = (NKT + 1) / 2;   // 32-key chunks of the PV product
   constexpr int ROWS = FwdBuf<NKT>::ROWS;
   constexpr int NBUF = FwdSmem<NKT>::NBUF;

@@ -389,9 +389,12 @@ __global__ __launch_bounds__(256, BM == 128 ? 3 : 2) void k_gemm_nt(const bf16* 
 // execution; right after that barrier the stage the step used takes the copies of the stage
 // three ahead. The accumulators hold transposed 32 x 32 blocks (the MFMA's operands swapped),
 // so a lane owns one output row and 4 consecutive columns per register group; the epilogue
-// (bias, q scale, bf16) stages the tile in LDS and stores 16-byte row chunks, as plain rows
-// (mode 0) or head-split planes (mode 1). Results are bitwise those of k_gemm_nt: the same
-// products summed over K in the same order.
+// (bias, loaded before the loop, q scale, bf16) pairs lanes 32 apart and stores 16-byte row
+// pieces straight from registers: in head-split planes (mode 1) the 32 rows of a block are 32
+// consecutive 64-byte rows, so the stores are contiguous. (Plain rows, mode 0, are supported
+// but not launched: on rows of a wide matrix the same stores are scattered, and the LDS-staged
+// copy-out of k_gemm_nt measured faster there.) Results are bitwise those of k_gemm_nt: the
+// same products summed over K in the same order.
 // ---------------------------------------------------------------------------
 namespace wide {
 constexpr int BM = 256, BN = 256, BK = 32, ST = 3;
@@ -399,8 +402,7 @@ constexpr int NW = 8, NT = 64 * NW, WN = 4;   // waves: 2 along M, 4 along N
 constexpr int WTM = 128, WTN = 64, TM = WTM / 32, TN = WTN / 32;
 constexpr int A_BYTES = BM * 64, STAGE = (BM + BN) * 64;  // one 32-deep K step of A and B
 constexpr int CP = BM / 16 / NW + BN / 16 / NW;           // 1 KB copies per wave per stage
-constexpr int CPITCH = BN + 8;                            // bf16 per row of the staged output tile
-constexpr int LDS = ST * STAGE > BM * CPITCH * 2 ? ST * STAGE : BM * CPITCH * 2;
+constexpr int LDS = ST * STAGE;
 
 __device__ __forceinline__ bf16x8 frag(uint32_t addr) {
   u32x4 v;
@@ -414,6 +416,21 @@ __device__ __forceinline__ void wait_frags(bf16x8 (&fa)[NA], bf16x8 (&fb)[NB]) {
   for (int i = 0; i < NA; ++i) asm volatile("" : "+v"(fa[i]));
 #pragma unroll
   for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(fb[j]));
+}
+// lanes 0-31 of y trade places with lanes 32-63 of x (v_permlane32_swap, both dwords)
+__device__ __forceinline__ void swap_upper_lower(bf16x4& x, bf16x4& y) {
+  u32x2 xv = __builtin_bit_cast(u32x2, x), yv = __builtin_bit_cast(u32x2, y);
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const auto r = __builtin_amdgcn_permlane32_swap(xv[d], yv[d], false, false);
+    xv[d] = r[0];
+    yv[d] = r[1];
+  }
+  x = __builtin_bit_cast(bf16x4, xv);
+  y = __builtin_bit_cast(bf16x4, yv);
+}
+__device__ __forceinline__ bf16x8 join8(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 // this wave's copies of a stage have landed once at most `newer` later stages' are in flight
 __device__ __forceinline__ void wait_stage(int newer) {
@@ -484,6 +501,17 @@ __global__ __launch_bounds__(wide::NT, 1) void k_gemm_nt_wide(const bf16* __rest
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
+  // the bias of the lane's 4-column groups, loaded here so that its latency hides behind the loop
+  const int half = lane >> 5;
+  bf16x4 bias4[TN][4];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const int n = n0 + wn * WTN + 32 * j + 8 * gg + 4 * half;
+      bias4[j][gg] = (ep.bias && n < N) ? *(const bf16x4*)(ep.bias + n) : bf16x4{};
+    }
+
   const int KT = K / BK;
 #pragma unroll
   for (int s = 0; s < ST; ++s)
@@ -526,59 +554,46 @@ __global__ __launch_bounds__(wide::NT, 1) void k_gemm_nt_wide(const bf16* __rest
     }
   }
 
-  // epilogue: bias and q scale on the transposed blocks (a lane's 4 consecutive columns per
-  // register group), bf16 tile through LDS, 16-byte row chunks out
-  bf16* Cs = (bf16*)smem;
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  const int half = lane >> 5;
+  // epilogue: bias and q scale on the transposed blocks (a lane's row and 4 consecutive columns
+  // per register group g), bf16; lanes 32 apart then trade groups so that each lane holds 8
+  // consecutive columns twice (columns 8 half .. +7 and 16 + 8 half .. +7 of the 32-column
+  // block) and stores them straight to its row as two 16-byte pieces: the 32 rows of a block
+  // are consecutive rows of one head plane (mode 1), so every row piece of the block is
+  // written by one pair of stores, with no pass through LDS
 #pragma unroll
-  for (int j = 0; j < TN; ++j)
+  for (int j = 0; j < TN; ++j) {
+    const int nblk = n0 + wn * WTN + 32 * j;
+    const float scv = (ep.mode == 1 && nblk < ep.C) ? ep.qscale : 1.f;  // C is a multiple of 32
+    int64_t col_off[2], row_pitch;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int nl = wn * WTN + 32 * j + 8 * g + 4 * half;
-      const int n = n0 + nl;
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (ep.bias && n < N) {
-        const bf16x4 b4 = *(const bf16x4*)(ep.bias + n);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bv[e] = to_f32(b4[e]);
-      }
-      const float scv = (ep.mode == 1 && n < ep.C) ? ep.qscale : 1.f;
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int ml = wm * WTM + 32 * i + fr;
-        bf16x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = to_bf16((acc[i][j][4 * g + e] + bv[e]) * scv);
-        *(bf16x4*)(Cs + ml * CPITCH + nl) = o;
+    for (int pc = 0; pc < 2; ++pc) {
+      const int n = nblk + 16 * pc + 8 * half;
+      if (ep.mode == 1) {
+        const int plane = n / ep.C;
+        const int rem = n - plane * ep.C;
+        const int head = rem / ep.hd;
+        col_off[pc] = ((int64_t)plane * ep.nh + head) * ep.n_tok * ep.hd + (rem - head * ep.hd);
+      } else {
+        col_off[pc] = n;
       }
     }
-  __syncthreads();
-  constexpr int CH_PER_ROW = BN / 8;
-  constexpr int ROW_STEP = NT / CH_PER_ROW;
-  constexpr int ITERS = BM / ROW_STEP;
-  static_assert(NT % CH_PER_ROW == 0 && BM % ROW_STEP == 0, "uniform copy-out loop");
-  const int cc = (tid % CH_PER_ROW) * 8;
-  const int n = n0 + cc;
-  const int row0 = tid / CH_PER_ROW;
-  int64_t col_off, row_pitch;
-  if (ep.mode == 1) {
-    const int plane = n / ep.C;
-    const int rem = n - plane * ep.C;
-    const int head = rem / ep.hd;
-    col_off = ((int64_t)plane * ep.nh + head) * ep.n_tok * ep.hd + (rem - head * ep.hd);
-    row_pitch = ep.hd;
-  } else {
-    col_off = n;
-    row_pitch = ep.ldc;
-  }
-#pragma unroll 4
-  for (int it = 0; it < ITERS; ++it) {
-    const int row = row0 + ROW_STEP * it;
-    const int64_t m = m0 + row;
-    if (m < M && n < N) {
-      const int64_t orow = (ep.mode == 0 && ep.out_rows) ? (int64_t)ep.out_rows[m] : m;
-      *(bf16x8*)(ep.out + col_off + orow * row_pitch) = *(const bf16x8*)(Cs + row * CPITCH + cc);
+    row_pitch = ep.mode == 1 ? ep.hd : ep.ldc;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      bf16x4 c[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[gg][e] = to_bf16((acc[i][j][4 * gg + e] + to_f32(bias4[j][gg][e])) * scv);
+      swap_upper_lower(c[0], c[1]);
+      swap_upper_lower(c[2], c[3]);
+      const int64_t m = m0 + wm * WTM + 32 * i + fr;
+      if (m < M) {
+        const int64_t orow = (ep.mode == 0 && ep.out_rows) ? (int64_t)ep.out_rows[m] : m;
+        const int n = nblk + 8 * half;
+        if (n < N) *(bf16x8*)(ep.out + col_off[0] + orow * row_pitch) = join8(c[0], c[1]);
+        if (n + 16 < N) *(bf16x8*)(ep.out + col_off[1] + orow * row_pitch) = join8(c[2], c[3]);
+      }
     }
   }
 }
