@@ -49,8 +49,8 @@ FWD_STAGES = ["qkv_gemm", "attn_fwd", "proj_gemm"]
 BWD_STAGES = ["w_transpose", "dproj_gemm", "wgrad_proj", "attn_bwd", "dbias_reduce", "dgrad_qkv", "wgrad_qkv"]
 # stage -> (kernel name as rocprofv3 reports it, source file) for the single-kernel stages
 STAGE_KERNEL = {
-    "qkv_gemm": ("k_gemm_nt_wide", "gemm.hip"), "proj_gemm": ("k_gemm_nt", "gemm.hip"),
-    "dproj_gemm": ("k_gemm_nt", "gemm.hip"), "dgrad_qkv": ("k_gemm_nt", "gemm.hip"),
+    "qkv_gemm": ("k_gemm_nt_wide<false>", "gemm.hip"), "proj_gemm": ("k_gemm_nt", "gemm.hip"),
+    "dproj_gemm": ("k_gemm_nt_wide<true>", "gemm.hip"), "dgrad_qkv": ("k_gemm_nt", "gemm.hip"),
     "attn_fwd": ("k_attn_fwd", "attn_fwd.hip"), "attn_bwd": ("k_attn_bwd", "attn_bwd.hip"),
 }
 

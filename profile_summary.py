@@ -32,13 +32,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # launch order of the GEMM kernels within one bench step (W fwd, SW fwd, SW bwd, W bwd); the
-# QKV product runs on its own kernel (k_gemm_nt_wide)
-NT_ROLES = ["proj_gemm", "proj_gemm", "dproj_gemm", "dgrad_qkv", "dproj_gemm", "dgrad_qkv"]
+# QKV product and dproj (head_dim 32) run on the wide kernel's two instances
+NT_ROLES = ["proj_gemm", "proj_gemm", "dgrad_qkv", "dgrad_qkv"]
 TN_ROLES = ["wgrad_proj", "wgrad_qkv", "wgrad_proj", "wgrad_qkv"]
-SINGLE = {"k_attn_fwd": "attn_fwd", "k_attn_bwd": "attn_bwd", "k_gemm_nt_wide": "qkv_gemm"}
+SINGLE = {"k_attn_fwd": "attn_fwd", "k_attn_bwd": "attn_bwd", "k_gemm_nt_wide<false>": "qkv_gemm",
+          "k_gemm_nt_wide<true>": "dproj_gemm"}
 # the same for one step of the two-block chain (block 0 fwd, block 1 fwd, block 1 bwd, block 0 bwd)
 NT_BLOCK_ROLES = (["proj_res_gemm", "mlp_w1_gelu", "mlp_w2_res"] * 2 +
-                  ["mlp_dgelu", "mlp_dxn", "dproj_gemm", "dgrad_qkv"] * 2)
+                  ["mlp_dgelu", "mlp_dxn", "dgrad_qkv"] * 2)
 TN_BLOCK_ROLES = ["wgrad_w2", "wgrad_w1", "wgrad_proj", "wgrad_qkv"] * 2
 BLOCK_START = "k_layernorm_fwd"
 SOURCES = {"k_gemm_nt": "gemm.hip", "k_gemm_nt_wide": "gemm.hip", "k_gemm_tn": "gemm.hip", "k_attn_fwd": "attn_fwd.hip",
@@ -63,6 +64,9 @@ def short(name):
             if lit:
                 args.append(lit.group(1))
                 i += lit.end()
+            elif rest.startswith("Lb0E", i) or rest.startswith("Lb1E", i):
+                args.append("true" if rest[i + 2] == "1" else "false")
+                i += 4
             elif rest.startswith("DF16b", i):
                 args.append("bf16")
                 i += 5
@@ -79,6 +83,11 @@ def short(name):
 
 def base(name):
     return short(name).split("<")[0]
+
+
+def single_role(name):
+    """The stage of a kernel that serves one stage: by its instance, else by its name."""
+    return SINGLE.get(short(name)) or SINGLE.get(base(name))
 
 
 def find(dirname, suffix):
@@ -175,7 +184,7 @@ def trace_roles(path):
             roles = TN_ROLES if phase == "chain" else TN_BLOCK_ROLES
             role = roles[seq[b] % len(roles)]
         else:
-            role = SINGLE.get(b, short(r["Kernel_Name"]))
+            role = single_role(r["Kernel_Name"]) or short(r["Kernel_Name"])
         seq[b] += 1
         out[(phase, role)].append(ns)
     return out
@@ -206,8 +215,8 @@ def per_dispatch(path, counter):
                 role = NT_ROLES[seq[b] % len(NT_ROLES)]
             elif b == "k_gemm_tn":
                 role = TN_ROLES[seq[b] % len(TN_ROLES)]
-            elif b in SINGLE:
-                role = SINGLE[b]
+            elif single_role(r["Kernel_Name"]):
+                role = single_role(r["Kernel_Name"])
             seq[b] += 1
         elif name == COPY:
             role = "copy"

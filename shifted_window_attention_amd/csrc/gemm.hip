@@ -5,8 +5,9 @@
 //                partition fused into the operand load), and the epilogue writes
 //                head-split q/k/v planes or plain rows (optionally through a row map)
 //                and can also form per-head row dot products with a second matrix.
-//   k_gemm_nt_wide: the same product for the QKV projection (gathered A rows, head-split
-//                epilogue) on 256 x 256 tiles fed by direct global->LDS copies.
+//   k_gemm_nt_wide: the same product for the QKV projection and, at head_dim 32, for dO with
+//                its per-head row dots (gathered A rows, head-split epilogue from registers)
+//                on 256 x 256 tiles fed by direct global->LDS copies.
 //   k_gemm_tn:   P[s, m, n] = sum_{t in chunk s} A[t, m] * B[t, n]   (contraction over
 //                tokens for the weight gradients; deterministic split-K partials)
 //   k_reduce_splits: fixed-order sum of the split-K partials (weights and biases).
@@ -393,8 +394,11 @@ __global__ __launch_bounds__(256, BM == 128 ? 3 : 2) void k_gemm_nt(const bf16* 
 // pieces straight from registers: in head-split planes (mode 1) the 32 rows of a block are 32
 // consecutive 64-byte rows, so the stores are contiguous. (Plain rows, mode 0, are supported
 // but not launched: on rows of a wide matrix the same stores are scattered, and the LDS-staged
-// copy-out of k_gemm_nt measured faster there.) Results are bitwise those of k_gemm_nt: the
-// same products summed over K in the same order.
+// copy-out of k_gemm_nt measured faster there.) DOT (the proj backward at head_dim 32, where a
+// 32-column block is one head): also -D = -rowsum(dO o) per head, from the lane's two stored
+// pieces and the matching pieces of the gathered o row, in the 8-column chunk order of
+// k_gemm_nt's reduction. Results are bitwise those of k_gemm_nt: the same products summed over
+// K, and the same row dots, in the same order.
 // ---------------------------------------------------------------------------
 namespace wide {
 constexpr int BM = 256, BN = 256, BK = 32, ST = 3;
@@ -417,17 +421,20 @@ __device__ __forceinline__ void wait_frags(bf16x8 (&fa)[NA], bf16x8 (&fb)[NB]) {
 #pragma unroll
   for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(fb[j]));
 }
-// lanes 0-31 of y trade places with lanes 32-63 of x (v_permlane32_swap, both dwords)
+// Lanes 0-31 of y trade places with lanes 32-63 of x. Inline assembly: the instruction writes
+// both of its registers, and the compiler's builtin for it has been seen to read one result
+// register twice when both results feed one expression; the s_nop gives the wait states a VALU
+// write needs before the swap reads the register.
+__device__ __forceinline__ void permlane32_swap(uint32_t& x, uint32_t& y) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
 __device__ __forceinline__ void swap_upper_lower(bf16x4& x, bf16x4& y) {
   u32x2 xv = __builtin_bit_cast(u32x2, x), yv = __builtin_bit_cast(u32x2, y);
-#pragma unroll
-  for (int d = 0; d < 2; ++d) {
-    const auto r = __builtin_amdgcn_permlane32_swap(xv[d], yv[d], false, false);
-    xv[d] = r[0];
-    yv[d] = r[1];
-  }
-  x = __builtin_bit_cast(bf16x4, xv);
-  y = __builtin_bit_cast(bf16x4, yv);
+  uint32_t x0 = xv[0], x1 = xv[1], y0 = yv[0], y1 = yv[1];
+  permlane32_swap(x0, y0);
+  permlane32_swap(x1, y1);
+  x = __builtin_bit_cast(bf16x4, u32x2{x0, x1});
+  y = __builtin_bit_cast(bf16x4, u32x2{y0, y1});
 }
 __device__ __forceinline__ bf16x8 join8(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -443,6 +450,7 @@ __device__ __forceinline__ void wait_stage(int newer) {
 }
 }  // namespace wide
 
+template <bool DOT>
 __global__ __launch_bounds__(wide::NT, 1) void k_gemm_nt_wide(const bf16* __restrict__ A, int64_t lda,
                                                              const int32_t* __restrict__ a_rows,
                                                              const bf16* __restrict__ B, int64_t ldb, int64_t M,
@@ -501,7 +509,8 @@ __global__ __launch_bounds__(wide::NT, 1) void k_gemm_nt_wide(const bf16* __rest
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-  // the bias of the lane's 4-column groups, loaded here so that its latency hides behind the loop
+  // the bias of the lane's 4-column groups, and the dot_o rows of its output rows, loaded here
+  // so that their latency hides behind the loop
   const int half = lane >> 5;
   bf16x4 bias4[TN][4];
 #pragma unroll
@@ -511,6 +520,15 @@ __global__ __launch_bounds__(wide::NT, 1) void k_gemm_nt_wide(const bf16* __rest
       const int n = n0 + wn * WTN + 32 * j + 8 * gg + 4 * half;
       bias4[j][gg] = (ep.bias && n < N) ? *(const bf16x4*)(ep.bias + n) : bf16x4{};
     }
+  int drow[TM];
+  if constexpr (DOT) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      int64_t m = m0 + wm * WTM + 32 * i + fr;
+      m = m < M ? m : M - 1;
+      drow[i] = ep.dot_rows ? ep.dot_rows[m] : (int)m;
+    }
+  }
 
   const int KT = K / BK;
 #pragma unroll
@@ -578,6 +596,16 @@ __global__ __launch_bounds__(wide::NT, 1) void k_gemm_nt_wide(const bf16* __rest
       }
     }
     row_pitch = ep.mode == 1 ? ep.hd : ep.ldc;
+    // row dot products (head_dim 32: the block is one head): the dot_o pieces that match the
+    // lane's two stored pieces, for all its rows, loaded before any is used
+    bf16x8 ov[TM][2];
+    if constexpr (DOT) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc)
+          ov[i][pc] = *(const bf16x8*)(ep.dot_o + (int64_t)drow[i] * ep.C + nblk + 16 * pc + 8 * half);
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       bf16x4 c[4];
@@ -587,12 +615,30 @@ __global__ __launch_bounds__(wide::NT, 1) void k_gemm_nt_wide(const bf16* __rest
         for (int e = 0; e < 4; ++e) c[gg][e] = to_bf16((acc[i][j][4 * gg + e] + to_f32(bias4[j][gg][e])) * scv);
       swap_upper_lower(c[0], c[1]);
       swap_upper_lower(c[2], c[3]);
+      const bf16x8 p0 = join8(c[0], c[1]), p1 = join8(c[2], c[3]);
       const int64_t m = m0 + wm * WTM + 32 * i + fr;
       if (m < M) {
         const int64_t orow = (ep.mode == 0 && ep.out_rows) ? (int64_t)ep.out_rows[m] : m;
         const int n = nblk + 8 * half;
-        if (n < N) *(bf16x8*)(ep.out + col_off[0] + orow * row_pitch) = join8(c[0], c[1]);
-        if (n + 16 < N) *(bf16x8*)(ep.out + col_off[1] + orow * row_pitch) = join8(c[2], c[3]);
+        if (n < N) *(bf16x8*)(ep.out + col_off[0] + orow * row_pitch) = p0;
+        if (n + 16 < N) *(bf16x8*)(ep.out + col_off[1] + orow * row_pitch) = p1;
+      }
+      if constexpr (DOT) {
+        // 8-column sums s0..s3 in column order (this lane: s0, s2 or s1, s3), combined as
+        // (s0 + s1) + (s2 + s3): the order of the 8-column chunks' pairwise reduction
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a += to_f32(p0[e]) * to_f32(ov[i][0][e]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b += to_f32(p1[e]) * to_f32(ov[i][1][e]);
+        // lanes 0-31: (s0, s1); lanes 32-63: (s2, s3); then lanes 0-31 take the other half's sum
+        uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+        permlane32_swap(ua, ub);
+        const float t = __builtin_bit_cast(float, ua) + __builtin_bit_cast(float, ub);
+        uint32_t tx = __builtin_bit_cast(uint32_t, t), ty = tx;
+        permlane32_swap(tx, ty);
+        const float dot = t + __builtin_bit_cast(float, ty);
+        if (half == 0 && m < M) ep.dot_out[(int64_t)(nblk / 32) * ep.n_tok + m] = dot * ep.dot_scale;
       }
     }
   }
@@ -936,7 +982,7 @@ hipError_t launch_qkv_fwd_bf16(const swin_attn_plan* p, const void* x, const voi
   if ((3 * p->C) % wide::BN != 0)
     return gemm_nt((const bf16*)x, p->C, p->dev.perm, (const bf16*)w, p->C, p->n_tok, 3 * p->C, p->C, ep, s);
   const int64_t tiles = ((p->n_tok + wide::BM - 1) / wide::BM) * ((3 * p->C + wide::BN - 1) / wide::BN);
-  k_gemm_nt_wide<<<xcd_grid(tiles), wide::NT, 0, s>>>((const bf16*)x, p->C, p->dev.perm, (const bf16*)w, p->C,
+  k_gemm_nt_wide<false><<<xcd_grid(tiles), wide::NT, 0, s>>>((const bf16*)x, p->C, p->dev.perm, (const bf16*)w, p->C,
                                                        p->n_tok, 3 * p->C, p->C, ep);
   return hipGetLastError();
 }
@@ -968,7 +1014,14 @@ hipError_t launch_dproj_bf16(const swin_attn_plan* p, const void* dy, const void
   ep.nh = p->nh;
   ep.hd = p->hd;
   ep.n_tok = p->n_tok;
-  return gemm_nt((const bf16*)dy, p->C, p->dev.perm, (const bf16*)wprojT, p->C, p->n_tok, p->C, p->C, ep, s);
+  // head_dim 32 with 256-column tiles dividing C: the wide kernel, whose register epilogue forms
+  // each head's dot from the lane pair's pieces (a 32-column block is one head)
+  if (p->hd != 32 || p->C % wide::BN != 0)
+    return gemm_nt((const bf16*)dy, p->C, p->dev.perm, (const bf16*)wprojT, p->C, p->n_tok, p->C, p->C, ep, s);
+  const int64_t tiles = ((p->n_tok + wide::BM - 1) / wide::BM) * (p->C / wide::BN);
+  k_gemm_nt_wide<true><<<xcd_grid(tiles), wide::NT, 0, s>>>((const bf16*)dy, p->C, p->dev.perm, (const bf16*)wprojT,
+                                                       p->C, p->n_tok, p->C, p->C, ep);
+  return hipGetLastError();
 }
 
 hipError_t launch_dgrad_qkv_bf16(const swin_attn_plan* p, const void* dqkv, const void* wqkvT, void* dx,
