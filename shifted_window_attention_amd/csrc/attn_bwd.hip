@@ -19,8 +19,9 @@
 // every wave then forms dQ^T = K^T dS^T for one query tile.
 //
 // Bias gradient without global atomics: all windows of a chunk share one class, so a
-// lane's (query, key) positions are the same in every window and its dS values are summed
-// over the chunk in registers. Once per workgroup the per-position sums are binned into
+// lane's (query, key) positions are the same in every window and its dS values (as rounded
+// to bf16 for the dK and dQ products) are summed over the chunk in fp32 registers, on the
+// matrix core against a 0/1 selector operand. Once per workgroup the per-position sums are binned into
 // the relative-position table in LDS, each bin owned by one thread and filled in a fixed
 // order, and the workgroup writes one partial table. A second kernel adds the partials
 // in order of work item. Every reduction therefore has a fixed order and repeated calls
@@ -154,6 +155,15 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
   }
   const int C = a.C;
   const float inv_log2e = 1.f / kLog2e;
+  // Selector operands for the bias-gradient sums on the matrix core: sel[u] (16 x 32, A operand)
+  // has a one at row r, column 8 (r / 4) + 4 u + r % 4, the slot of query 16 u + r of a chunk in
+  // the dS operand, so mfma16(sel[u], dS chunk, acc) adds the chunk's tile-u dS (as rounded to
+  // bf16 for the dK and dQ products) to acc in the dbacc layout.
+  bf16x8 sel[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[u][e] = to_bf16((g == (li >> 2) && e == 4 * u + (li & 3)) ? 1.f : 0.f);
   __syncthreads();
 
   // A __syncthreads() waits for every outstanding vector memory operation, the copies of
@@ -202,10 +212,8 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float p = fast_exp2(s[i]);
-            const float ds = p * dp[i];
-            dbacc[qt][i] += ds;
             pb[4 * u + i] = to_bf16(p);
-            sb[4 * u + i] = to_bf16(ds);
+            sb[4 * u + i] = to_bf16(p * dp[i]);
           }
           *(bf16x4*)(dSt + key * SPT + 16 * qt + 4 * g) = bf16x4{sb[4 * u], sb[4 * u + 1], sb[4 * u + 2], sb[4 * u + 3]};
         }
@@ -215,6 +223,9 @@ __global__ __launch_bounds__(64 * NKT, 1) void k_attn_bwd(BwdArgs a) {
         dvacc[dt] = mfma16(tile_frag_tr(cur.dO, 32 * c, 16 * dt, g, li), pb, dvacc[dt]);
         dkacc[dt] = mfma16(tile_frag_tr(cur.q, 32 * c, 16 * dt, g, li), sb, dkacc[dt]);
       }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (2 * c + u < NKT) dbacc[2 * c + u] = mfma16(sel[u], sb, dbacc[2 * c + u]);
       // bound live ranges to one query chunk (the two tiles inside a chunk may interleave: the
       // second tile's S and dP products overlap the first tile's exp and conversions)
       __builtin_amdgcn_sched_barrier(0);

@@ -17,7 +17,8 @@
 //
 // The logits are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16), so a lane
 // holds one query and 4 consecutive keys of every 16-key tile. The row max is an
-// in-register reduction plus two cross-lane steps; the row sum comes from the matrix core
+// in-register reduction plus two cross-lane steps, needed only when exp2 of the raw logits
+// leaves the safe range (below); the row sum comes from the matrix core
 // (an all-ones operand against the same bf16 P as the PV product); and the probabilities
 // of two adjacent key tiles are already the B operand of O^T = V^T P^T. The V^T operand is
 // read from the row-major V tile with gfx950's transposing LDS read. A window has at most
@@ -189,39 +190,93 @@ __global__ __launch_bounds__(64 * NKT, FwdSmem<NKT>::WAVES_PER_SIMD) void k_attn
     f32x4 s[NKT];
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) asm volatile("" : "+v"(bias[kt]));  // expand per window, not hoisted
+    f32x4 oacc[2], lacc;
+    float m;
+    if constexpr (NKT <= 10) {
+      auto logits = [&]() {
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      const f32x4 b4 = {(float)bias[kt][0], (float)bias[kt][1], (float)bias[kt][2], (float)bias[kt][3]};
-      s[kt] = mfma16(*(const bf16x8*)(cur.k + kq_off + 1024 * kt), bq, b4);
-    }
-    float m = -INFINITY;
+        for (int kt = 0; kt < NKT; ++kt) {
+          const f32x4 b4 = {(float)bias[kt][0], (float)bias[kt][1], (float)bias[kt][2], (float)bias[kt][3]};
+          s[kt] = mfma16(*(const bf16x8*)(cur.k + kq_off + 1024 * kt), bq, b4);
+        }
+      };
+      // O^T = V^T P^T, and the row sums of the same bf16 P from an all-ones A operand: every row
+      // of that product is the lane's query sum, so no cross-lane reduction is needed
+      auto pv = [&]() {
+        oacc[0] = oacc[1] = lacc = f32x4{};
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
+        for (int c = 0; c < NKC; ++c) {
+          bf16x8 pb;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) m = fmaxf(m, s[kt][i]);
-    m = wave_max_xor16_32(m);
+          for (int i = 0; i < 4; ++i) {
+            pb[i] = to_bf16(s[2 * c][i]);
+            pb[4 + i] = (2 * c + 1 < NKT) ? to_bf16(s[2 * c + 1][i]) : to_bf16(0.f);
+          }
+          bf16x8 v0, v1;
+          tile_frag_tr2_at(cur.v + 2048 * c, vt_off0, vt_off1, v0, v1);
+          oacc[0] = mfma16(v0, pb, oacc[0]);
+          oacc[1] = mfma16(v1, pb, oacc[1]);
+          lacc = mfma16(ones, pb, lacc);
+        }
+      };
+      // The softmax is invariant to a per-row offset, so the exponent offset is needed only to
+      // keep exp2 in range, and the first pass takes none: P = exp2(S2), l = rowsum(P). A row sum
+      // in [2^-60, 2^100] means no term overflowed and every term that underflowed lies below
+      // 2^-58 of the row's largest; otherwise (also for inf or NaN sums) the wave recomputes its
+      // logits and takes the row maximum m as the offset. Either way lse2 = offset + log2(l).
+      logits();
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
+      for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[kt][i] = fast_exp2(s[kt][i] - m);
-
-    // O^T = V^T P^T, and the row sums of the same bf16 P from an all-ones A operand: every row
-    // of that product is the lane's query sum, so no cross-lane reduction is needed
-    f32x4 oacc[2] = {f32x4{}, f32x4{}};
-    f32x4 lacc = f32x4{};
+        for (int i = 0; i < 4; ++i) s[kt][i] = fast_exp2(s[kt][i]);
+      pv();
+      m = 0.f;
+      if (__builtin_amdgcn_ballot_w64(!(lacc[0] >= 0x1p-60f && lacc[0] <= 0x1p100f)) != 0) {
+        logits();
+        m = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < NKC; ++c) {
-      bf16x8 pb;
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = to_bf16(s[2 * c][i]);
-        pb[4 + i] = (2 * c + 1 < NKT) ? to_bf16(s[2 * c + 1][i]) : to_bf16(0.f);
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, s[kt][i]);
+        m = wave_max_xor16_32(m);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[kt][i] = fast_exp2(s[kt][i] - m);
+        pv();
       }
-      bf16x8 v0, v1;
-      tile_frag_tr2_at(cur.v + 2048 * c, vt_off0, vt_off1, v0, v1);
-      oacc[0] = mfma16(v0, pb, oacc[0]);
-      oacc[1] = mfma16(v1, pb, oacc[1]);
-      lacc = mfma16(ones, pb, lacc);
+    } else {
+      // beyond 10 key tiles the two passes' live ranges would spill: always the offset m
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        const f32x4 b4 = {(float)bias[kt][0], (float)bias[kt][1], (float)bias[kt][2], (float)bias[kt][3]};
+        s[kt] = mfma16(*(const bf16x8*)(cur.k + kq_off + 1024 * kt), bq, b4);
+      }
+      m = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, s[kt][i]);
+      m = wave_max_xor16_32(m);
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[kt][i] = fast_exp2(s[kt][i] - m);
+      oacc[0] = oacc[1] = lacc = f32x4{};
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) {
+        bf16x8 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[i] = to_bf16(s[2 * c][i]);
+          pb[4 + i] = (2 * c + 1 < NKT) ? to_bf16(s[2 * c + 1][i]) : to_bf16(0.f);
+        }
+        bf16x8 v0, v1;
+        tile_frag_tr2_at(cur.v + 2048 * c, vt_off0, vt_off1, v0, v1);
+        oacc[0] = mfma16(v0, pb, oacc[0]);
+        oacc[1] = mfma16(v1, pb, oacc[1]);
+        lacc = mfma16(ones, pb, lacc);
+      }
     }
     const float l = lacc[0];
     const float inv = __builtin_amdgcn_rcpf(l);

@@ -38,8 +38,8 @@ def _maxabs(a, b):
     return float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
 
 
-def _check(cfg, with_bwd=True):
-    inp = make_inputs(cfg)
+def _check(cfg, with_bwd=True, inp=None):
+    inp = make_inputs(cfg) if inp is None else inp
     got = run_chain(cfg, inp, with_bwd=with_bwd)
     ref = chain_full(cfg, inp, with_bwd=with_bwd)
     tol = TOL_BF16 if cfg.dtype == "bf16" else TOL_F32
@@ -97,6 +97,21 @@ def test_bf16_backward_with_table_over_8192_bins():
     cfg = _cfg("global_40x60", (1, 40, 60), (1, 40, 60), ((0, 0, 0),), periodic=0)
     log("bf16 global 40x60 forward and backward (9401 bins)", cfg.grid, cfg.window)
     _check(cfg)
+
+
+@pytest.mark.parametrize("offset", [200.0, -200.0])
+def test_bf16_constant_table_offset(offset):
+    """A constant bias table adds the same amount to every unmasked logit of a row, which the
+    softmax ignores. At +-200 (+-288.5 in log2 units) exp2 of the raw logits overflows or
+    underflows, so the forward's offset-free first pass must fall back to the row-maximum offset
+    (144-token windows, W-MSA then SW-MSA, ragged edge windows)."""
+    cfg = _cfg("table_offset", (1, 30, 40), (1, 12, 12), ((0, 0, 0), (0, 6, 6)))
+    inp = make_inputs(cfg)
+    for m in inp.modules:
+        m.table = np.full_like(m.table, offset)
+        m.table_dev = np.full_like(m.table_dev, offset)
+    log("bf16 constant bias table %+.0f" % offset, cfg.grid, cfg.window)
+    _check(cfg, inp=inp)
 
 
 F32_CASES = [
