@@ -63,7 +63,9 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 }
 
 // One workgroup per (window, head); one thread per query with an online softmax over the
-// window's keys (K and V staged in LDS).
+// window's keys (K and V staged in LDS). HDM bounds head_dim (32 or 64): the per-query
+// vectors are unrolled over HDM with a head_dim guard, so they live in registers.
+template <int HDM>
 __global__ __launch_bounds__(256) void k_attn_f32(const float* __restrict__ qkv, const float* __restrict__ table,
                                                   float* __restrict__ o, float* __restrict__ lse,
                                                   const ClassInfo* __restrict__ classes,
@@ -90,29 +92,40 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float* __restrict__ qkv,
   __syncthreads();
   const float* tab = table + (int64_t)h * nbins;
   for (int q = threadIdx.x; q < n; q += blockDim.x) {
-    float qv[64];
-    for (int d = 0; d < hd; ++d) qv[d] = Qh[(int64_t)q * hd + d] * tau;
+    float qv[HDM], acc[HDM];
+#pragma unroll
+    for (int d = 0; d < HDM; ++d) {
+      qv[d] = d < hd ? Qh[(int64_t)q * hd + d] * tau : 0.f;
+      acc[d] = 0.f;
+    }
     const int qw = q % ci.ext[2], qh = (q / ci.ext[2]) % ci.ext[1], qd = q / (ci.ext[2] * ci.ext[1]);
     const int ql = (qd >= ci.split[0]) | ((qh >= ci.split[1]) << 1) | ((qw >= ci.split[2]) << 2);
-    float m = -INFINITY, l = 0.f, acc[64];
-    for (int d = 0; d < hd; ++d) acc[d] = 0.f;
+    float m = -INFINITY, l = 0.f;
     for (int k = 0; k < n; ++k) {
       const int kw = k % ci.ext[2], kh = (k / ci.ext[2]) % ci.ext[1], kd = k / (ci.ext[2] * ci.ext[1]);
       const int kl = (kd >= ci.split[0]) | ((kh >= ci.split[1]) << 1) | ((kw >= ci.split[2]) << 2);
       if (kl != ql) continue;
+      const float* kr = Ks + k * hd;
+      const float* vr = Vs + k * hd;
       float s = 0.f;
-      for (int d = 0; d < hd; ++d) s = fmaf(qv[d], Ks[k * hd + d], s);
+#pragma unroll
+      for (int d = 0; d < HDM; ++d)
+        if (d < hd) s = fmaf(qv[d], kr[d], s);
       const int bin = ((qd - kd + wd - 1) * (2 * wh - 1) + (qh - kh + wh - 1)) * (2 * ww - 1) + (qw - kw + ww - 1);
       s += tab[bin];
       const float mn = fmaxf(m, s);
       const float corr = expf(m - mn);
       const float p = expf(s - mn);
       l = l * corr + p;
-      for (int d = 0; d < hd; ++d) acc[d] = acc[d] * corr + p * Vs[k * hd + d];
+#pragma unroll
+      for (int d = 0; d < HDM; ++d)
+        if (d < hd) acc[d] = acc[d] * corr + p * vr[d];
       m = mn;
     }
     const float inv = 1.f / l;
-    for (int d = 0; d < hd; ++d) o[(off + q) * C + h * hd + d] = acc[d] * inv;
+#pragma unroll
+    for (int d = 0; d < HDM; ++d)
+      if (d < hd) o[(off + q) * C + h * hd + d] = acc[d] * inv;
     lse[(int64_t)h * n_tok + off + q] = m + logf(l);
   }
 }
@@ -131,9 +144,15 @@ hipError_t launch_fwd_f32(const swin_attn_plan* p, const void* x, const void* w_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = 2 * (size_t)p->stats.max_tokens * p->hd * sizeof(float);
-  k_attn_f32<<<dim3((unsigned)p->n_win, (unsigned)p->nh), 256, lds, s>>>(
-      qkv, table, o, lse, p->dev.classes, p->dev.class_win, p->dev.win_off, p->n_tok, p->nh, C, p->hd, p->nbins,
-      p->d.window[0], p->d.window[1], p->d.window[2], p->tau, (int)p->classes.size());
+  const dim3 ga((unsigned)p->n_win, (unsigned)p->nh);
+  if (p->hd <= 32)
+    k_attn_f32<32><<<ga, 256, lds, s>>>(qkv, table, o, lse, p->dev.classes, p->dev.class_win, p->dev.win_off,
+                                        p->n_tok, p->nh, C, p->hd, p->nbins, p->d.window[0], p->d.window[1],
+                                        p->d.window[2], p->tau, (int)p->classes.size());
+  else
+    k_attn_f32<64><<<ga, 256, lds, s>>>(qkv, table, o, lse, p->dev.classes, p->dev.class_win, p->dev.win_off,
+                                        p->n_tok, p->nh, C, p->hd, p->nbins, p->d.window[0], p->d.window[1],
+                                        p->d.window[2], p->tau, (int)p->classes.size());
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2((unsigned)((p->n_tok + 63) / 64), (unsigned)((C + 63) / 64));
