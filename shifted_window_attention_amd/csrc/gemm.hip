@@ -578,6 +578,18 @@ __global__ __launch_bounds__(wide::NT, 1) void k_gemm_nt_wide(const bf16* __rest
   // block) and stores them straight to its row as two 16-byte pieces: the 32 rows of a block
   // are consecutive rows of one head plane (mode 1), so every row piece of the block is
   // written by one pair of stores, with no pass through LDS
+  // row dot products (head_dim 32: a 32-column block is one head): the dot_o pieces that match
+  // the lane's stored pieces, for all its rows and blocks, loaded before any is used
+  bf16x8 ovall[TN][TM][2];
+  if constexpr (DOT) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc)
+          ovall[j][i][pc] = *(const bf16x8*)(ep.dot_o + (int64_t)drow[i] * ep.C + n0 + wn * WTN + 32 * j + 16 * pc + 8 * half);
+  }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int nblk = n0 + wn * WTN + 32 * j;
@@ -596,16 +608,7 @@ __global__ __launch_bounds__(wide::NT, 1) void k_gemm_nt_wide(const bf16* __rest
       }
     }
     row_pitch = ep.mode == 1 ? ep.hd : ep.ldc;
-    // row dot products (head_dim 32: the block is one head): the dot_o pieces that match the
-    // lane's two stored pieces, for all its rows, loaded before any is used
-    bf16x8 ov[TM][2];
-    if constexpr (DOT) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int pc = 0; pc < 2; ++pc)
-          ov[i][pc] = *(const bf16x8*)(ep.dot_o + (int64_t)drow[i] * ep.C + nblk + 16 * pc + 8 * half);
-    }
+    bf16x8 (&ov)[TM][2] = ovall[j];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       bf16x4 c[4];
