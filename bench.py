@@ -12,8 +12,9 @@ in each backward).
 
 Then the other workloads of the measurement plan, each on its own (180x360 batch 2, the ragged
 181x361 grid and the 8x180x360 level grid forward + backward; the 32x64 fp32 grid forward):
-median / min / max over 50 calls after 10 warm-ups, with the fp64 oracle timed on the same
-inputs (and the brute-force per-token loop on the fp32 grid).
+median / min / max over 50 calls after 10 warm-ups, then the same over 50 replays of the calls
+captured once in a HIP graph (graph_replay: no per-call host work), with the fp64 oracle timed
+on the same inputs (and the brute-force per-token loop on the fp32 grid).
 
 Prints one JSON line on stdout:
   value = token-blocks per second (tokens x modules per step / step time),
@@ -268,11 +269,11 @@ def time_config(hip, N, stream, name, calls=50, warmup=10, cpu_seconds=2.0, with
               "b_proj": torch.empty(C, dtype=torch.float32, device="cuda"),
               "table": torch.empty_like(m.table)} for m in mods] if cfg.backward else []
 
-    def call():
+    def call(s=stream):
         xin = x
         for m, y in zip(mods, ys):
             N.swin_attn_fwd(m.plan.handle, xin, m.w_qkv, m.b_qkv, m.w_proj, m.b_proj, m.table, y, m.saved,
-                            stream=stream)
+                            stream=s)
             xin = y
         if cfg.backward:
             d = dy
@@ -280,7 +281,7 @@ def time_config(hip, N, stream, name, calls=50, warmup=10, cpu_seconds=2.0, with
                 m, g = mods[i], grads[i]
                 xin = x if i == 0 else ys[i - 1]
                 N.swin_attn_bwd(m.plan.handle, d, xin, m.w_qkv, m.w_proj, m.table, m.saved, dxs[i], g["w_qkv"],
-                                g["b_qkv"], g["w_proj"], g["b_proj"], g["table"], m.ws, stream=stream)
+                                g["b_qkv"], g["w_proj"], g["b_proj"], g["table"], m.ws, stream=s)
                 d = dxs[i]
 
     for _ in range(warmup):
@@ -293,6 +294,27 @@ def time_config(hip, N, stream, name, calls=50, warmup=10, cpu_seconds=2.0, with
         assert hip.l.hipEventRecord(ev[2 * i + 1], stream.cuda_stream) == 0
     torch.cuda.synchronize()
     ms = np.array([hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(calls)])
+    # the same calls captured once in a HIP graph (torch's graph API over the library's stream) and
+    # replayed: the device time without per-call host work in the way
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        call(side)
+    stream.wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call(side)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            graph.replay()
+        for i in range(calls):
+            assert hip.l.hipEventRecord(ev[2 * i], stream.cuda_stream) == 0
+            graph.replay()
+            assert hip.l.hipEventRecord(ev[2 * i + 1], stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    gms = np.array([hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(calls)])
+    del graph
     hip.destroy(ev)
     flops = 0
     for m in mods:
@@ -310,6 +332,11 @@ def time_config(hip, N, stream, name, calls=50, warmup=10, cpu_seconds=2.0, with
         res["fp32_peak_frac"] = round(tfl / PEAK_F32_TFLOPS, 5)
     else:
         res["mfma_peak_frac"] = round(tfl / PEAK_BF16_TFLOPS, 4)
+    gmed = float(np.median(gms))
+    res["graph_replay"] = {"median_ms": round(gmed, 4), "min_ms": round(float(gms.min()), 4),
+                           "max_ms": round(float(gms.max()), 4),
+                           "tokens_per_s": round(cfg.n_tokens * cfg.modules / (gmed * 1e-3), 1),
+                           "tflops": round(flops / (gmed * 1e-3) / 1e12, 2)}
     if with_cpu:
         from oracle import swin_oracle as O
         lays = [O.window_layout(cfg.batch, cfg.grid, cfg.window, s, cfg.periodic) for s in cfg.shifts]

@@ -64,15 +64,20 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 
 // One workgroup per (window, head); one thread per query with an online softmax over the
 // window's keys (K and V staged in LDS). HDM bounds head_dim (32 or 64): the per-query
-// vectors are unrolled over HDM with a head_dim guard, so they live in registers.
-template <int HDM>
+// vectors are unrolled over HDM with a head_dim guard, so they live in registers. The bias
+// table index of a pair is linear in the two tokens' window coordinates, bin = qpos - kpos +
+// const, so each key's kpos and wrap label are formed once per workgroup in LDS. EXACT:
+// head_dim equals HDM (no guards).
+template <int HDM, bool EXACT>
 __global__ __launch_bounds__(256) void k_attn_f32(const float* __restrict__ qkv, const float* __restrict__ table,
                                                   float* __restrict__ o, float* __restrict__ lse,
                                                   const ClassInfo* __restrict__ classes,
                                                   const int32_t* __restrict__ class_win,
                                                   const int32_t* __restrict__ win_off, int64_t n_tok, int nh, int C,
-                                                  int hd, int nbins, int wd, int wh, int ww, float tau, int n_cls) {
+                                                  int hd_arg, int nbins, int wd, int wh, int ww, float tau,
+                                                  int n_cls) {
   extern __shared__ float sm[];
+  const int hd = EXACT ? HDM : hd_arg;
   const int h = blockIdx.y;
   const int slot = blockIdx.x;  // index into the class-sorted window list
   int c = 0;
@@ -82,6 +87,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float* __restrict__ qkv,
   const int64_t off = win_off[class_win[slot]];
   float* Ks = sm;
   float* Vs = sm + n * hd;
+  int2* kinfo = (int2*)(Vs + n * hd);  // per key: (position term of the bin, wrap label)
   const float* Qh = qkv + ((int64_t)(0 * nh + h) * n_tok + off) * hd;
   const float* Kh = qkv + ((int64_t)(1 * nh + h) * n_tok + off) * hd;
   const float* Vh = qkv + ((int64_t)(2 * nh + h) * n_tok + off) * hd;
@@ -89,8 +95,20 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float* __restrict__ qkv,
     Ks[i] = Kh[i];
     Vs[i] = Vh[i];
   }
+  const int th = 2 * wh - 1, tw = 2 * ww - 1;
+  auto coords = [&](int t, int& pos, int& lab) {
+    const int tw_ = t % ci.ext[2], th_ = (t / ci.ext[2]) % ci.ext[1], td_ = t / (ci.ext[2] * ci.ext[1]);
+    pos = (td_ * th + th_) * tw + tw_;
+    lab = (td_ >= ci.split[0]) | ((th_ >= ci.split[1]) << 1) | ((tw_ >= ci.split[2]) << 2);
+  };
+  for (int k = threadIdx.x; k < n; k += blockDim.x) {
+    int pos, lab;
+    coords(k, pos, lab);
+    kinfo[k] = int2{pos, lab};
+  }
   __syncthreads();
   const float* tab = table + (int64_t)h * nbins;
+  const int bin0 = ((wd - 1) * th + (wh - 1)) * tw + (ww - 1);  // bin of a pair at zero offset
   for (int q = threadIdx.x; q < n; q += blockDim.x) {
     float qv[HDM], acc[HDM];
 #pragma unroll
@@ -98,21 +116,20 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float* __restrict__ qkv,
       qv[d] = d < hd ? Qh[(int64_t)q * hd + d] * tau : 0.f;
       acc[d] = 0.f;
     }
-    const int qw = q % ci.ext[2], qh = (q / ci.ext[2]) % ci.ext[1], qd = q / (ci.ext[2] * ci.ext[1]);
-    const int ql = (qd >= ci.split[0]) | ((qh >= ci.split[1]) << 1) | ((qw >= ci.split[2]) << 2);
+    int qpos, ql;
+    coords(q, qpos, ql);
+    const float* tq = tab + bin0 + qpos;  // tq[-kpos] is the pair's bias
     float m = -INFINITY, l = 0.f;
     for (int k = 0; k < n; ++k) {
-      const int kw = k % ci.ext[2], kh = (k / ci.ext[2]) % ci.ext[1], kd = k / (ci.ext[2] * ci.ext[1]);
-      const int kl = (kd >= ci.split[0]) | ((kh >= ci.split[1]) << 1) | ((kw >= ci.split[2]) << 2);
-      if (kl != ql) continue;
+      const int2 ki = kinfo[k];
+      if (ki.y != ql) continue;
       const float* kr = Ks + k * hd;
       const float* vr = Vs + k * hd;
       float s = 0.f;
 #pragma unroll
       for (int d = 0; d < HDM; ++d)
         if (d < hd) s = fmaf(qv[d], kr[d], s);
-      const int bin = ((qd - kd + wd - 1) * (2 * wh - 1) + (qh - kh + wh - 1)) * (2 * ww - 1) + (qw - kw + ww - 1);
-      s += tab[bin];
+      s += tq[-ki.x];
       const float mn = fmaxf(m, s);
       const float corr = expf(m - mn);
       const float p = expf(s - mn);
@@ -143,16 +160,21 @@ hipError_t launch_fwd_f32(const swin_attn_plan* p, const void* x, const void* w_
                                 3 * C, C, 1, qkv, nullptr, C, p->nh, p->hd, p->n_tok);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = 2 * (size_t)p->stats.max_tokens * p->hd * sizeof(float);
+  const size_t lds = 2 * (size_t)p->stats.max_tokens * p->hd * sizeof(float) + (size_t)p->stats.max_tokens * 8;
   const dim3 ga((unsigned)p->n_win, (unsigned)p->nh);
-  if (p->hd <= 32)
-    k_attn_f32<32><<<ga, 256, lds, s>>>(qkv, table, o, lse, p->dev.classes, p->dev.class_win, p->dev.win_off,
-                                        p->n_tok, p->nh, C, p->hd, p->nbins, p->d.window[0], p->d.window[1],
-                                        p->d.window[2], p->tau, (int)p->classes.size());
+  auto attn = [&](auto kern) {
+    kern<<<ga, 256, lds, s>>>(qkv, table, o, lse, p->dev.classes, p->dev.class_win, p->dev.win_off, p->n_tok, p->nh,
+                              C, p->hd, p->nbins, p->d.window[0], p->d.window[1], p->d.window[2], p->tau,
+                              (int)p->classes.size());
+  };
+  if (p->hd == 32)
+    attn(k_attn_f32<32, true>);
+  else if (p->hd == 64)
+    attn(k_attn_f32<64, true>);
+  else if (p->hd < 32)
+    attn(k_attn_f32<32, false>);
   else
-    k_attn_f32<64><<<ga, 256, lds, s>>>(qkv, table, o, lse, p->dev.classes, p->dev.class_win, p->dev.win_off,
-                                        p->n_tok, p->nh, C, p->hd, p->nbins, p->d.window[0], p->d.window[1],
-                                        p->d.window[2], p->tau, (int)p->classes.size());
+    attn(k_attn_f32<64, false>);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2((unsigned)((p->n_tok + 63) / 64), (unsigned)((C + 63) / 64));

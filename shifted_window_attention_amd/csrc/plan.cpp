@@ -99,7 +99,7 @@ static swin_status check_kernel_support(const swin_attn_desc* d, int64_t max_tok
       return fail(SWIN_ERR_UNSUPPORTED, "fp32 windows of more than 256 tokens are not supported");
     if (nbins > kMaxBins) return fail(SWIN_ERR_UNSUPPORTED, "relative-position table larger than 2048 bins per head");
     if (hd > 64) return fail(SWIN_ERR_UNSUPPORTED, "fp32 kernels need head_dim <= 64");
-    if (2 * max_tokens * hd * 4 > 160 * 1024)
+    if (2 * max_tokens * hd * 4 + max_tokens * 8 > 160 * 1024)
       return fail(SWIN_ERR_UNSUPPORTED, "fp32 window K/V tiles exceed the 160 KB of LDS");
   }
   return SWIN_OK;

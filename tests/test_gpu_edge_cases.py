@@ -118,6 +118,9 @@ F32_CASES = [
     _cfg("f32_ragged", (1, 21, 29), (1, 6, 8), ((0, 3, 4),), dtype="f32", backward=False),
     _cfg("f32_window_1x1", (1, 6, 10), (1, 1, 1), ((0, 0, 0),), dtype="f32", backward=False),
     _cfg("f32_global", (1, 8, 16), (1, 8, 16), ((0, 0, 0),), dtype="f32", backward=False, batch=2),
+    # head_dim 16 and 48: the guarded variants of the fp32 attention kernel (head_dim below its bound)
+    _cfg("f32_hd16", (1, 12, 20), (1, 4, 8), ((0, 2, 4),), channels=32, heads=2, dtype="f32", backward=False),
+    _cfg("f32_hd48", (1, 12, 20), (1, 4, 8), ((0, 2, 4),), channels=96, heads=2, dtype="f32", backward=False),
 ]
 
 
