@@ -351,6 +351,20 @@ static const bwd_launcher kBwd[kMaxBwdTiles + 1] = {nullptr,           launch_bw
                                                     launch_bwd_one<6>, launch_bwd_one<7>, launch_bwd_one<8>,
                                                     launch_bwd_one<9>, launch_bwd_one<10>};
 
+// Workgroups of the k_attn_bwd<nqt> launch (dynamic LDS of dyn bytes) that one CU holds at once.
+int attn_bwd_blocks_per_cu(int nqt, size_t dyn) {
+  static const void* const kern[kMaxBwdTiles + 1] = {
+      nullptr,
+      (const void*)k_attn_bwd<1>, (const void*)k_attn_bwd<2>, (const void*)k_attn_bwd<3>, (const void*)k_attn_bwd<4>,
+      (const void*)k_attn_bwd<5>, (const void*)k_attn_bwd<6>, (const void*)k_attn_bwd<7>, (const void*)k_attn_bwd<8>,
+      (const void*)k_attn_bwd<9>, (const void*)k_attn_bwd<10>};
+  int n = 0;
+  if (nqt < 1 || nqt > kMaxBwdTiles ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern[nqt], 64 * nqt, dyn) != hipSuccess)
+    n = 1;
+  return n < 1 ? 1 : n;
+}
+
 hipError_t launch_dproj_bf16(const swin_attn_plan* p, const void* dy, const void* wprojT, void* dO, const void* o,
                              float* dd, hipStream_t s);
 hipError_t launch_dgrad_qkv_bf16(const swin_attn_plan* p, const void* dqkv, const void* wqkvT, void* dx,

@@ -58,7 +58,7 @@ struct FwdBuf {
 // direct-to-LDS copies against LDS reads to the explicit waits below.
 template <int NKT>
 struct FwdSmem {
-  static constexpr int B = sizeof(FwdBuf<NKT>), T = 4 * (kMaxBins + kMaxChunk + 16 * NKT);
+  static constexpr int B = sizeof(FwdBuf<NKT>), T = 4 * (kMaxBins + kFwdMaxChunk + 16 * NKT);
   // several workgroups per CU when registers and LDS allow it (four up to 4 query tiles, three
   // up to 6, two up to 8, with the bias in fp32), with as many buffers as then fit; otherwise
   // three buffers if one workgroup fits them
@@ -69,7 +69,7 @@ struct FwdSmem {
   static constexpr int NBUF = 3 * B + T <= LDS_CAP ? 3 : (2 * B + T <= LDS_CAP ? 2 : (3 * B + T <= 160 * 1024 ? 3 : 2));
   FwdBuf<NKT> buf[NBUF];
   float tab[kMaxBins];  // the head's bias table times log2(e)
-  int offs[kMaxChunk];
+  int offs[kFwdMaxChunk];
   int codes[16 * NKT];  // per-token local-offset codes and wrap labels
 };
 
@@ -308,6 +308,20 @@ static const fwd_launcher kFwd[17] = {nullptr,          launch_one<1>,  launch_o
                                       launch_one<8>,    launch_one<9>,  launch_one<10>, launch_one<11>,
                                       launch_one<12>,   launch_one<13>, launch_one<14>, launch_one<15>,
                                       launch_one<16>};
+
+// Workgroups of the k_attn_fwd<nqt> launch that one CU holds at once (at least 1).
+int attn_fwd_blocks_per_cu(int nqt) {
+  static const void* const kern[17] = {
+      nullptr,
+      (const void*)k_attn_fwd<1>,  (const void*)k_attn_fwd<2>,  (const void*)k_attn_fwd<3>,  (const void*)k_attn_fwd<4>,
+      (const void*)k_attn_fwd<5>,  (const void*)k_attn_fwd<6>,  (const void*)k_attn_fwd<7>,  (const void*)k_attn_fwd<8>,
+      (const void*)k_attn_fwd<9>,  (const void*)k_attn_fwd<10>, (const void*)k_attn_fwd<11>, (const void*)k_attn_fwd<12>,
+      (const void*)k_attn_fwd<13>, (const void*)k_attn_fwd<14>, (const void*)k_attn_fwd<15>, (const void*)k_attn_fwd<16>};
+  int n = 0;
+  if (nqt < 1 || nqt > 16 || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern[nqt], 64 * nqt, 0) != hipSuccess)
+    n = 1;
+  return n < 1 ? 1 : n;
+}
 
 hipError_t launch_attn_fwd_bf16(const swin_attn_plan* p, const void* qkv, const float* table, void* o, float* lse,
                                 hipStream_t s) {

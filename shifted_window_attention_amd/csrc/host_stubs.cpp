@@ -42,6 +42,8 @@ hipError_t launch_wgrad_bf16(const bf16_t*, int64_t, const bf16_t*, int64_t, int
   return hipErrorNotSupported;
 }
 hipError_t noalloc_scratch(int, void**) { return hipErrorNotSupported; }
+int attn_fwd_blocks_per_cu(int) { return 1; }
+int attn_bwd_blocks_per_cu(int, size_t) { return 1; }
 hipError_t launch_transpose_bf16(const void*, void*, int, int, hipStream_t) { return hipErrorNotSupported; }
 template <typename TX>
 hipError_t launch_layernorm_fwd(const TX*, const bf16_t*, const bf16_t*, bf16_t*, float*, float*, int64_t, int, float,

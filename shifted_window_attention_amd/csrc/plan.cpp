@@ -6,6 +6,7 @@
 //   * the per-window token offset/length table, which lets short edge windows
 //     run without padding,
 //   * window classes (extent + wrap-label split) and per-class work chunks.
+#include <functional>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -230,30 +231,45 @@ static void free_dev(swin_attn_plan* p) {
 
 // Windows per workgroup: enough chunks to fill the chip several times over, few enough
 // that per-class bias/mask setup is amortised.
-static int chunk_for(int64_t count, int heads, int64_t target_wgs, int cap) {
-  int64_t c = (count * heads + target_wgs - 1) / target_wgs;
-  return (int)std::max<int64_t>(1, std::min<int64_t>(cap, c));
-}
-
-// Work items grouped by tile count (one kernel instantiation per count), then by class.
-static void build_work(const std::vector<ClassInfo>& classes, int heads, int64_t target, int cap,
-                       std::vector<WorkItem>& out, std::vector<WorkRange>& ranges) {
+// Work items grouped by tile count (one launch per count). Within a launch every class is cut
+// into chunks of the same number of windows ch (each work item is one chunk for every head), and
+// ch minimises rounds * (ch + ovh): rounds = ceil(items / slots) waves of workgroups over the
+// launch's slots (CUs x workgroups per CU), ovh the fixed cost of a workgroup in windows (set-up,
+// and in the backward the bias-gradient binning). A class of a few windows thus gets a few
+// items instead of one per head per window; ties go to the smaller chunk (more items).
+static void build_work(const std::vector<ClassInfo>& classes, int heads, int n_cu, int ovh, int cap,
+                       const std::function<int(int)>& blocks_per_cu, std::vector<WorkItem>& out,
+                       std::vector<WorkRange>& ranges) {
   out.clear();
   ranges.clear();
   for (int nqt = 16; nqt >= 1; --nqt) {
+    std::vector<int> cls;
+    for (int c = 0; c < (int)classes.size(); ++c)
+      if (classes[c].nqt == nqt) cls.push_back(c);
+    if (cls.empty()) continue;
+    const int64_t slots = (int64_t)n_cu * blocks_per_cu(nqt);
+    int best = 1;
+    int64_t best_cost = -1;
+    for (int ch = 1; ch <= cap; ++ch) {
+      int64_t items = 0;
+      for (int c : cls) items += (classes[c].count + ch - 1) / ch;
+      const int64_t rounds = (items * heads + slots - 1) / slots;
+      const int64_t cost = rounds * (ch + ovh);
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best = ch;
+      }
+    }
     const int begin = (int)out.size();
-    for (int c = 0; c < (int)classes.size(); ++c) {
-      if (classes[c].nqt != nqt) continue;
-      const int ch = chunk_for(classes[c].count, heads, target, cap);
-      for (int f = 0; f < classes[c].count; f += ch) {
+    for (int c : cls)
+      for (int f = 0; f < classes[c].count; f += best) {
         WorkItem w{};
         w.cls = c;
         w.first = classes[c].first + f;
-        w.count = std::min(ch, classes[c].count - f);
+        w.count = std::min(best, classes[c].count - f);
         out.push_back(w);
       }
-    }
-    if ((int)out.size() > begin) ranges.push_back(WorkRange{nqt, begin, (int)out.size() - begin});
+    ranges.push_back(WorkRange{nqt, begin, (int)out.size() - begin});
   }
 }
 
@@ -371,7 +387,13 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
       p->class_win[p->classes[c].first + fill[c]++] = (int32_t)w;
     }
   }
-  build_work(p->classes, p->nh, 1024, kMaxChunk, p->fwd_work, p->fwd_ranges);
+  // work items are sized for the current device's CU count (the plan is created on it)
+  int n_cu = 0, cur_dev = 0;
+  if (hipGetDevice(&cur_dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, cur_dev) != hipSuccess || n_cu < 1)
+    n_cu = 256;
+  build_work(p->classes, p->nh, n_cu, kFwdItemOverhead, kFwdMaxChunk, attn_fwd_blocks_per_cu, p->fwd_work,
+             p->fwd_ranges);
   if (p->tiled || p->tiled_bwd) {
     // token-code tables of every class: key codes, then query codes, kCodeRound-padded
     const bool enc = p->nbins <= kTabLds;
@@ -397,9 +419,14 @@ swin_status swin_attn_plan_create(const swin_attn_desc* desc, swin_attn_plan** o
       for (int b = 0; b * 128 < n; ++b) p->tiled_kv_work.push_back(WorkItem{c, (int32_t)w, b, code_off[c]});
     }
   }
-  // the backward ends every workgroup with a pass that bins its bias-gradient sums: half the
-  // forward's workgroup count (twice the windows each) measured faster on small grids
-  build_work(p->classes, p->nh, 512, kMaxChunk, p->bwd_work, p->bwd_ranges);
+  // the backward ends every workgroup with a pass that bins its bias-gradient sums: a larger
+  // fixed cost per workgroup than the forward's
+  {
+    const size_t dyn = 2 * (size_t)p->nbins * sizeof(float);
+    build_work(p->classes, p->nh, n_cu, kBwdItemOverhead, kMaxChunk,
+               [dyn](int nqt) { return nqt <= kMaxBwdTiles ? attn_bwd_blocks_per_cu(nqt, dyn) : 1; }, p->bwd_work,
+               p->bwd_ranges);
+  }
 
   // saved state and workspace layout
   const size_t es = desc->dtype == SWIN_BF16 ? 2 : 4;

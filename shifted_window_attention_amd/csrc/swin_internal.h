@@ -80,7 +80,10 @@ struct WorkRange {
 
 constexpr int kMaxFwdTiles = 16;  // forward: windows of up to 256 tokens
 constexpr int kMaxBwdTiles = 10;  // backward: windows of up to 160 tokens (LDS budget)
-constexpr int kMaxChunk = 64;     // windows per attention work item
+constexpr int kFwdMaxChunk = 64;   // windows per forward work item
+constexpr int kMaxChunk = 160;     // windows per backward work item
+constexpr int kFwdItemOverhead = 2;  // fixed cost of a forward / backward workgroup, in windows
+constexpr int kBwdItemOverhead = 4;
 constexpr int kMaxBins = 2048;    // bias-table bins per head (windows of <= 256 tokens have < 2048)
 constexpr int kTiledMaxBwdBins = 8192;  // tiled backward: bias-gradient bins per head held in LDS (larger
                                         // tables are accumulated with global integer atomics)
@@ -149,6 +152,9 @@ hipError_t launch_rows_move(const void* src, void* dst, const int32_t* idx, int6
 // bf16 path
 hipError_t launch_qkv_fwd_bf16(const swin_attn_plan* p, const void* x, const void* w, const void* b,
                                void* qkv, hipStream_t s);
+// Workgroups per CU of the one-tile attention kernels (HIP occupancy query; at least 1).
+int attn_fwd_blocks_per_cu(int nqt);
+int attn_bwd_blocks_per_cu(int nqt, size_t dyn_lds);
 hipError_t launch_attn_fwd_bf16(const swin_attn_plan* p, const void* qkv, const float* table, void* o,
                                 float* lse, hipStream_t s);
 hipError_t launch_proj_fwd_bf16(const swin_attn_plan* p, const void* o, const void* w, const void* b, void* y,
